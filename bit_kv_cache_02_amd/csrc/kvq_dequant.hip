@@ -1,0 +1,99 @@
+// kvq_dequant_page: whole pages of the 4-bit cache back to fp32, plus the plain copy kernel used to
+// measure HBM bandwidth.
+//   INT4   y^ = fma(scale, code, zero): a single rounding of the exact value (token-wise INT4 with an
+//          fp16 scale and zero, SAW-INT4 summary, "Summary"/"Method").
+//   MXFP4  y^ = e2m1(code) * 2^(E-127), exact (FP4 with UE8M0 group scales, UltraQuant article).
+// With KVQ_UNROTATE the rotation is undone: x^ = R_b y^ (R_b symmetric orthogonal), by an fp32
+// Walsh-Hadamard butterfly in LDS.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+namespace {
+
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t idx = c & 7u;
+  // magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6: (2 + (idx&1)) * 2^((idx>>1) - 2) for idx >= 2
+  float mag = idx < 2u ? 0.5f * (float)idx : ldexpf(1.0f + 0.5f * (float)(idx & 1u), (int)(idx >> 1) - 1);
+  return (c & 8u) ? -mag : mag;
+}
+
+}  // namespace
+
+// One workgroup per (page, kv head): 256 threads, thread = (slot s = tid/16, column a = tid%16);
+// each thread owns channels a + 32q + 16e (q = 0..3, e = 0..1) of slot s, i.e. row bytes 4a..4a+3.
+__global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
+  __shared__ float buf[2][kPage][kHeadDim];
+  const int tid = threadIdx.x;
+  const int s = tid >> 4, col = tid & 15;
+  const int i = blockIdx.x / p.hkv, h = blockIdx.x % p.hkv;
+  const uint8_t* base = p.pool + ((int64_t)p.page_ids[i] * p.hkv + h) * kPageHeadBytes;
+  for (int which = 0; which < 2; ++which) {
+    uint32_t word;  // row bytes 4col..4col+3 of slot s
+    if (which == 0) {
+      word = *(const uint32_t*)(base + 64 * s + 4 * col);
+    } else {
+      const uint8_t* vb = base + kVCodesOff + 256 * (s >> 2) + 16 * col + (s & 3);
+      word = (uint32_t)vb[0] | ((uint32_t)vb[4] << 8) | ((uint32_t)vb[8] << 16) | ((uint32_t)vb[12] << 24);
+    }
+    const uint32_t pw = *(const uint32_t*)(base + (which ? kVParamsOff : kKParamsOff) + 4 * s);
+    for (int q = 0; q < 4; ++q) {
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t c = (word >> (8 * q + 4 * e)) & 15u;
+        const int ch = col + 32 * q + 16 * e;
+        float y;
+        if (p.fmt == 0) {
+          y = fmaf(f16_bits_to_f32(pw & 0xFFFFu), (float)c, f16_bits_to_f32(pw >> 16));
+        } else {
+          const int ex = (int)((pw >> (8 * (ch >> 5))) & 255u);
+          y = ldexpf(e2m1_value(c), ex - 127);
+        }
+        buf[which][s][ch] = y;
+      }
+    }
+  }
+  __syncthreads();
+  float scale = 1.0f;
+  if (p.unrotate && p.had_block > 1) {
+    for (int len = 1; len < p.had_block; len <<= 1) {
+      for (int k = tid; k < 2 * kPage * 64; k += 256) {
+        const int row = k >> 6, kk = k & 63;
+        const int jj = (kk / len) * 2 * len + (kk % len);
+        float* r = &buf[0][0][0] + row * kHeadDim;
+        const float u = r[jj], v = r[jj + len];
+        r[jj] = u + v;
+        r[jj + len] = u - v;
+      }
+      __syncthreads();
+    }
+    scale = p.had_block == 128 ? 0.08838834764831845f : 0.125f;
+  }
+  const int64_t out_base = ((int64_t)i * p.hkv + h) * kPage * kHeadDim;
+  for (int k = tid; k < kPage * kHeadDim; k += 256) {
+    p.out_k[out_base + k] = (&buf[0][0][0])[k] * scale;
+    p.out_v[out_base + k] = (&buf[1][0][0])[k] * scale;
+  }
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                  int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)src, (u32x4*)dst, n16);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,119 @@
+// Device-side helpers shared by the libkvq HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 16;
+constexpr int kPageHeadBytes = 2176;
+constexpr int kVCodesOff = 1024;
+constexpr int kKParamsOff = 2048;
+constexpr int kVParamsOff = 2112;
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// dtype codes (same values as kvq_dtype in kvq.h; duplicated so kernels need no C header)
+enum : int { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2, DT_E4M3 = 3 };
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---- DPP row (16-lane) reductions; every lane of the row ends with the same bits ----
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f<kQuadSwap1>(x));
+  x = fmaxf(x, dpp_f<kQuadSwap2>(x));
+  x = fmaxf(x, dpp_f<kRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kRowMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float row_min16(float x) {
+  x = fminf(x, dpp_f<kQuadSwap1>(x));
+  x = fminf(x, dpp_f<kQuadSwap2>(x));
+  x = fminf(x, dpp_f<kRowHalfMirror>(x));
+  x = fminf(x, dpp_f<kRowMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x = x + dpp_f<kQuadSwap1>(x);
+  x = x + dpp_f<kQuadSwap2>(x);
+  x = x + dpp_f<kRowHalfMirror>(x);
+  x = x + dpp_f<kRowMirror>(x);
+  return x;
+}
+
+// Full-wave reductions (prologue/epilogue only).
+__device__ __forceinline__ float wave_max(float x) {
+  x = row_max16(x);
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// ---- scalar conversions ----
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;  // NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
+}
+// OCP FP8 E4M3 (FN): 1 sign, 4 exponent (bias 7), 3 mantissa bits; 0x7F/0xFF are NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  uint32_t s = (b >> 7) & 1u, e = (b >> 3) & 15u, m = b & 7u;
+  float v;
+  if (e == 15u && m == 7u) v = __builtin_nanf("");
+  else if (e == 0u) v = (float)m * 0x1p-9f;
+  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return s ? -v : v;
+}
+
+__device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
+  switch (dt) {
+    case DT_F16: return f16_bits_to_f32(((const uint16_t*)p)[i]);
+    case DT_BF16: return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+    case DT_F32: return ((const float*)p)[i];
+    default: return e4m3_to_f32(((const uint8_t*)p)[i]);
+  }
+}
+__device__ __forceinline__ void store_elem(void* p, int64_t i, int dt, float x) {
+  switch (dt) {
+    case DT_F16: ((uint16_t*)p)[i] = (uint16_t)f32_to_f16_bits(x); break;
+    case DT_BF16: ((uint16_t*)p)[i] = (uint16_t)f32_to_bf16_bits(x); break;
+    default: ((float*)p)[i] = x; break;
+  }
+}
+
+// Byte permute: bytes of {hi, lo} selected by `sel` (0..3 = lo bytes, 4..7 = hi bytes, 0x0C = 0).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ int popc(uint32_t x) { return __builtin_popcount(x); }
+
+}  // namespace kvq

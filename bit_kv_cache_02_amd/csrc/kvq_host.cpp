@@ -1,0 +1,208 @@
+// C ABI of libkvq (declared in include/kvq.h): argument validation, launch planning, errors.
+// Validation runs before any HIP call, so invalid calls fail the same way with or without a GPU.
+#include "../../include/kvq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return KVQ_OK;
+  return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Common cache checks.  Returns KVQ_OK or an error status (with the message set).
+int check_cache(const kvq_cache* c) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache descriptor is NULL");
+  if (!c->pool) return fail(KVQ_ERR_INVALID_ARG, "cache->pool is NULL");
+  if (c->num_kv_heads < 1) return fail(KVQ_ERR_INVALID_ARG, "num_kv_heads must be >= 1 (got %d)", c->num_kv_heads);
+  if (c->num_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "num_pages must be >= 1");
+  if (c->reserved != 0) return fail(KVQ_ERR_INVALID_ARG, "cache->reserved must be 0");
+  if (c->head_dim != KVQ_HEAD_DIM) return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", c->head_dim);
+  if (c->page_size != KVQ_PAGE_SIZE) return fail(KVQ_ERR_UNSUPPORTED, "page_size %d unsupported (only 16)", c->page_size);
+  if (c->format != KVQ_FMT_INT4_TOKEN && c->format != KVQ_FMT_MXFP4_G32)
+    return fail(KVQ_ERR_UNSUPPORTED, "format %d unknown", c->format);
+  if (c->had_block != 1 && c->had_block != 64 && c->had_block != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "had_block %d unsupported (1, 64 or 128)", c->had_block);
+  if (c->format == KVQ_FMT_MXFP4_G32 && c->had_block == 64)
+    return fail(KVQ_ERR_UNSUPPORTED, "MXFP4 uses the full 128-wide rotation (had_block 128, or 1 for tests)");
+  if (((uintptr_t)c->pool) & 15) return fail(KVQ_ERR_INVALID_ARG, "pool must be 16-byte aligned");
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+size_t kvq_page_bytes(const kvq_cache* cache) {
+  if (!cache || cache->num_kv_heads < 1) return 0;
+  return (size_t)cache->num_kv_heads * KVQ_PAGE_HEAD_BYTES;
+}
+
+const char* kvq_strerror(int status) {
+  switch (status) {
+    case KVQ_OK: return "success";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* kvq_last_error(void) { return g_last_error; }
+
+int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype,
+               int32_t num_tokens, int32_t num_seqs, const int32_t* cu_new,
+               const int32_t* start_pos, const int32_t* block_table, int32_t max_pages,
+               int32_t max_new_tokens, void* stream) {
+  g_last_error[0] = 0;
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (!k || !v) return fail(KVQ_ERR_INVALID_ARG, "k and v must not be NULL");
+  if (!cu_new || !start_pos || !block_table) return fail(KVQ_ERR_INVALID_ARG, "cu_new, start_pos and block_table must not be NULL");
+  if (kv_dtype != KVQ_F16 && kv_dtype != KVQ_BF16) return fail(KVQ_ERR_UNSUPPORTED, "kv_dtype %d unsupported (F16 or BF16)", kv_dtype);
+  if (num_tokens < 0 || num_seqs < 0) return fail(KVQ_ERR_INVALID_ARG, "num_tokens and num_seqs must be >= 0");
+  if (max_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (max_new_tokens < 0) return fail(KVQ_ERR_INVALID_ARG, "max_new_tokens must be >= 0");
+  if ((((uintptr_t)k) | ((uintptr_t)v)) & 15) return fail(KVQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  if (num_seqs > 65535) return fail(KVQ_ERR_UNSUPPORTED, "num_seqs %d above 65535", num_seqs);
+  if (num_tokens == 0 || num_seqs == 0 || max_new_tokens == 0) return KVQ_OK;
+  kvq::AppendParams p;
+  p.pool = (uint8_t*)cache->pool;
+  p.k = (const uint8_t*)k;
+  p.v = (const uint8_t*)v;
+  p.cu_new = cu_new;
+  p.start_pos = start_pos;
+  p.block_table = block_table;
+  p.hkv = cache->num_kv_heads;
+  p.num_seqs = num_seqs;
+  p.max_pages = max_pages;
+  p.max_new = max_new_tokens;
+  return hip_status(kvq::launch_append(p, kv_dtype == KVQ_BF16, cache->had_block, cache->format, (hipStream_t)stream),
+                    "kvq_append launch");
+}
+
+static int decode_geometry(const kvq_cache* cache, int32_t num_q_heads, int32_t num_seqs, int32_t max_seq_len) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads)
+    return fail(KVQ_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads, cache->num_kv_heads);
+  if (num_q_heads / cache->num_kv_heads > 8)
+    return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d above 8", num_q_heads / cache->num_kv_heads);
+  if (num_seqs < 0) return fail(KVQ_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (max_seq_len < 1) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+  return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_q_heads, int32_t num_seqs,
+                                  int32_t max_seq_len) {
+  if (decode_geometry(cache, num_q_heads, num_seqs, max_seq_len) != KVQ_OK) return (size_t)-1;
+  const kvq::DecodePlan plan = kvq::plan_decode(num_seqs, cache->num_kv_heads, max_seq_len);
+  return kvq::decode_workspace_bytes(plan, num_seqs, cache->num_kv_heads, num_q_heads / cache->num_kv_heads);
+}
+
+int kvq_decode_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, float q_scale,
+                    int32_t num_q_heads, int32_t num_seqs, const int32_t* seq_lens,
+                    int32_t max_seq_len, const int32_t* block_table, int32_t max_pages,
+                    float sm_scale, void* out, int32_t out_dtype, uint32_t flags,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  int st = decode_geometry(cache, num_q_heads, num_seqs, max_seq_len);
+  if (st != KVQ_OK) return st;
+  if (!q || !seq_lens || !block_table || !out) return fail(KVQ_ERR_INVALID_ARG, "q, seq_lens, block_table and out must not be NULL");
+  if (q_dtype < KVQ_F16 || q_dtype > KVQ_FP8_E4M3) return fail(KVQ_ERR_UNSUPPORTED, "q_dtype %d unknown", q_dtype);
+  if (out_dtype != KVQ_F32 && out_dtype != KVQ_F16 && out_dtype != KVQ_BF16)
+    return fail(KVQ_ERR_UNSUPPORTED, "out_dtype %d unsupported (F32, F16 or BF16)", out_dtype);
+  if (max_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if ((int64_t)max_seq_len > (int64_t)max_pages * KVQ_PAGE_SIZE)
+    return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d exceeds max_pages*16 = %lld", max_seq_len, (long long)max_pages * KVQ_PAGE_SIZE);
+  if (flags & ~KVQ_OUT_ROTATED) return fail(KVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (!std::isfinite(q_scale) || !std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARG, "q_scale and sm_scale must be finite");
+  if (cache->format != KVQ_FMT_INT4_TOKEN) return fail(KVQ_ERR_UNSUPPORTED, "MXFP4 decode is not built yet");
+  if (num_seqs == 0) return KVQ_OK;
+  const int hkv = cache->num_kv_heads;
+  const int group = num_q_heads / hkv;
+  const kvq::DecodePlan plan = kvq::plan_decode(num_seqs, hkv, max_seq_len);
+  const size_t need = kvq::decode_workspace_bytes(plan, num_seqs, hkv, group);
+  if ((int64_t)num_seqs * hkv * plan.nsplit > 0x7FFFFFFF) return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
+  kvq::DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  if (need > 0) {
+    if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (workspace_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes given, %zu required", workspace_bytes, need);
+    if (((uintptr_t)workspace) & 255) return fail(KVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    kvq::carve_workspace(workspace, plan, num_seqs, hkv, group, &p.counters, &p.part_ml, &p.part_o);
+  }
+  p.pool = (const uint8_t*)cache->pool;
+  p.q = q;
+  p.seq_lens = seq_lens;
+  p.block_table = block_table;
+  p.out = out;
+  p.hkv = hkv;
+  p.group = group;
+  p.hq = num_q_heads;
+  p.num_seqs = num_seqs;
+  p.max_pages = max_pages;
+  p.had_block = cache->had_block;
+  p.q_dtype = q_dtype;
+  p.out_dtype = out_dtype;
+  p.out_rotated = (flags & KVQ_OUT_ROTATED) ? 1 : 0;
+  p.q_scale = q_scale;
+  p.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  p.plan = plan;
+  return hip_status(kvq::launch_decode(p, cache->format, (hipStream_t)stream), "kvq_decode_attn launch");
+}
+
+int kvq_dequant_page(const kvq_cache* cache, const int32_t* page_ids, int32_t n, float* out_k,
+                     float* out_v, uint32_t flags, void* stream) {
+  g_last_error[0] = 0;
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (n < 0) return fail(KVQ_ERR_INVALID_ARG, "n must be >= 0");
+  if (flags & ~KVQ_UNROTATE) return fail(KVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (n == 0) return KVQ_OK;
+  if (!page_ids || !out_k || !out_v) return fail(KVQ_ERR_INVALID_ARG, "page_ids, out_k and out_v must not be NULL");
+  if ((int64_t)n * cache->num_kv_heads > 0x7FFFFFFF) return fail(KVQ_ERR_UNSUPPORTED, "too many pages");
+  kvq::DequantParams p;
+  p.pool = (const uint8_t*)cache->pool;
+  p.page_ids = page_ids;
+  p.out_k = out_k;
+  p.out_v = out_v;
+  p.n = n;
+  p.hkv = cache->num_kv_heads;
+  p.had_block = cache->had_block;
+  p.unrotate = (flags & KVQ_UNROTATE) ? 1 : 0;
+  p.fmt = cache->format;
+  return hip_status(kvq::launch_dequant(p, (hipStream_t)stream), "kvq_dequant_page launch");
+}
+
+int kvq_hbm_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!src || !dst) return fail(KVQ_ERR_INVALID_ARG, "src and dst must not be NULL");
+  if (bytes % 16) return fail(KVQ_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  if ((((uintptr_t)src) | ((uintptr_t)dst)) & 15) return fail(KVQ_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  if (bytes == 0) return KVQ_OK;
+  return hip_status(kvq::launch_copy(src, dst, bytes, (hipStream_t)stream), "kvq_hbm_copy launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal launch interface between the C ABI host code and the HIP kernels of libkvq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct AppendParams {
+  uint8_t* pool;
+  const uint8_t* k;
+  const uint8_t* v;
+  const int32_t* cu_new;
+  const int32_t* start_pos;
+  const int32_t* block_table;
+  int32_t hkv;
+  int32_t num_seqs;
+  int32_t max_pages;
+  int32_t max_new;
+};
+
+struct DecodePlan {
+  int32_t pages_per_split;  // pages one workgroup handles
+  int32_t nsplit;           // workgroups per (sequence, kv head)
+  int32_t waves;            // waves per workgroup
+};
+
+struct DecodeParams {
+  const uint8_t* pool;
+  const void* q;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  void* out;
+  float* part_o;     // [units][nsplit][G][128] split partials (unnormalised o')
+  float* part_ml;    // [units][nsplit][G][2]   running max (log2 domain) and sum
+  int32_t* counters; // [units] arrival counters, zero between calls
+  int32_t hkv;
+  int32_t group;     // q heads per kv head (1..8)
+  int32_t hq;
+  int32_t num_seqs;
+  int32_t max_pages;
+  int32_t had_block;
+  int32_t q_dtype;
+  int32_t out_dtype;
+  int32_t out_rotated;
+  float q_scale;
+  float sm_scale_log2;  // sm_scale * log2(e)
+  DecodePlan plan;
+};
+
+struct DequantParams {
+  const uint8_t* pool;
+  const int32_t* page_ids;
+  float* out_k;
+  float* out_v;
+  int32_t n;
+  int32_t hkv;
+  int32_t had_block;
+  int32_t unrotate;
+  int32_t fmt;
+};
+
+hipError_t launch_append(const AppendParams& p, bool bf16, int had_block, int fmt, hipStream_t stream);
+DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len);
+size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int hkv, int group);
+void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, int group,
+                     int32_t** counters, float** part_ml, float** part_o);
+hipError_t launch_decode(const DecodeParams& p, int fmt, hipStream_t stream);
+hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+}  // namespace kvq

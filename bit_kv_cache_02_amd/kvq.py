@@ -1,0 +1,213 @@
+"""Python binding of libkvq (argument marshalling only).
+
+Every function here forwards to the C ABI declared in ``include/kvq.h``; all the
+computation runs in the library's HIP kernels on the caller's current HIP
+stream.  PyTorch provides device memory and the stream.  The module raises
+if ``libkvq.so`` has not been built: there is no fallback path.
+"""
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = 0, -1, -2, -3, -4
+FMT_INT4, FMT_MXFP4 = 0, 1
+F16, BF16, F32, FP8_E4M3 = 0, 1, 2, 3
+OUT_ROTATED = 1
+UNROTATE = 1
+HEAD_DIM = 128
+PAGE_SIZE = 16
+PAGE_HEAD_BYTES = 2176
+
+_DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32,
+               torch.float8_e4m3fn: FP8_E4M3}
+_FMT_CODE = {"int4": FMT_INT4, "mxfp4": FMT_MXFP4}
+
+
+class KvqCacheDesc(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("had_block", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64), ("pool", ctypes.c_void_p)]
+
+
+class KvqError(RuntimeError):
+    pass
+
+
+_lib = None
+
+# (name, restype, argtypes) of every symbol kvq.h declares
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+SIGNATURES = [
+    ("kvq_abi_version", ctypes.c_int, []),
+    ("kvq_page_bytes", ctypes.c_size_t, [ctypes.POINTER(KvqCacheDesc)]),
+    ("kvq_append", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _P, _I32, _I32, _I32, _P, _P, _P,
+                                  _I32, _I32, _P]),
+    ("kvq_decode_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(KvqCacheDesc), _I32, _I32, _I32]),
+    ("kvq_decode_attn", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _I32, ctypes.c_float, _I32,
+                                       _I32, _P, _I32, _P, _I32, ctypes.c_float, _P, _I32,
+                                       ctypes.c_uint32, _P, ctypes.c_size_t, _P]),
+    ("kvq_dequant_page", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _I32, _P, _P,
+                                        ctypes.c_uint32, _P]),
+    ("kvq_strerror", ctypes.c_char_p, [ctypes.c_int]),
+    ("kvq_last_error", ctypes.c_char_p, []),
+    ("kvq_hbm_copy", ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+]
+
+
+def lib():
+    """The loaded libkvq (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise KvqError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m bit_kv_cache_02_amd.build` (no fallback exists)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status == KVQ_OK:
+        return
+    msg = f"{what}: {lib().kvq_strerror(status).decode()}: {lib().kvq_last_error().decode()}"
+    if status in (KVQ_ERR_INVALID_ARG, KVQ_ERR_WORKSPACE):
+        raise ValueError(msg)
+    if status == KVQ_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise KvqError(msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, device=True):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+class Cache:
+    """One layer's paged 4-bit cache: a caller-owned uint8 pool [num_pages][Hkv][2176]."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, had_block: int, fmt: str = "int4",
+                 device="cuda", pool: Optional[torch.Tensor] = None, fill: Optional[int] = None):
+        self.fmt = fmt
+        self.num_kv_heads = num_kv_heads
+        self.had_block = had_block
+        self.num_pages = num_pages
+        if pool is None:
+            pool = torch.empty((num_pages, num_kv_heads, PAGE_HEAD_BYTES), dtype=torch.uint8,
+                               device=device)
+            if fill is not None:
+                pool.fill_(fill)
+        if tuple(pool.shape) != (num_pages, num_kv_heads, PAGE_HEAD_BYTES) or pool.dtype != torch.uint8:
+            raise ValueError("pool must be uint8[num_pages][num_kv_heads][2176]")
+        self.pool = pool
+
+    def desc(self) -> KvqCacheDesc:
+        return KvqCacheDesc(_FMT_CODE[self.fmt], self.num_kv_heads, HEAD_DIM, PAGE_SIZE,
+                            self.had_block, 0, self.num_pages, self.pool.data_ptr())
+
+
+def abi_version() -> int:
+    return lib().kvq_abi_version()
+
+
+def append(cache: Cache, k: torch.Tensor, v: torch.Tensor, cu_new: torch.Tensor,
+           start_pos: torch.Tensor, block_table: torch.Tensor, max_new_tokens: int):
+    """Rotate, quantize and write tokens k, v [T][Hkv][128] into the cache (kvq_append)."""
+    for t, n in ((k, "k"), (v, "v")):
+        _require(t, n)
+    for t, n in ((cu_new, "cu_new"), (start_pos, "start_pos"), (block_table, "block_table")):
+        _require(t, n, torch.int32)
+    if k.dtype not in (torch.float16, torch.bfloat16) or v.dtype != k.dtype:
+        raise ValueError("k and v must both be float16 or bfloat16")
+    d = cache.desc()
+    st = lib().kvq_append(ctypes.byref(d), _ptr(k), _ptr(v), _DTYPE_CODE[k.dtype], k.shape[0],
+                          start_pos.shape[0], _ptr(cu_new), _ptr(start_pos), _ptr(block_table),
+                          block_table.shape[1], int(max_new_tokens), _stream())
+    _check(st, "kvq_append")
+
+
+def decode_workspace_bytes(cache: Cache, num_q_heads: int, num_seqs: int, max_seq_len: int) -> int:
+    d = cache.desc()
+    n = lib().kvq_decode_workspace_bytes(ctypes.byref(d), num_q_heads, num_seqs, max_seq_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError(f"kvq_decode_workspace_bytes: {lib().kvq_last_error().decode()}")
+    return n
+
+
+def make_workspace(cache: Cache, num_q_heads: int, num_seqs: int, max_seq_len: int, device="cuda"):
+    """Zero-filled workspace for kvq_decode_attn (None when none is needed)."""
+    n = decode_workspace_bytes(cache, num_q_heads, num_seqs, max_seq_len)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def decode_attn(cache: Cache, q: torch.Tensor, seq_lens: torch.Tensor, block_table: torch.Tensor,
+                max_seq_len: int, out: Optional[torch.Tensor] = None, q_scale: float = 1.0,
+                sm_scale: Optional[float] = None, out_dtype=torch.float32, rotated: bool = False,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """softmax(q'.K'^T) V' over the paged cache, rotated back (kvq_decode_attn)."""
+    _require(q, "q")
+    _require(seq_lens, "seq_lens", torch.int32)
+    _require(block_table, "block_table", torch.int32)
+    b, hq, dim = q.shape
+    if out is None:
+        out = torch.empty((b, hq, dim), dtype=out_dtype, device=q.device)
+    _require(out, "out")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if workspace is None:
+        workspace = make_workspace(cache, hq, b, max_seq_len, q.device)
+    d = cache.desc()
+    st = lib().kvq_decode_attn(ctypes.byref(d), _ptr(q), _DTYPE_CODE[q.dtype], float(q_scale), hq, b,
+                               _ptr(seq_lens), int(max_seq_len), _ptr(block_table),
+                               block_table.shape[1], float(sm_scale), _ptr(out),
+                               _DTYPE_CODE[out.dtype], OUT_ROTATED if rotated else 0,
+                               _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                               _stream())
+    _check(st, "kvq_decode_attn")
+    return out
+
+
+def dequant_pages(cache: Cache, page_ids: torch.Tensor, unrotate: bool = False):
+    """(k, v) float32 [n][Hkv][16][128] of whole pages (kvq_dequant_page)."""
+    _require(page_ids, "page_ids", torch.int32)
+    n = page_ids.numel()
+    shape = (n, cache.num_kv_heads, PAGE_SIZE, HEAD_DIM)
+    out_k = torch.empty(shape, dtype=torch.float32, device=page_ids.device)
+    out_v = torch.empty(shape, dtype=torch.float32, device=page_ids.device)
+    d = cache.desc()
+    st = lib().kvq_dequant_page(ctypes.byref(d), _ptr(page_ids), n, _ptr(out_k), _ptr(out_v),
+                                UNROTATE if unrotate else 0, _stream())
+    _check(st, "kvq_dequant_page")
+    return out_k, out_v
+
+
+def hbm_copy(src: torch.Tensor, dst: torch.Tensor):
+    """Plain copy kernel (bandwidth probe)."""
+    st = lib().kvq_hbm_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(), _stream())
+    _check(st, "kvq_hbm_copy")

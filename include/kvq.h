@@ -1,0 +1,179 @@
+/*
+ * kvq.h -- C ABI of libkvq: a rotated 4-bit paged KV cache for AMD MI355X (gfx950).
+ *
+ * The method (SAW-INT4 summary, aissential.tech, "Summary" and "Method"; UltraQuant
+ * article, oracore.dev, section on how the method works):
+ *   write path  every new K/V token vector is rotated by a block-diagonal Walsh-Hadamard
+ *               matrix R_b = blockdiag(H_b / sqrt(b)), quantized token-wise to 4 bits and
+ *               written into a paged cache through a block table (kvq_append);
+ *   read path   decode attention reads the 4-bit pages back, dequantizes in registers and
+ *               computes softmax(q'.K'^T) V' with q' = R_b q, rotating the result back
+ *               (kvq_decode_attn).  An orthogonal R_b preserves q.k (IsoQuant abstract).
+ * Two 4-bit formats: token-wise asymmetric INT4 with an fp16 scale and zero per vector,
+ * and MXFP4 (e2m1 codes, one UE8M0 power-of-two scale per 32 channels, UltraQuant).
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers must point to device memory (hipMalloc / a torch
+ *     CUDA tensor) owned by the caller; `cache` and scalars are host values.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only enqueued: the
+ *     library never synchronizes, never allocates device memory and keeps no mutable
+ *     global state, so calls are thread-safe; calls on one stream run in order.
+ *   - Host-side argument checks run before any HIP call and return a negative kvq_status;
+ *     kvq_last_error() then names the argument.  Device-side data (token counts, sequence
+ *     lengths, page ids) is trusted: out-of-range values are undefined behaviour.
+ *   - A failed kernel launch returns KVQ_ERR_HIP with the HIP error text in kvq_last_error().
+ *   - No C++ exception crosses this boundary.
+ *
+ * Cache geometry (ABI v1): head_dim 128, page 16 tokens.  One page-head block (one page, one
+ * kv head) is 2176 bytes; the pool is uint8[num_pages][num_kv_heads][2176]:
+ *   [0,1024)     K code rows: slot s at 64*s; row byte 4a+q (a=0..15, q=0..3) holds channel
+ *                a+32q in its low nibble and channel a+32q+16 in its high nibble (channels
+ *                of the rotated vector).
+ *   [1024,2048)  V code rows, same row bytes, interleaved by slot quads: byte j of slot s at
+ *                1024 + 256*(s/4) + 4*j + (s%4).
+ *   [2048,2112)  K parameters, slot s at 2048+4s;  [2112,2176) V parameters, same.
+ *                INT4: fp16 scale then fp16 zero (little-endian); value = scale*code + zero.
+ *                MXFP4: UE8M0 bytes of channel groups [0,32),[32,64),[64,96),[96,128);
+ *                value = e2m1(code) * 2^(E-127); code bit 3 is the sign.
+ * Only the bytes of appended slots are ever written.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_HEAD_DIM 128
+#define KVQ_PAGE_SIZE 16
+#define KVQ_PAGE_HEAD_BYTES 2176
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent geometry       */
+  KVQ_ERR_UNSUPPORTED = -2, /* valid but not implemented: head_dim, page size, dtype... */
+  KVQ_ERR_WORKSPACE = -3,   /* decode workspace missing or smaller than required         */
+  KVQ_ERR_HIP = -4          /* a HIP call (kernel launch) failed                          */
+} kvq_status;
+
+typedef enum { KVQ_FMT_INT4_TOKEN = 0, KVQ_FMT_MXFP4_G32 = 1 } kvq_format;
+
+typedef enum { KVQ_F16 = 0, KVQ_BF16 = 1, KVQ_F32 = 2, KVQ_FP8_E4M3 = 3 } kvq_dtype;
+
+/* kvq_decode_attn flags */
+#define KVQ_OUT_ROTATED 1u /* leave the output in the rotated basis (skip the final R_b) */
+/* kvq_dequant_page flags */
+#define KVQ_UNROTATE 1u    /* return R_b * y^ (the original basis) instead of y^          */
+
+/* Description of one cache (one layer).  Host struct; `pool` is a device pointer. */
+typedef struct {
+  int32_t format;       /* kvq_format                                                     */
+  int32_t num_kv_heads; /* >= 1                                                           */
+  int32_t head_dim;     /* must be 128                                                    */
+  int32_t page_size;    /* must be 16                                                     */
+  int32_t had_block;    /* Hadamard block width b: 1 (no rotation, "plain INT4"), 64, 128 */
+                        /* MXFP4 requires 128 (or 1, for tests)                            */
+  int32_t reserved;     /* must be 0                                                      */
+  int64_t num_pages;    /* pages in the pool                                              */
+  void* pool;           /* device uint8[num_pages][num_kv_heads][2176], 16-byte aligned   */
+} kvq_cache;
+
+/* Version of this ABI (KVQ_ABI_VERSION). */
+int kvq_abi_version(void);
+
+/* Bytes of one page across all kv heads: num_kv_heads * 2176; 0 if `cache` is invalid. */
+size_t kvq_page_bytes(const kvq_cache* cache);
+
+/*
+ * kvq_append -- fused rotate + 4-bit quantize + paged write of new K and V tokens.
+ * (SAW-INT4 summary, "Summary": a fused rotation-quantization kernel writing directly into
+ * paged KV-cache layouts.)
+ *
+ *   k, v         device, [num_tokens][num_kv_heads][128], dtype kv_dtype (KVQ_F16 or
+ *                KVQ_BF16), contiguous, 16-byte aligned.
+ *   cu_new       device int32[num_seqs+1], non-decreasing, cu_new[0] = 0 and
+ *                cu_new[num_seqs] <= num_tokens: tokens cu_new[b]..cu_new[b+1]-1 belong to
+ *                sequence b.
+ *   start_pos    device int32[num_seqs]: position of sequence b's first new token.  Token i
+ *                goes to position p = start_pos[b] + i - cu_new[b], i.e. page
+ *                block_table[b*max_pages + p/16], slot p%16.
+ *   block_table  device int32[num_seqs][max_pages]; entries used must be < num_pages.
+ *   max_new_tokens  host hint: >= every cu_new[b+1]-cu_new[b] (sizes the grid); tokens
+ *                beyond it are not written.
+ * Writes each vector's 64 code bytes and 4 parameter bytes; nothing else in the pool.
+ * Positions appended by one call must be distinct.
+ */
+int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype,
+               int32_t num_tokens, int32_t num_seqs, const int32_t* cu_new,
+               const int32_t* start_pos, const int32_t* block_table, int32_t max_pages,
+               int32_t max_new_tokens, void* stream);
+
+/*
+ * Bytes of workspace kvq_decode_attn needs for these sizes (same arguments as there).
+ * The workspace holds split partials and one counter per (sequence, kv head).  It must be
+ * zero-filled once before its first use; every call leaves the counters at zero again.
+ * Returns 0 when no workspace is needed (then `workspace` may be NULL), or (size_t)-1 on
+ * invalid arguments.
+ */
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_q_heads,
+                                  int32_t num_seqs, int32_t max_seq_len);
+
+/*
+ * kvq_decode_attn -- paged decode attention over the 4-bit cache, dequantizing in registers.
+ * (SAW-INT4 summary, "Summary": attention served straight from the paged 4-bit cache;
+ * UltraQuant: queries attend against FP4 KV tensors with group scales.)
+ *
+ *   q            device [num_seqs][num_q_heads][128], dtype q_dtype (F16, BF16, F32,
+ *                FP8_E4M3), contiguous.  The kernel uses q_scale * q.
+ *   num_q_heads  a multiple of num_kv_heads, with group G = num_q_heads/num_kv_heads <= 8;
+ *                query head h reads kv head h / G.
+ *   seq_lens     device int32[num_seqs]: tokens attended, positions [0, seq_lens[b]);
+ *                1 <= seq_lens[b] <= max_seq_len.
+ *   max_seq_len  host hint used to size the grid; must be <= max_pages*16.
+ *   sm_scale     softmax scale (1/sqrt(128) is the usual value).
+ *   out          device [num_seqs][num_q_heads][128], dtype out_dtype (F32, F16, BF16):
+ *                o = R_b * sum_t softmax_t(sm_scale * q'.k^'_t) v^'_t, or the rotated-basis
+ *                result with KVQ_OUT_ROTATED.
+ *   workspace    device, >= kvq_decode_workspace_bytes(...) bytes, zero-filled before first
+ *                use; do not share one workspace between streams.
+ * Decode does not append: a decode step is kvq_append then kvq_decode_attn on one stream.
+ */
+int kvq_decode_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, float q_scale,
+                    int32_t num_q_heads, int32_t num_seqs, const int32_t* seq_lens,
+                    int32_t max_seq_len, const int32_t* block_table, int32_t max_pages,
+                    float sm_scale, void* out, int32_t out_dtype, uint32_t flags,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_dequant_page -- dequantize whole pages (all 16 slots, all kv heads) to fp32.
+ *   page_ids     device int32[n], each < num_pages.
+ *   out_k, out_v device float[n][num_kv_heads][16][128]; channel order is natural.
+ *   flags        0: values in the rotated basis (y^ = scale*code + zero, one fp32 rounding,
+ *                or e2m1*2^(E-127) exactly); KVQ_UNROTATE: R_b * y^.
+ * Slots never written hold whatever bytes the pool had.
+ */
+int kvq_dequant_page(const kvq_cache* cache, const int32_t* page_ids, int32_t n,
+                     float* out_k, float* out_v, uint32_t flags, void* stream);
+
+/* Static description of a kvq_status. */
+const char* kvq_strerror(int status);
+
+/* Detail of the last error on the calling thread (empty string if none). */
+const char* kvq_last_error(void);
+
+/*
+ * kvq_hbm_copy -- plain device-to-device copy kernel (16-byte vector loads and stores).
+ * Not part of the method: it measures achievable HBM bandwidth and calibrates memory
+ * traffic counters.  bytes must be a multiple of 16; src and dst 16-byte aligned.
+ */
+int kvq_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,190 @@
+"""Parity of kvq_decode_attn and kvq_dequant_page with the oracle.
+
+The cache both sides read is written by the oracle (its bytes uploaded to the device),
+so the attention comparison runs on the same dequantized cache and no oracle input
+comes from the HIP path.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_kv_cache_02_amd import kvq, workloads as wl
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+QDT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.float8_e4m3fn}
+
+
+def oracle_cache(rng, lens, hkv, hb, fmt=oracle.FMT_INT4, permute=True, dist="llama", extra=2):
+    n_pages = [-(-int(n) // 16) for n in lens]
+    total = sum(n_pages) + extra
+    ids = rng.permutation(total) if permute else np.arange(total)
+    table = np.zeros((len(lens), max(n_pages)), np.int32)
+    off = 0
+    for b, n in enumerate(n_pages):
+        table[b, :n] = ids[off:off + n]
+        off += n
+    t = int(sum(lens))
+    k = rng.standard_normal((t, hkv, 128)).astype(np.float32)
+    v = (rng.standard_normal((t, hkv, 128)) * 0.5).astype(np.float32)
+    if dist == "llama":
+        k[:, :, [5, 60, 111]] *= 15
+    k = torch.from_numpy(k).bfloat16().float().numpy()
+    v = torch.from_numpy(v).bfloat16().float().numpy()
+    pool = np.full((total, hkv, 2176), 0x5A, np.uint8)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    oracle.append(pool, k, v, cu, np.zeros(len(lens), np.int64), table, hb, fmt)
+    return pool, table
+
+
+def run_decode(label, pool, table, lens, hq, hb, fmt=oracle.FMT_INT4, q=None, q_dtype="bf16",
+               q_scale=1.0, sm_scale=None, out_dtype=torch.float32, rotated=False, seed=0,
+               check=True):
+    print(f"[decode] {label}", flush=True)
+    rng = np.random.default_rng(seed)
+    b = len(lens)
+    if q is None:
+        q = rng.standard_normal((b, hq, 128)).astype(np.float32)
+    q = torch.from_numpy(q).to(QDT[q_dtype])
+    qnp = q.float().numpy()
+    hkv = pool.shape[1]
+    cache = kvq.Cache(pool.shape[0], hkv, hb, "int4" if fmt == oracle.FMT_INT4 else "mxfp4",
+                      pool=torch.from_numpy(pool).cuda())
+    max_len = int(max(lens))
+    out = kvq.decode_attn(cache, q.cuda(), torch.tensor(lens, dtype=torch.int32).cuda(),
+                          torch.from_numpy(table).cuda(), max_len, q_scale=q_scale,
+                          sm_scale=sm_scale, out_dtype=out_dtype, rotated=rotated)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    if not check:
+        return got
+    ref = oracle.decode_attention(pool, qnp, lens, table, hb, fmt, q_scale=q_scale,
+                                  sm_scale=sm_scale, out_rotated=rotated)
+    err = parity.attn_row_error(got, ref)
+    print(f"[decode] {label}: max row err {err.max():.3e}, p99.9 {np.quantile(err, 0.999):.3e}",
+          flush=True)
+    assert err.max() <= parity.ATTN_TOL, f"{label}: row error {err.max():.3e}"
+    return got
+
+
+def test_decode_tiny_workload():
+    w = wl.WORKLOADS["tiny"]
+    k, v = wl.sequence_kv(w, 0, 256)
+    pool = np.full((16, 1, 2176), 0x5A, np.uint8)
+    table = np.arange(16, dtype=np.int32)[None]
+    oracle.append(pool, k, v, np.array([0, 256]), np.array([0]), table, 64)
+    q = wl.queries(w)
+    run_decode("tiny", pool, table, [256], 4, 64, q=q, q_dtype="f16")
+
+
+@pytest.mark.parametrize("hb", [1, 64, 128])
+@pytest.mark.parametrize("group", [1, 4, 8])
+def test_decode_ragged(hb, group):
+    rng = np.random.default_rng(hb * 10 + group)
+    lens = [1, 15, 16, 17, 100, 257, 640]
+    hkv = 2
+    pool, table = oracle_cache(rng, lens, hkv, hb)
+    run_decode(f"ragged/b{hb}/G{group}", pool, table, lens, hkv * group, hb, seed=group)
+
+
+def test_decode_long_splits():
+    # long sequences: several workgroups per (sequence, kv head) and the in-kernel merge
+    rng = np.random.default_rng(21)
+    lens = [5000, 3333, 1024, 40]
+    pool, table = oracle_cache(rng, lens, 2, 64)
+    run_decode("long-splits", pool, table, lens, 8, 64)
+
+
+@pytest.mark.parametrize("q_dtype", ["f16", "f32", "e4m3"])
+def test_decode_query_dtypes(q_dtype):
+    rng = np.random.default_rng(22)
+    lens = [77, 300]
+    pool, table = oracle_cache(rng, lens, 2, 128)
+    run_decode(f"q-{q_dtype}", pool, table, lens, 8, 128, q_dtype=q_dtype, q_scale=0.7,
+               sm_scale=0.05)
+
+
+def test_decode_rotated_output_and_bf16():
+    rng = np.random.default_rng(23)
+    lens = [90, 31]
+    pool, table = oracle_cache(rng, lens, 2, 64)
+    run_decode("rotated", pool, table, lens, 8, 64, rotated=True)
+    f32 = run_decode("f32", pool, table, lens, 8, 64, seed=5)
+    bf = run_decode("bf16-out", pool, table, lens, 8, 64, seed=5, out_dtype=torch.bfloat16,
+                    check=False)
+    # bf16 output is the round-to-nearest-even of the fp32 result
+    assert np.array_equal(bf, torch.from_numpy(f32).bfloat16().float().numpy())
+
+
+def test_decode_outlier_scores_and_sharp_softmax():
+    # large sm_scale makes the softmax nearly one-hot: exercises the running-max rescale
+    rng = np.random.default_rng(24)
+    lens = [513, 64]
+    pool, table = oracle_cache(rng, lens, 1, 128)
+    run_decode("sharp", pool, table, lens, 4, 128, sm_scale=2.0)
+    run_decode("flat", pool, table, lens, 4, 128, sm_scale=1e-3)
+
+
+def test_decode_page_permutation_invariance_and_determinism():
+    rng = np.random.default_rng(25)
+    lens = [200, 45]
+    pool, table = oracle_cache(rng, lens, 2, 128, permute=False, extra=5)
+    q = rng.standard_normal((2, 8, 128)).astype(np.float32)
+    a = run_decode("perm-a", pool, table, lens, 8, 128, q=q, check=False)
+    a2 = run_decode("perm-a2", pool, table, lens, 8, 128, q=q, check=False)
+    perm = rng.permutation(pool.shape[0])
+    pool2 = np.empty_like(pool)
+    pool2[perm] = pool
+    b = run_decode("perm-b", pool2, perm[table].astype(np.int32), lens, 8, 128, q=q, check=False)
+    assert np.array_equal(a, a2)
+    assert np.array_equal(a, b)
+
+
+def test_decode_gqa_equal_queries_give_equal_rows():
+    rng = np.random.default_rng(26)
+    lens = [130]
+    pool, table = oracle_cache(rng, lens, 1, 64)
+    q = np.repeat(rng.standard_normal((1, 1, 128)).astype(np.float32), 4, axis=1)
+    out = run_decode("gqa-equal", pool, table, lens, 4, 64, q=q)
+    assert np.array_equal(out[0, 0], out[0, 3])
+
+
+def test_decode_workspace_reuse():
+    # the arrival counters are left at zero: repeated calls on one workspace agree
+    rng = np.random.default_rng(27)
+    lens = [3000, 2000]
+    pool, table = oracle_cache(rng, lens, 2, 64)
+    cache = kvq.Cache(pool.shape[0], 2, 64, pool=torch.from_numpy(pool).cuda())
+    q = torch.randn(2, 8, 128, generator=torch.Generator().manual_seed(1)).bfloat16().cuda()
+    sl = torch.tensor(lens, dtype=torch.int32).cuda()
+    bt = torch.from_numpy(table).cuda()
+    ws = kvq.make_workspace(cache, 8, 2, 3000)
+    assert ws is not None
+    outs = [kvq.decode_attn(cache, q, sl, bt, 3000, workspace=ws).cpu() for _ in range(4)]
+    for o in outs[1:]:
+        assert torch.equal(outs[0], o)
+    counters = ws[:2 * 2 * 4].cpu()
+    assert not counters.any()
+
+
+@pytest.mark.parametrize("hb", [64, 128])
+def test_dequant_pages(hb):
+    rng = np.random.default_rng(30 + hb)
+    lens = [40, 70]
+    pool, table = oracle_cache(rng, lens, 3, hb)
+    print(f"[dequant] b{hb}", flush=True)
+    cache = kvq.Cache(pool.shape[0], 3, hb, pool=torch.from_numpy(pool).cuda())
+    ids = np.array([table[0, 0], table[1, 4], table[1, 0], table[0, 2]], np.int32)
+    k, v = kvq.dequant_pages(cache, torch.from_numpy(ids).cuda())
+    kr, vr = oracle.dequant_pages(pool, ids, hb)
+    # rotated basis: one fp32 rounding of the exact s*c + z
+    assert np.array_equal(k.cpu().numpy(), kr.astype(np.float32))
+    assert np.array_equal(v.cpu().numpy(), vr.astype(np.float32))
+    ku, vu = kvq.dequant_pages(cache, torch.from_numpy(ids).cuda(), unrotate=True)
+    kur, vur = oracle.dequant_pages(pool, ids, hb, unrotate=True)
+    for got, ref in ((ku, kur), (vu, vur)):
+        got = got.cpu().numpy().astype(np.float64)
+        assert np.abs(got - ref).max() <= 1e-6 * np.abs(ref).max()
