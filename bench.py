@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated 4-bit paged KV-cache hot path on one MI355X.
+
+A step is one decode step of one Llama-3-8B-shaped attention layer: append the new
+token of each of 32 sequences into the paged INT4 cache (block-diagonal Hadamard
+b = 128, token-wise INT4), then decode attention of 32 query heads over 8 kv heads
+and 4096 cached tokens per sequence.  Steps cycle over 8 independent layer caches
+(8 x 143 MB) so that the 256 MB Infinity Cache cannot serve the pages.
+
+Printed: one JSON line with the whole-step algorithmic throughput (GB/s), the
+decode and append kernel times from HIP events on the launch stream, the decode
+kernel's roofline fraction against 8 TB/s, the measured copy bandwidth, the
+prefill-append throughput (64 x 2048 tokens, with and without rotation) and the
+CPU oracle's rate on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from bit_kv_cache_02_amd import kvq, workloads as wl  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+PAGE_HEAD = 2176
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "bit_kv_cache_02_amd", "csrc", "kvq_decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_step_bytes(w, lens, out_bytes=2):
+    kv = int(sum(lens)) * w.num_kv_heads * 136
+    q = w.batch * w.num_q_heads * 128 * 2
+    out = w.batch * w.num_q_heads * 128 * out_bytes
+    bt = int(sum(-(-int(n) // 16) for n in lens)) * 4 + w.batch * 4
+    return kv + q + out + bt
+
+
+def append_bytes(n_tokens, hkv, in_bytes=2):
+    return n_tokens * hkv * (2 * 128 * in_bytes + 2 * 68) + n_tokens * 4
+
+
+def build_layers(w, n_layers, dev):
+    """Prefill n_layers caches with the workload's 4095 cached tokens per sequence (on the GPU)."""
+    lens = wl.seq_lens(w)
+    table, num_pages = wl.block_table(w, lens)
+    data = wl.decode_step_inputs(w)
+    k = torch.from_numpy(np.concatenate(data["prefix_k"])).to(torch.bfloat16).to(dev)
+    v = torch.from_numpy(np.concatenate(data["prefix_v"])).to(torch.bfloat16).to(dev)
+    pre = lens - 1
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(pre)]), dtype=torch.int32, device=dev)
+    start0 = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    bt = torch.from_numpy(table).to(dev)
+    caches = []
+    for _ in range(n_layers):
+        c = kvq.Cache(num_pages, w.num_kv_heads, w.had_block, device=dev)
+        kvq.append(c, k, v, cu, start0, bt, int(pre.max()))
+        caches.append(c)
+    torch.cuda.synchronize()
+    del k, v
+    step = {
+        "k": torch.from_numpy(data["new_k"]).to(torch.bfloat16).to(dev),
+        "v": torch.from_numpy(data["new_v"]).to(torch.bfloat16).to(dev),
+        "cu": torch.arange(w.batch + 1, dtype=torch.int32, device=dev),
+        "start": torch.from_numpy(pre.astype(np.int32)).to(dev),
+        "q": torch.from_numpy(wl.queries(w)).to(torch.bfloat16).to(dev),
+        "lens": torch.from_numpy(lens.astype(np.int32)).to(dev),
+        "bt": bt,
+    }
+    return caches, step, lens, table
+
+
+def time_decode_steps(w, caches, step, lens, steps, warmup):
+    dev = step["q"].device
+    max_len = int(lens.max())
+    ws = kvq.make_workspace(caches[0], w.num_q_heads, w.batch, max_len, dev)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+
+    def one(i):
+        c = caches[i % len(caches)]
+        kvq.append(c, step["k"], step["v"], step["cu"], step["start"], step["bt"], 1)
+        ev[i][1].record()
+        kvq.decode_attn(c, step["q"], step["lens"], step["bt"], max_len, out=out, workspace=ws)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps + warmup)]
+    for i in range(warmup):
+        ev[i][0].record()
+        one(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warmup, warmup + steps):
+        ev[i][0].record()
+        one(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    app = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup, warmup + steps)]) * 1e3
+    dec = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(warmup, warmup + steps)]) * 1e3
+    return wall, app, dec
+
+
+def time_prefill_append(dev, repeats=10):
+    """64 x 2048 heavy-tailed bf16 tokens into 2 alternating pools; rotation b=128 vs none."""
+    w = wl.WORKLOADS["prefill"]
+    lens = wl.seq_lens(w)
+    table, num_pages = wl.block_table(w, lens)
+    ks, vs = [], []
+    for b in range(w.batch):
+        k, v = wl.sequence_kv(w, b, int(lens[b]))
+        ks.append(torch.from_numpy(k).to(torch.bfloat16))
+        vs.append(torch.from_numpy(v).to(torch.bfloat16))
+    k = torch.cat(ks).to(dev)
+    v = torch.cat(vs).to(dev)
+    del ks, vs
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    start = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    bt = torch.from_numpy(table).to(dev)
+    res = {}
+    for hb in (128, 1):
+        pools = [kvq.Cache(num_pages, w.num_kv_heads, hb, device=dev) for _ in range(2)]
+        for c in pools:
+            kvq.append(c, k, v, cu, start, bt, int(lens.max()))
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(repeats)]
+        for i in range(repeats):
+            evs[i][0].record()
+            kvq.append(pools[i % 2], k, v, cu, start, bt, int(lens.max()))
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        res[hb] = float(np.median([a.elapsed_time(b) for a, b in evs]) * 1e3)
+        del pools
+    n_tok = int(lens.sum())
+    nbytes = append_bytes(n_tok, w.num_kv_heads)
+    return {
+        "workload": "prefill append: 64 seqs x 2048 new tokens, 8 kv heads, bf16 Student-t(3), page 16",
+        "us_rotated_b128": round(res[128], 2),
+        "us_plain_int4": round(res[1], 2),
+        "rotation_overhead_pct": round(100.0 * (res[128] / res[1] - 1.0), 2),
+        "GBps": round(nbytes / res[128] / 1e3, 1),
+        "tokens_per_s": round(n_tok / res[128] * 1e6, 1),
+        "frac_of_hbm_peak": round(nbytes / res[128] / 1e3 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": nbytes,
+    }
+
+
+def hbm_copy_probe(dev, nbytes=1 << 30, repeats=10):
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    kvq.hbm_copy(src, dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(repeats):
+        kvq.hbm_copy(src, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / repeats
+    return 2 * nbytes / us / 1e3
+
+
+def cpu_baseline(w, budget_s=12.0, n_seqs=4):
+    """The oracle's decode step (append the new token + decode attention) on a sample of
+    n_seqs whole sequences of the same workload, repeated until budget_s of CPU time."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    seqs = list(range(n_seqs))
+    data = wl.decode_step_inputs(w, seqs=seqs)
+    lens = data["lens"][:n_seqs]
+    sub = wl.small_variant(w, n_seqs, int(lens[0]))
+    table, num_pages = wl.block_table(sub, lens)
+    pool = np.zeros((num_pages, w.num_kv_heads, PAGE_HEAD), np.uint8)
+    pre = lens - 1
+    oracle.append(pool, np.concatenate([data["prefix_k"][b] for b in seqs]),
+                  np.concatenate([data["prefix_v"][b] for b in seqs]),
+                  np.concatenate([[0], np.cumsum(pre)]), np.zeros(n_seqs, np.int64), table, w.had_block)
+    q = wl.queries(w)[:n_seqs]
+    nk = data["new_k"][:n_seqs]
+    nv = data["new_v"][:n_seqs]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.append(pool, nk, nv, np.arange(n_seqs + 1), pre, table, w.had_block)
+        oracle.decode_attention(pool, q, lens, table, w.had_block)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    sub_bytes = decode_step_bytes(sub, lens) + append_bytes(n_seqs, w.num_kv_heads)
+    return {
+        "value": round(sub_bytes * reps / el / 1e9, 5),
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{n_seqs} of {w.batch} sequences (all 32 q / 8 kv heads, context 4096), "
+                  f"append of the step token + decode attention, repeated {reps}x in {el:.1f} s; "
+                  f"host os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}",
+    }
+
+
+def traffic_entry(algo_bytes):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if still current."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+        if rec.get("decode_source_sha256") != src:
+            return None
+        return int(rec["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    kvq.lib()
+    w = wl.WORKLOADS["llama"]
+    log("[bench] building 8 layer caches (llama shape)")
+    caches, step, lens, _ = build_layers(w, args.layers, dev)
+    log("[bench] timing decode steps")
+    wall, app_us, dec_us = time_decode_steps(w, caches, step, lens, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    dbytes = decode_step_bytes(w, lens)
+    abytes = append_bytes(w.batch, w.num_kv_heads)
+    step_bytes = dbytes + abytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_mean = float(dec_us.mean())
+    achieved = dbytes / dec_mean / 1e3
+    from bit_kv_cache_02_amd.kvq import decode_workspace_bytes
+    res = {
+        "metric": "INT4-KV append GB/s + paged INT4 decode-attn us/step, % of HBM peak",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic (seeded; K ~ N(0,1) with 3 outlier channels x15 per kv head, V ~ N(0,0.5), q ~ N(0,1), bf16)",
+        "config": {
+            "workload": "Llama-3-8B layer decode step: batch 32 x context 4096, 32 q / 8 kv heads, "
+                        "head_dim 128, page 16, bf16 K/V/q, token-wise INT4 (fp16 scale+zero), Hadamard "
+                        "block 128; append 1 token per sequence + decode attention; 8 layer caches cycled",
+            "batch": w.batch, "context": int(lens[0]), "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads, "had_block": w.had_block, "layers_cycled": args.layers,
+            "out_dtype": "bf16",
+        },
+        "decode_us": round(dec_mean, 3),
+        "decode_us_median": round(float(np.median(dec_us)), 3),
+        "decode_GBps": round(achieved, 1),
+        "append_step_us": round(float(app_us.mean()), 3),
+        "append_step_GBps": round(abytes / float(app_us.mean()) / 1e3, 2),
+        "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": {"decode": dbytes, "append_step": abytes},
+        "decode_workspace_bytes": decode_workspace_bytes(caches[0], w.num_q_heads, w.batch, int(lens.max())),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel<0> (kvq_decode_attn, INT4)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_entry(dbytes),
+        },
+    }
+    log("[bench] HBM copy probe")
+    res["hbm_copy_GBps"] = round(hbm_copy_probe(dev), 1)
+    res["decode_frac_of_copy_bw"] = round(achieved / res["hbm_copy_GBps"], 4)
+    del caches
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        log("[bench] prefill append")
+        res["prefill_append"] = time_prefill_append(dev)
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -3,8 +3,12 @@
     python -m bit_kv_cache_02_amd.build        (or build() from Python)
 
 Every HIP source is compiled for gfx950 only; packed-fp32 instructions are
-disabled (-Xclang -target-feature -Xclang -packed-fp32-ops), and fast-math stays
-off so that divisions and the round-to-nearest tricks keep IEEE semantics.
+disabled (-Xclang -target-feature -Xclang -packed-fp32-ops).  MFMA accumulators
+live in ordinary VGPRs (-amdgpu-mfma-vgpr-form), so the VALU can rescale them
+without AGPR copies.  Kernels run with the IEEE mode bit off and NaNs assumed
+absent (-fno-honor-nans -mno-amdgpu-ieee): min/max then need no NaN
+canonicalisation and fuse with DPP moves.  Fast-math stays off, so divisions,
+rounding and the add-then-subtract rounding tricks keep IEEE semantics.
 """
 import os
 import subprocess
@@ -17,6 +21,8 @@ SOURCES = ["kvq_host.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_dequant.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+         "-fno-honor-nans", "-mno-amdgpu-ieee",
          "-Wall", "-Wno-unused-function"]
 
 

@@ -2,7 +2,7 @@
 // registers (SAW-INT4 summary, "Summary": attention served from paged 4-bit KV; UltraQuant
 // article, section on how the method works: queries attend over 4-bit KV with group scales).
 //
-// A workgroup (4 waves) owns one (sequence, kv head, split): a run of pages of one sequence.
+// A workgroup (W waves) owns one (sequence, kv head, split): a run of pages of one sequence.
 // Per page (16 tokens x 128 channels, one 2176-byte page-head block) each wave does:
 //   scores   S[g][t] = sk_t * (q'_g . c_t) + zk_t * sum(q'_g)      (INT4: y^ = s*c + z)
 //            q'_g . c_t runs on v_mfma_i32_16x16x64_i8 straight on the 4-bit codes: q' is held as
@@ -16,9 +16,11 @@
 //            ~22 bits of it.
 // The page layout puts V codes of four consecutive tokens in one 32-bit word per row byte, which
 // is the B-operand shape of the p.V MFMA, so one 16-byte load per lane feeds it directly.
-// The waves' partials merge in LDS; with several splits per (sequence, kv head) the last
-// workgroup to finish merges the splits (arrival counter in the workspace).  The output is
-// rotated back with an in-LDS fp32 Walsh-Hadamard butterfly.
+// Each wave streams its pages through a register prefetch pipeline (the query loads and the
+// first page loads are issued before anything waits).  The waves' partials merge in LDS; when a
+// (sequence, kv head) is split over several workgroups, a second small kernel merges the split
+// partials.  The query rotation and the final rotation back run in fp32 in registers, one head per
+// wave, with lane shuffles for the cross-lane butterfly stages.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -28,49 +30,169 @@ namespace kvq {
 
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kMaxG = 8;
 constexpr float kNegBig = -1.0e30f;
 
+template <int W>
 struct DecodeSmem {
-  float qf[kMaxG][kHeadDim];
+  // q' limbs in the byte order of the q.K A tile: [limb][g][a2][jg][16 bytes]
+  uint8_t qlimb[2][kMaxG][2][4][16];
   float qdelta[kMaxG];
   float qsum[kMaxG];
-  float ptile[kWaves][kMaxG][kPage];
-  float wo[kWaves][kMaxG][kHeadDim];
-  float wm[kWaves][kMaxG];
-  float wl[kWaves][kMaxG];
-  int is_last;
+  _Float16 ptile[W][2 * kMaxG][kPage];  // p~ split into fp16 high/low parts, A-tile rows 2g+limb
+  float wo[W][kMaxG][kHeadDim];
+  float wm[W][kMaxG];
+  float wl[W][kMaxG];
 };
 
 __device__ __forceinline__ float inv_sqrt_block(int hb) {
   return hb == 128 ? 0.08838834764831845f : (hb == 64 ? 0.125f : 1.0f);
 }
 
-// In-place unnormalised Walsh-Hadamard transform of G rows of 128 floats in LDS over blocks of hb
-// channels (natural Sylvester order).  Callers synchronise before; returns synchronised.
-__device__ void fwht_rows(float* x, int rows, int hb, int tid, int nthreads) {
-  for (int len = 1; len < hb; len <<= 1) {
-    for (int i = tid; i < rows * 64; i += nthreads) {
-      const int g = i >> 6, k = i & 63;
-      const int jj = (k / len) * 2 * len + (k % len);
-      float* r = x + g * kHeadDim;
-      const float u = r[jj], v = r[jj + len];
-      r[jj] = u + v;
-      r[jj + len] = u - v;
-    }
-    __syncthreads();
+// Walsh-Hadamard transform of one 128-vector held by a wave, element `lane` in x0 and element
+// `lane + 64` in x1 (unnormalised, blocks of hb channels, natural Sylvester order).  Cross-lane
+// stages use lane shuffles, so no workgroup barrier is needed.
+__device__ __forceinline__ void fwht_wave(float& x0, float& x1, int hb, int lane) {
+  for (int len = 1; len < hb && len < 64; len <<= 1) {
+    const float y0 = __shfl_xor(x0, len), y1 = __shfl_xor(x1, len);
+    const bool upper = (lane & len) != 0;
+    x0 = upper ? y0 - x0 : x0 + y0;
+    x1 = upper ? y1 - x1 : x1 + y1;
   }
+  if (hb == 128) {
+    const float t = x0;
+    x0 = t + x1;
+    x1 = t - x1;
+  }
+}
+
+struct PageData {
+  u32x4 k;      // K row bytes 16*jg..16*jg+15 of token n
+  u32x4 v;      // V words: row bytes 4n..4n+3 of tokens 4jg..4jg+3
+  uint32_t kp;  // K params of token n
+  uint32_t vp;  // V params of token n
+};
+
+// `base` is wave-uniform: the buffer descriptor lives in scalar registers and the per-lane offsets
+// are loop invariant, so a page costs no vector address arithmetic.
+__device__ __forceinline__ PageData load_page(const uint8_t* base, int koff, int voff, int poff) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, kPageHeadBytes);
+  PageData d;
+  // cache policy 2 = nontemporal: the pages are streamed once per step
+  d.k = __builtin_amdgcn_raw_buffer_load_b128(r, koff, 0, 2);
+  d.v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2);
+  d.kp = __builtin_amdgcn_raw_buffer_load_b32(r, poff, kKParamsOff, 2);
+  d.vp = __builtin_amdgcn_raw_buffer_load_b32(r, poff, kVParamsOff, 2);
+  return d;
+}
+
+// Per-wave streaming state.
+struct WaveState {
+  float m0, m1, l0, l1, pz0, pz1;
+  f32x4 acc[8];
+};
+
+__device__ __forceinline__ void process_page(const PageData& pg, int valid, WaveState& s, const i32x4 (&qa)[2],
+                                             float alpha0, float beta0, float alpha1, float beta1,
+                                             bool has0, bool has1, int n, int jg, bool a_row_used,
+                                             _Float16 (*ptile)[kPage]) {
+  const uint32_t M4 = 0x0F0F0F0Fu, M16 = 0x000F000Fu;
+  const bool tv = n < valid;
+
+  // q'.c_t on the integer matrix cores
+  const i32x4 kb0 = i32x4{(int)(pg.k[0] & M4), (int)(pg.k[1] & M4), (int)(pg.k[2] & M4), (int)(pg.k[3] & M4)};
+  const i32x4 kb1 = i32x4{(int)((pg.k[0] >> 4) & M4), (int)((pg.k[1] >> 4) & M4), (int)((pg.k[2] >> 4) & M4),
+                          (int)((pg.k[3] >> 4) & M4)};
+  i32x4 sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], kb0, i32x4{0, 0, 0, 0}, 0, 0, 0);
+  sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], kb1, sc, 0, 0, 0);
+
+  const float sk = f16_bits_to_f32(pg.kp & 0xFFFFu), zk = f16_bits_to_f32(pg.kp >> 16);
+  float x0 = fmaf((float)(sc[0] * 256 + sc[1]) * alpha0, sk, zk * beta0);
+  float x1 = fmaf((float)(sc[2] * 256 + sc[3]) * alpha1, sk, zk * beta1);
+  x0 = tv ? x0 : -INFINITY;
+  x1 = tv ? x1 : -INFINITY;
+
+  const float pm0 = row_max16(x0), pm1 = row_max16(x1);
+  const float sv = f16_bits_to_f32(pg.vp & 0xFFFFu), zv = f16_bits_to_f32(pg.vp >> 16);
+  // The reference max m only moves when a score exceeds it by more than 2^8 (or when p~ = p * sv
+  // could leave the fp16 range): any m gives the same softmax, and p <= 2^8 keeps the fp16 and
+  // fp32 partial sums in range.  exp2 of very negative arguments may flush to zero: harmless here.
+  if (__any(pm0 > s.m0 + 8.0f || pm1 > s.m1 + 8.0f || ((pm0 > s.m0 || pm1 > s.m1) && sv > 128.0f))) {
+    const float mn0 = fmaxf(s.m0, pm0), mn1 = fmaxf(s.m1, pm1);
+    const float f0 = __builtin_amdgcn_exp2f(s.m0 - mn0), f1 = __builtin_amdgcn_exp2f(s.m1 - mn1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s.acc[i][0] *= f0;
+      s.acc[i][1] *= f0;
+      s.acc[i][2] *= f1;
+      s.acc[i][3] *= f1;
+    }
+    s.l0 *= f0;
+    s.l1 *= f1;
+    s.pz0 *= f0;
+    s.pz1 *= f1;
+    s.m0 = mn0;
+    s.m1 = mn1;
+  }
+  const float p0 = __builtin_amdgcn_exp2f(x0 - s.m0), p1 = __builtin_amdgcn_exp2f(x1 - s.m1);
+  s.l0 += p0;
+  s.l1 += p1;
+  s.pz0 = tv ? fmaf(p0, zv, s.pz0) : s.pz0;
+  s.pz1 = tv ? fmaf(p1, zv, s.pz1) : s.pz1;
+
+  // p~ = p * sv as fp16 high + low parts, stored at A-tile rows 2g+limb in the k order of the
+  // V words (tokens 0, 2, 1, 3 of each quad: bits 0 and 1 of the token swapped)
+  const float pt0 = tv ? p0 * sv : 0.0f, pt1 = tv ? p1 * sv : 0.0f;
+  const _Float16 h0 = (_Float16)pt0, h1 = (_Float16)pt1;
+  const _Float16 r0 = (_Float16)(pt0 - (float)h0), r1 = (_Float16)(pt1 - (float)h1);
+  const int pos = (n & ~3) | ((n & 1) << 1) | ((n >> 1) & 1);
+  if (has0) {
+    ptile[4 * jg + 0][pos] = h0;
+    ptile[4 * jg + 1][pos] = r0;
+  }
+  if (has1) {
+    ptile[4 * jg + 2][pos] = h1;
+    ptile[4 * jg + 3][pos] = r1;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const f16x4 pa = a_row_used ? *(const f16x4*)&ptile[n][4 * jg] : f16x4{0, 0, 0, 0};
+  __builtin_amdgcn_wave_barrier();
+
+  // V codes as fp16 subnormals: word q of the lane holds row byte 4n+q of 4 tokens.  Low nibbles
+  // (channel n+32q) enter as c*2^-24, high nibbles (channel n+32q+16) are masked in place and
+  // enter as 16c*2^-24; their accumulators carry that factor 16 until the end.
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t Y = pg.v[q], Y8 = Y >> 8;
+    const f16x4 blo = __builtin_bit_cast(f16x4, u32x2{Y & M16, Y8 & M16});          // tokens 0,2 | 1,3
+    const f16x4 bhi = __builtin_bit_cast(f16x4, u32x2{Y & (M16 << 4), Y8 & (M16 << 4)});
+    s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, blo, s.acc[2 * q], 0, 0, 0);
+    s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bhi, s.acc[2 * q + 1], 0, 0, 0);
+  }
+}
+
+// Rotate one head's normalised o' (element lane in o0, lane + 64 in o1) back and store it.
+__device__ __forceinline__ void store_head(const DecodeParams& a, float o0, float o1, int b, int h, int lane) {
+  float scale = 1.0f;
+  if (!a.out_rotated) {
+    fwht_wave(o0, o1, a.had_block, lane);
+    scale = inv_sqrt_block(a.had_block);
+  }
+  const int64_t base = ((int64_t)b * a.hq + h) * kHeadDim;
+  store_elem(a.out, base + lane, a.out_dtype, o0 * scale);
+  store_elem(a.out, base + lane + 64, a.out_dtype, o1 * scale);
 }
 
 }  // namespace
 
-template <int FMT>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
-  __shared__ DecodeSmem sm;
+template <int FMT, int W, int D>
+__global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
+  __shared__ DecodeSmem<W> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nsplit = a.plan.nsplit;
   const int P = a.plan.pages_per_split;
   const int split = blockIdx.x % nsplit;
@@ -78,256 +200,227 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
   const int kvh = unit % a.hkv;
   const int b = unit / a.hkv;
   const int G = a.group;
+  const float isb = inv_sqrt_block(a.had_block);
+  const int n = lane & 15;   // token (QK, softmax) / output column (p.V)
+  const int jg = lane >> 4;  // row group: heads 2jg, 2jg+1
+
+  // ---- 0. query loads first (they depend on nothing); wave w holds heads w, w+W, ... ----
+  constexpr int kMaxHeadsPerWave = (kMaxG + W - 1) / W;
+  float qv[kMaxHeadsPerWave][2];
+#pragma unroll
+  for (int k = 0; k < kMaxHeadsPerWave; ++k) {
+    const int g = wave + k * W;
+    qv[k][0] = qv[k][1] = 0.0f;
+    if (g < G) {
+      const int64_t qb = ((int64_t)b * a.hq + kvh * G + g) * kHeadDim;
+      qv[k][0] = load_elem(a.q, qb + lane, a.q_dtype);
+      qv[k][1] = load_elem(a.q, qb + lane + 64, a.q_dtype);
+    }
+  }
+
+  // Pages are dealt to the waves round-robin (wave w takes pages p_begin + w + W*i), so the block
+  // table entries a wave needs do not depend on the sequence length and load alongside it.
+  const int p_begin = split * P;
+  const int pw0 = p_begin + wave;
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  const int bt_idx = pw0 + W * lane;
+  const int pid_vec = (lane * W < P && bt_idx < a.max_pages) ? bt[bt_idx] : 0;
   const int L = a.seq_lens[b];
   const int n_pages = (L + kPage - 1) / kPage;
-  const int p_begin = split * P;
   if (p_begin >= n_pages) return;  // uniform over the workgroup
   const int p_end = min(p_begin + P, n_pages);
   const int nsplit_b = (n_pages + P - 1) / P;
-  const float isb = inv_sqrt_block(a.had_block);
 
-  // ---- 1. q' = R_b (q_scale q) for the G query heads of this kv head ----
-  for (int i = tid; i < G * kHeadDim; i += 256) {
-    const int g = i >> 7, d = i & 127;
-    sm.qf[g][d] = a.q_scale * load_elem(a.q, ((int64_t)b * a.hq + kvh * G + g) * kHeadDim + d, a.q_dtype);
-  }
-  __syncthreads();
-  fwht_rows(&sm.qf[0][0], G, a.had_block, tid, 256);
-
-  // ---- 2. q' as 16-bit fixed point per head: q' ~= delta_g * Q, |Q| <= 32000 ----
-  for (int g = wave; g < G; g += kWaves) {
-    const float v0 = sm.qf[g][lane] * isb, v1 = sm.qf[g][lane + 64] * isb;
-    const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-    const float delta = amax > 0.0f ? amax / 32000.0f : 1.0f;
-    const int q0 = (int)rintf(v0 / delta), q1 = (int)rintf(v1 / delta);
-    const int qs = wave_sum_i(q0 + q1);
-    sm.qf[g][lane] = (float)q0;
-    sm.qf[g][lane + 64] = (float)q1;
-    if (lane == 0) {
-      sm.qdelta[g] = delta;
-      sm.qsum[g] = delta * (float)qs;  // sum of the q' actually used
-    }
-  }
-  __syncthreads();
-
-  const int n = lane & 15;     // token (QK, softmax) / output column (p.V)
-  const int jg = lane >> 4;    // row group: heads 2jg, 2jg+1
-  const int ga = n >> 1;       // A-tile row 2g+limb -> head of this lane's A row
-  const int limb = n & 1;      // 0: high limb / high fp16 part, 1: low
-  // A tile of the q.K MFMA: byte p = 4w+q2 of operand a2 is channel (4jg+w) + 32q2 + 16a2, which is
-  // where the K row word that lane group jg loads keeps that channel after the nibble split.
-  i32x4 qa[2];
-#pragma unroll
-  for (int a2 = 0; a2 < 2; ++a2) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t word = 0;
-      if (ga < G) {
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const int Q = (int)sm.qf[ga][4 * jg + w + 32 * q2 + 16 * a2];
-          const int hi = (Q + 128) >> 8;
-          const int lo = Q - 256 * hi;
-          word |= (uint32_t)((limb == 0 ? hi : lo) & 255) << (8 * q2);
-        }
-      }
-      qa[a2][w] = (int)word;
-    }
-  }
-  const int g0 = 2 * jg, g1 = 2 * jg + 1;
-  const bool has0 = g0 < G, has1 = g1 < G;
-  const float c2 = a.sm_scale_log2;
-  const float alpha0 = has0 ? sm.qdelta[g0] * c2 : 0.0f, beta0 = has0 ? sm.qsum[g0] * c2 : 0.0f;
-  const float alpha1 = has1 ? sm.qdelta[g1] * c2 : 0.0f, beta1 = has1 ? sm.qsum[g1] * c2 : 0.0f;
-
-  // ---- 3. stream this wave's pages ----
-  const int chunk = (p_end - p_begin + kWaves - 1) / kWaves;
-  const int wp0 = p_begin + wave * chunk;
-  const int wp1 = min(wp0 + chunk, p_end);
-  float mrun0 = kNegBig, mrun1 = kNegBig;
-  float l0 = 0.f, l1 = 0.f, pz0 = 0.f, pz1 = 0.f;
-  f32x4 acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
-  const int64_t head_off = (int64_t)kvh * kPageHeadBytes;
+  // ---- 1. this wave's pages; start the first loads before the query math ----
+  const int npw = max(0, (p_end - pw0 + W - 1) / W);  // <= 64 (planned: P <= 64 W)
+  const uint8_t* pool_h = a.pool + (int64_t)kvh * kPageHeadBytes;
   const int64_t page_stride = (int64_t)a.hkv * kPageHeadBytes;
-  const uint32_t M4 = 0x0F0F0F0Fu, M16 = 0x000F000Fu;
-
-  for (int p = wp0; p < wp1; ++p) {
-    const uint8_t* base = a.pool + (int64_t)bt[p] * page_stride + head_off;
-    const u32x4 kv4 = *(const u32x4*)(base + 64 * n + 16 * jg);
-    const u32x4 vv4 = *(const u32x4*)(base + kVCodesOff + 16 * lane);
-    const uint32_t kp = *(const uint32_t*)(base + kKParamsOff + 4 * n);
-    const uint32_t vp = *(const uint32_t*)(base + kVParamsOff + 4 * n);
-    const bool tv = n < L - p * kPage;
-
-    // q'.c_t on the integer matrix cores
-    const i32x4 kb0 = i32x4{(int)(kv4[0] & M4), (int)(kv4[1] & M4), (int)(kv4[2] & M4), (int)(kv4[3] & M4)};
-    const i32x4 kb1 = i32x4{(int)((kv4[0] >> 4) & M4), (int)((kv4[1] >> 4) & M4), (int)((kv4[2] >> 4) & M4),
-                            (int)((kv4[3] >> 4) & M4)};
-    i32x4 s = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], kb0, i32x4{0, 0, 0, 0}, 0, 0, 0);
-    s = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], kb1, s, 0, 0, 0);
-
-    const float sk = f16_bits_to_f32(kp & 0xFFFFu), zk = f16_bits_to_f32(kp >> 16);
-    float x0 = fmaf((float)(s[0] * 256 + s[1]) * alpha0, sk, zk * beta0);
-    float x1 = fmaf((float)(s[2] * 256 + s[3]) * alpha1, sk, zk * beta1);
-    x0 = tv ? x0 : -INFINITY;
-    x1 = tv ? x1 : -INFINITY;
-
-    const float mn0 = fmaxf(mrun0, row_max16(x0));
-    const float mn1 = fmaxf(mrun1, row_max16(x1));
-    const float f0 = exp2f(mrun0 - mn0), f1 = exp2f(mrun1 - mn1);
-    if (__any(f0 < 1.0f || f1 < 1.0f)) {
+  auto page_base = [&](int i) {
+    // uniform by construction; readfirstlane makes that explicit so the buffer descriptor stays in
+    // scalar registers
+    const uint64_t addr = (uint64_t)(pool_h + (int64_t)__builtin_amdgcn_readlane(pid_vec, i) * page_stride);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+  };
+  const int koff = 64 * n + 16 * jg, voff = kVCodesOff + 16 * lane, poff = 4 * n;
+  constexpr int NB = D + 1;  // register buffers: D pages in flight plus the one being processed
+  PageData st[NB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc[i][0] *= f0;
-        acc[i][1] *= f0;
-        acc[i][2] *= f1;
-        acc[i][3] *= f1;
-      }
-    }
-    mrun0 = mn0;
-    mrun1 = mn1;
-    const float p0 = exp2f(x0 - mn0), p1 = exp2f(x1 - mn1);
-    const float sv = f16_bits_to_f32(vp & 0xFFFFu), zv = f16_bits_to_f32(vp >> 16);
-    l0 = fmaf(l0, f0, p0);
-    l1 = fmaf(l1, f1, p1);
-    pz0 = tv ? fmaf(p0, zv, pz0 * f0) : pz0 * f0;
-    pz1 = tv ? fmaf(p1, zv, pz1 * f1) : pz1 * f1;
+  for (int d = 0; d < D; ++d)
+    if (d < npw) st[d] = load_page(page_base(d), koff, voff, poff);
 
-    // p~ = p * sv, moved from the (token-lane) softmax layout to the A layout of the p.V MFMA
-    if (has0) sm.ptile[wave][g0][n] = tv ? p0 * sv : 0.0f;
-    if (has1) sm.ptile[wave][g1][n] = tv ? p1 * sv : 0.0f;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    f16x4 pa = f16x4{0, 0, 0, 0};
-    if (ga < G) {
-      const f32x4 pv = *(const f32x4*)&sm.ptile[wave][ga][4 * jg];
-      const float v4[4] = {pv[0], pv[2], pv[1], pv[3]};  // k order of the V words: t0, t2, t1, t3
+  // ---- 2. q' = R_b (q_scale q) in registers, then 16-bit fixed point q' ~= delta_g * Q with
+  //         |Q| <= 32000, stored as two int8 limbs (Q = 256*hi + lo) in the A-tile byte order ----
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const _Float16 hi = (_Float16)v4[i];
-        pa[i] = limb == 0 ? hi : (_Float16)(v4[i] - (float)hi);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // V codes as fp16 subnormals c*2^-24: word q of the lane holds row byte 4n+q of 4 tokens
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t Y = vv4[q];
+  for (int k = 0; k < kMaxHeadsPerWave; ++k) {
+    const int g = wave + k * W;
+    if (g < G) {
+      float v0 = qv[k][0] * a.q_scale, v1 = qv[k][1] * a.q_scale;
+      fwht_wave(v0, v1, a.had_block, lane);
+      v0 *= isb;
+      v1 *= isb;
+      const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+      const float delta = amax > 0.0f ? amax / 32000.0f : 1.0f;
+      const int q0 = (int)rintf(v0 / delta), q1 = (int)rintf(v1 / delta);
+      const int qs = wave_sum_i(q0 + q1);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const uint32_t w0 = (Y >> (4 * e)) & M16;       // tokens 0, 2
-        const uint32_t w1 = (Y >> (8 + 4 * e)) & M16;   // tokens 1, 3
-        const f16x4 bv = __builtin_bit_cast(f16x4, u32x2{w0, w1});
-        acc[2 * q + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bv, acc[2 * q + e], 0, 0, 0);
+        const int ch = lane + 64 * e, Q = e ? q1 : q0;
+        const int hi = (Q + 128) >> 8, lo = Q - 256 * hi;
+        // channel (4jg + w) + 32q2 + 16a2 sits at byte 4w + q2 of operand a2, lane group jg
+        const int c16 = ch & 15, c_hi = ch >> 4;
+        uint8_t* dst = &sm.qlimb[0][g][c_hi & 1][c16 >> 2][4 * (c16 & 3) + (c_hi >> 1)];
+        dst[0] = (uint8_t)(hi & 255);
+        dst[sizeof(sm.qlimb[0])] = (uint8_t)(lo & 255);
+      }
+      if (lane == 0) {
+        sm.qdelta[g] = delta;
+        sm.qsum[g] = delta * (float)qs;  // sum of the q' actually used
+      }
+    }
+  }
+  __syncthreads();
+
+  const int ga = n >> 1;   // A-tile row 2g+limb -> head of this lane's A row
+  const int limb = n & 1;  // 0: high limb / high fp16 part, 1: low
+  const bool a_row_used = ga < G;
+  i32x4 qa[2];
+#pragma unroll
+  for (int a2 = 0; a2 < 2; ++a2)
+    qa[a2] = a_row_used ? *(const i32x4*)&sm.qlimb[limb][ga][a2][jg][0] : i32x4{0, 0, 0, 0};
+  const bool has0 = 2 * jg < G, has1 = 2 * jg + 1 < G;
+  const float c2 = a.sm_scale_log2;
+  const float alpha0 = has0 ? sm.qdelta[2 * jg] * c2 : 0.0f, beta0 = has0 ? sm.qsum[2 * jg] * c2 : 0.0f;
+  const float alpha1 = has1 ? sm.qdelta[2 * jg + 1] * c2 : 0.0f, beta1 = has1 ? sm.qsum[2 * jg + 1] * c2 : 0.0f;
+
+  // ---- 3. stream this wave's pages ----
+  WaveState s;
+  s.m0 = s.m1 = kNegBig;
+  s.l0 = s.l1 = s.pz0 = s.pz1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int valid0 = L - pw0 * kPage;
+  for (int i0 = 0; i0 < npw; i0 += NB) {
+#pragma unroll
+    for (int d = 0; d < NB; ++d) {
+      const int i = i0 + d;
+      if (i < npw) {
+        // page i sits in buffer d; page i + D goes to the buffer freed by page i - 1
+        if (i + D < npw) st[(d + D) % NB] = load_page(page_base(i + D), koff, voff, poff);
+        process_page(st[d], valid0 - i * W * kPage, s, qa, alpha0, beta0, alpha1, beta1, has0, has1, n, jg,
+                     a_row_used, sm.ptile[wave]);
       }
     }
   }
 
   // ---- 4. wave partial -> LDS ----
-  l0 = row_sum16(l0);
-  l1 = row_sum16(l1);
-  pz0 = row_sum16(pz0);
-  pz1 = row_sum16(pz1);
+  const float l0 = row_sum16(s.l0), l1 = row_sum16(s.l1);
+  const float pz0 = row_sum16(s.pz0), pz1 = row_sum16(s.pz1);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int ch = n + 32 * q + 16 * e;
-      const f32x4 v = acc[2 * q + e];
-      if (has0) sm.wo[wave][g0][ch] = 16777216.0f * (v[0] + v[1]) + pz0;
-      if (has1) sm.wo[wave][g1][ch] = 16777216.0f * (v[2] + v[3]) + pz1;
+      const f32x4 v = s.acc[2 * q + e];
+      const float sc = e ? 1048576.0f : 16777216.0f;  // 2^24, or 2^24/16 for the high nibbles
+      if (has0) sm.wo[wave][2 * jg][ch] = sc * (v[0] + v[1]) + pz0;
+      if (has1) sm.wo[wave][2 * jg + 1][ch] = sc * (v[2] + v[3]) + pz1;
     }
   }
   if (n == 0) {
-    if (has0) { sm.wm[wave][g0] = mrun0; sm.wl[wave][g0] = l0; }
-    if (has1) { sm.wm[wave][g1] = mrun1; sm.wl[wave][g1] = l1; }
+    if (has0) { sm.wm[wave][2 * jg] = s.m0; sm.wl[wave][2 * jg] = l0; }
+    if (has1) { sm.wm[wave][2 * jg + 1] = s.m1; sm.wl[wave][2 * jg + 1] = l1; }
   }
   __syncthreads();
 
-  // ---- 5. merge the waves; then either finish or hand over a split partial ----
-  float* fo = &sm.qf[0][0];  // reuse: final o' [G][128]
+  // ---- 5. merge the waves (wave w handles heads w, w+W, ...); finish, or write the split partial ----
   const int64_t slot = (int64_t)unit * nsplit + split;
-  for (int i = tid; i < G * kHeadDim; i += 256) {
-    const int g = i >> 7, ch = i & 127;
+  for (int g = wave; g < G; g += W) {
     float M = sm.wm[0][g];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][g]);
-    float O = 0.f, Ls = 0.f;
+    for (int w = 1; w < W; ++w) M = fmaxf(M, sm.wm[w][g]);
+    float O0 = 0.f, O1 = 0.f, Ls = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       const float f = exp2f(sm.wm[w][g] - M);
-      O = fmaf(f, sm.wo[w][g][ch], O);
+      O0 = fmaf(f, sm.wo[w][g][lane], O0);
+      O1 = fmaf(f, sm.wo[w][g][lane + 64], O1);
       Ls = fmaf(f, sm.wl[w][g], Ls);
     }
     if (nsplit_b == 1) {
-      fo[i] = O / Ls;
+      store_head(a, O0 / Ls, O1 / Ls, b, kvh * G + g, lane);
     } else {
-      a.part_o[(slot * G + g) * kHeadDim + ch] = O;
-      if (ch == 0) {
+      float* po = a.part_o + (slot * G + g) * kHeadDim;
+      po[lane] = O0;
+      po[lane + 64] = O1;
+      if (lane == 0) {
         a.part_ml[(slot * G + g) * 2 + 0] = M;
         a.part_ml[(slot * G + g) * 2 + 1] = Ls;
       }
     }
   }
-  if (nsplit_b > 1) {
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int prev = atomicAdd(&a.counters[unit], 1);
-      sm.is_last = prev == nsplit_b - 1;
-    }
-    __syncthreads();
-    if (!sm.is_last) return;
-    __threadfence();
-    const int64_t s0 = (int64_t)unit * nsplit;
-    for (int i = tid; i < G * kHeadDim; i += 256) {
-      const int g = i >> 7, ch = i & 127;
-      float M = kNegBig;
-      for (int s = 0; s < nsplit_b; ++s) M = fmaxf(M, a.part_ml[((s0 + s) * G + g) * 2]);
-      float O = 0.f, Ls = 0.f;
-      for (int s = 0; s < nsplit_b; ++s) {
-        const float f = exp2f(a.part_ml[((s0 + s) * G + g) * 2] - M);
-        O = fmaf(f, a.part_o[((s0 + s) * G + g) * kHeadDim + ch], O);
-        Ls = fmaf(f, a.part_ml[((s0 + s) * G + g) * 2 + 1], Ls);
-      }
-      fo[i] = O / Ls;
-    }
-    if (tid == 0) a.counters[unit] = 0;
-  }
-  __syncthreads();
+}
 
-  // ---- 6. rotate back (o = R_b o') and store ----
-  float oscale = 1.0f;
-  if (!a.out_rotated) {
-    fwht_rows(fo, G, a.had_block, tid, 256);
-    oscale = isb;
-  }
-  for (int i = tid; i < G * kHeadDim; i += 256) {
-    const int g = i >> 7, ch = i & 127;
-    store_elem(a.out, ((int64_t)b * a.hq + kvh * G + g) * kHeadDim + ch, a.out_dtype, fo[i] * oscale);
+// Merge the split partials of every (sequence, kv head) that was split, rotate back, store.
+// One workgroup per (sequence, kv head); wave w handles heads w, w+4, ...
+__global__ __launch_bounds__(256) void combine_kernel(DecodeParams a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x;
+  const int kvh = unit % a.hkv, b = unit / a.hkv;
+  const int G = a.group;
+  const int P = a.plan.pages_per_split;
+  const int n_pages = (a.seq_lens[b] + kPage - 1) / kPage;
+  const int nsplit_b = (n_pages + P - 1) / P;
+  if (nsplit_b <= 1) return;
+  const int64_t s0 = (int64_t)unit * a.plan.nsplit;
+  for (int g = wave; g < G; g += 4) {
+    float M = kNegBig;
+    for (int s = 0; s < nsplit_b; ++s) M = fmaxf(M, a.part_ml[((s0 + s) * G + g) * 2]);
+    float O0 = 0.f, O1 = 0.f, Ls = 0.f;
+    for (int s = 0; s < nsplit_b; ++s) {
+      const float f = exp2f(a.part_ml[((s0 + s) * G + g) * 2] - M);
+      const float* po = a.part_o + ((s0 + s) * G + g) * kHeadDim;
+      O0 = fmaf(f, po[lane], O0);
+      O1 = fmaf(f, po[lane + 64], O1);
+      Ls = fmaf(f, a.part_ml[((s0 + s) * G + g) * 2 + 1], Ls);
+    }
+    store_head(a, O0 / Ls, O1 / Ls, b, kvh * G + g, lane);
   }
 }
 
 DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len) {
   DecodePlan plan;
-  plan.waves = kWaves;
   const int max_pg = (max_seq_len + kPage - 1) / kPage;
   const int64_t units = (int64_t)num_seqs * hkv;
-  int target = 1024;
-  if (const char* env = getenv("KVQ_DECODE_TARGET_WGS")) target = atoi(env);
-  int P = 256;
-  if (const char* env = getenv("KVQ_DECODE_PAGES_PER_SPLIT")) {
-    P = atoi(env);
+  // Wide batches (a (sequence, kv head) per CU or more): 8-wave workgroups, one per unit when it
+  // fits (no split, no combine).  Narrow batches of long sequences: 4-wave workgroups over 128-page
+  // splits, so that the CUs fill up.  Measured on the decode workloads of the benchmark.
+  int W, P;
+  if (units >= 256) {
+    W = 8;
+    P = 512;
   } else {
-    while (P > 16 && units * ((max_pg + P / 2 - 1) / (P / 2)) <= target) P /= 2;
+    W = 4;
+    P = 128;
+    while (P > 16 && units * ((max_pg + P - 1) / P) < 512) P /= 2;
   }
-  if (P < 4) P = 4;
+  int D = 3;
+  // tuning overrides, read once per process
+  static const int env_w = getenv("KVQ_DECODE_WAVES") ? atoi(getenv("KVQ_DECODE_WAVES")) : 0;
+  static const int env_p = getenv("KVQ_DECODE_PAGES_PER_SPLIT") ? atoi(getenv("KVQ_DECODE_PAGES_PER_SPLIT")) : 0;
+  static const int env_d = getenv("KVQ_DECODE_DEPTH") ? atoi(getenv("KVQ_DECODE_DEPTH")) : 0;
+  if (env_w) W = env_w;
+  if (env_p) P = env_p;
+  if (env_d) D = env_d;
+  if (W != 4 && W != 8 && W != 16) W = 8;
+  if (D != 2 && D != 3 && D != 4) D = 3;
+  if (W == 16) D = 2;  // register budget of 1024-thread workgroups
+  if (P > 64 * W) P = 64 * W;
+  if (P < 1) P = 1;
+  plan.waves = W;
+  plan.depth = D;
   plan.pages_per_split = P;
   plan.nsplit = max_pg > 0 ? (max_pg + P - 1) / P : 1;
   return plan;
@@ -355,12 +448,20 @@ void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, in
 }
 
 hipError_t launch_decode(const DecodeParams& p, int fmt, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.num_seqs * p.hkv * p.plan.nsplit;
-  if (fmt == 0) {
-    hipLaunchKernelGGL(decode_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, p);
-  } else {
-    return hipErrorInvalidValue;  // MXFP4 decode is provided by its own kernel file
-  }
+  if (fmt != 0) return hipErrorInvalidValue;  // MXFP4 decode is provided by its own kernel file
+  const int64_t units = (int64_t)p.num_seqs * p.hkv;
+  const dim3 grid((unsigned)(units * p.plan.nsplit));
+#define KVQ_DECODE_CASE(WV, DV)                                                                  \
+  if (p.plan.waves == WV && p.plan.depth == DV) {                                              \
+    hipLaunchKernelGGL((decode_kernel<0, WV, DV>), grid, dim3(WV * 64), 0, stream, p);          \
+  } else
+  KVQ_DECODE_CASE(4, 2) KVQ_DECODE_CASE(4, 3) KVQ_DECODE_CASE(4, 4)
+  KVQ_DECODE_CASE(8, 2) KVQ_DECODE_CASE(8, 3) KVQ_DECODE_CASE(8, 4)
+  KVQ_DECODE_CASE(16, 2) { return hipErrorInvalidValue; }
+#undef KVQ_DECODE_CASE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.plan.nsplit <= 1) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)units), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -78,8 +78,18 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
 
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                   int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+  // each thread moves 4 x 16 bytes per step, all four loads issued before the stores
+  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t i = t;
+  for (; i + 3 * nthreads < n16; i += 4 * nthreads) {
+    const u32x4 a0 = src[i], a1 = src[i + nthreads], a2 = src[i + 2 * nthreads], a3 = src[i + 3 * nthreads];
+    dst[i] = a0;
+    dst[i + nthreads] = a1;
+    dst[i + 2 * nthreads] = a2;
+    dst[i + 3 * nthreads] = a3;
+  }
+  for (; i < n16; i += nthreads) dst[i] = src[i];
 }
 
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
@@ -90,7 +100,7 @@ hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
   const int64_t n16 = (int64_t)(bytes / 16);
   int64_t blocks = (n16 + 255) / 256;
-  if (blocks > 256 * 32) blocks = 256 * 32;
+  if (blocks > 256 * 16) blocks = 256 * 16;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)src, (u32x4*)dst, n16);
   return hipGetLastError();

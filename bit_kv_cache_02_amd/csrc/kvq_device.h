@@ -27,9 +27,11 @@ enum : int { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2, DT_E4M3 = 3 };
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // ---- DPP row (16-lane) reductions; every lane of the row ends with the same bits ----
+// All patterns used below read lanes inside the same row, so bound_ctrl never applies; setting it
+// lets the compiler fuse the move into the consuming VALU op (v_max_f32_dpp ...).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
@@ -115,5 +117,11 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 }
 
 __device__ __forceinline__ int popc(uint32_t x) { return __builtin_popcount(x); }
+
+// Raw buffer resource over `bytes` bytes at `p` (gfx9 dword3 0x00020000); loads past the end
+// return zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
 
 }  // namespace kvq

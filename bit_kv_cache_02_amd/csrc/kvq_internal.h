@@ -23,6 +23,7 @@ struct DecodePlan {
   int32_t pages_per_split;  // pages one workgroup handles
   int32_t nsplit;           // workgroups per (sequence, kv head)
   int32_t waves;            // waves per workgroup
+  int32_t depth;            // pages in flight per wave (register prefetch pipeline)
 };
 
 struct DecodeParams {
