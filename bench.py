@@ -215,7 +215,9 @@ def cpu_baseline(w, budget_s=12.0, n_seqs=4):
 
 
 def traffic_entry(algo_bytes):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if still current."""
+    """HBM bytes per decode launch from committed rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE,
+    each scaled by what the counter reads for the bench's 1 GiB copy), if the decode kernel source
+    has not changed since."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
         src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
@@ -235,7 +237,11 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--profile-run", action="store_true",
+                    help="short run for rocprofv3: few steps, no prefill and no CPU leg")
     args = ap.parse_args()
+    if args.profile_run:
+        args.steps, args.warmup, args.no_prefill, args.no_cpu = 20, 5, True, True
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -289,7 +295,7 @@ def main():
         "decode_workspace_bytes": decode_workspace_bytes(caches[0], w.num_q_heads, w.batch, int(lens.max())),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_kernel<0> (kvq_decode_attn, INT4)",
+            "kernel": "kvq::decode_kernel (kvq_decode_attn, INT4)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

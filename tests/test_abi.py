@@ -121,17 +121,18 @@ def test_decode_rejects_bad_args(kw, status):
 
 
 def test_decode_workspace_sizing_and_check():
+    # a few long sequences are split over several workgroups and need a workspace
     d = _desc(num_kv_heads=8)
     lib = kvq.lib()
-    need = lib.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 32, 4096)
+    need = lib.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 2, 32768)
     assert need > 0 and need % 4 == 0
-    assert lib.kvq_decode_workspace_bytes(ctypes.byref(d), 3, 32, 4096) == ctypes.c_size_t(-1).value
+    assert lib.kvq_decode_workspace_bytes(ctypes.byref(d), 3, 2, 32768) == ctypes.c_size_t(-1).value
     # one short page: no split, no workspace
     assert lib.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 1, 16) == 0
     big = _desc(num_kv_heads=8, num_pages=1 << 20)
-    assert _decode(big, hq=32, B=32, msl=4096, mp=256, ws=None) == kvq.KVQ_ERR_WORKSPACE
-    assert _decode(big, hq=32, B=32, msl=4096, mp=256, wsb=need - 1) == kvq.KVQ_ERR_WORKSPACE
-    assert _decode(big, hq=32, B=32, msl=4096, mp=256, ws=ctypes.c_void_p(4096 + 16), wsb=need) \
+    assert _decode(big, hq=32, B=2, msl=32768, mp=2048, ws=None) == kvq.KVQ_ERR_WORKSPACE
+    assert _decode(big, hq=32, B=2, msl=32768, mp=2048, wsb=need - 1) == kvq.KVQ_ERR_WORKSPACE
+    assert _decode(big, hq=32, B=2, msl=32768, mp=2048, ws=ctypes.c_void_p(4096 + 16), wsb=need) \
         == kvq.KVQ_ERR_WORKSPACE
 
 
