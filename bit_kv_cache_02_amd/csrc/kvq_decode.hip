@@ -35,8 +35,10 @@ constexpr float kNegBig = -1.0e30f;
 
 template <int W>
 struct DecodeSmem {
-  // q' limbs in the byte order of the q.K A tile: [limb][g][a2][jg][16 bytes]
+  // INT4: q' limbs in the byte order of the q.K A tile: [limb][g][a2][jg][16 bytes]
   uint8_t qlimb[2][kMaxG][2][4][16];
+  // MXFP4: q' as fp16 high/low parts in the A-tile order of the f16 q.K MFMA: [part][g][kk][jg][8]
+  _Float16 qh[2][kMaxG][4][4][8];
   float qdelta[kMaxG];
   float qsum[kMaxG];
   _Float16 ptile[W][2 * kMaxG][kPage];  // p~ split into fp16 high/low parts, A-tile rows 2g+limb
@@ -66,24 +68,50 @@ __device__ __forceinline__ void fwht_wave(float& x0, float& x1, int hb, int lane
   }
 }
 
+template <int FMT>
 struct PageData {
   u32x4 k;      // K row bytes 16*jg..16*jg+15 of token n
   u32x4 v;      // V words: row bytes 4n..4n+3 of tokens 4jg..4jg+3
   uint32_t kp;  // K params of token n
-  uint32_t vp;  // V params of token n
+  uint32_t vp;  // INT4: V params of token n
+};
+template <>
+struct PageData<1> {
+  u32x4 k;
+  u32x4 v;
+  uint32_t kp;  // UE8M0 bytes of token n (K)
+  u32x4 vp4;    // UE8M0 bytes of tokens 4jg..4jg+3 (V)
 };
 
 // `base` is wave-uniform: the buffer descriptor lives in scalar registers and the per-lane offsets
 // are loop invariant, so a page costs no vector address arithmetic.
-__device__ __forceinline__ PageData load_page(const uint8_t* base, int koff, int voff, int poff) {
+template <int FMT>
+__device__ __forceinline__ PageData<FMT> load_page(const uint8_t* base, int koff, int voff, int poff, int qoff) {
   const __amdgpu_buffer_rsrc_t r = make_rsrc(base, kPageHeadBytes);
-  PageData d;
+  PageData<FMT> d;
   // cache policy 2 = nontemporal: the pages are streamed once per step
   d.k = __builtin_amdgcn_raw_buffer_load_b128(r, koff, 0, 2);
   d.v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2);
   d.kp = __builtin_amdgcn_raw_buffer_load_b32(r, poff, kKParamsOff, 2);
-  d.vp = __builtin_amdgcn_raw_buffer_load_b32(r, poff, kVParamsOff, 2);
+  if constexpr (FMT == 0) d.vp = __builtin_amdgcn_raw_buffer_load_b32(r, poff, kVParamsOff, 2);
+  else d.vp4 = __builtin_amdgcn_raw_buffer_load_b128(r, qoff, kVParamsOff, 2);
   return d;
+}
+
+// 2^(E-127) for the UE8M0 byte E at bit `shift` of w (E = 0 gives 0: an all-zero or sub-2^-125 group)
+__device__ __forceinline__ float ue8m0_scale(uint32_t w, int shift) {
+  return __uint_as_float(((w >> shift) & 0xFFu) << 23);
+}
+
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+// Two e2m1 codes of byte `sel` of w -> two fp16 values times `scale` (low nibble first).
+__device__ __forceinline__ f16x2 cvt_fp4(uint32_t w, float scale, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3);
+  }
 }
 
 // Per-wave streaming state.
@@ -92,7 +120,7 @@ struct WaveState {
   f32x4 acc[8];
 };
 
-__device__ __forceinline__ void process_page(const PageData& pg, int valid, WaveState& s, const i32x4 (&qa)[2],
+__device__ __forceinline__ void process_page(const PageData<0>& pg, int valid, WaveState& s, const i32x4 (&qa)[2],
                                              float alpha0, float beta0, float alpha1, float beta1,
                                              bool has0, bool has1, int n, int jg, bool a_row_used,
                                              _Float16 (*ptile)[kPage]) {
@@ -173,6 +201,88 @@ __device__ __forceinline__ void process_page(const PageData& pg, int valid, Wave
   }
 }
 
+// MXFP4 page: K and V are dequantized to fp16 tiles with their UE8M0 group scales by the gfx950
+// fp4 conversion (two codes of one byte -> two fp16), then both contractions run on f16 MFMA.
+//   q.K: v_mfma_f32_16x16x32_f16, A = q' as fp16 high/low parts (rows 2g, 2g+1), B = K tile;
+//        dword kk of the lane's K chunk feeds MFMA kk: byte q -> channels (4jg+kk)+32q (+16),
+//        all in channel group q (one scale).
+//   p.V: v_mfma_f32_16x16x16_f16, A = p split high/low, B = V tile: byte r of V word q is token
+//        4jg+r, channels n+32q and n+32q+16 (group q), repacked so one register holds two tokens.
+__device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid, WaveState& s,
+                                                const f16x8 (&qh)[4], float c2, bool has0, bool has1,
+                                                int n, int jg, bool a_row_used, _Float16 (*ptile)[kPage]) {
+  const bool tv = n < valid;
+  f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const uint32_t w = pg.k[kk];
+    f16x8 kb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f16x2 h2 = cvt_fp4(w, ue8m0_scale(pg.kp, 8 * q), q);
+      kb[2 * q] = h2[0];
+      kb[2 * q + 1] = h2[1];
+    }
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[kk], kb, sc, 0, 0, 0);
+  }
+  float x0 = (sc[0] + sc[1]) * c2, x1 = (sc[2] + sc[3]) * c2;
+  x0 = tv ? x0 : -INFINITY;
+  x1 = tv ? x1 : -INFINITY;
+
+  const float pm0 = row_max16(x0), pm1 = row_max16(x1);
+  // p <= 2^8 stays far inside fp16 (no value scale is folded into p here)
+  if (__any(pm0 > s.m0 + 8.0f || pm1 > s.m1 + 8.0f)) {
+    const float mn0 = fmaxf(s.m0, pm0), mn1 = fmaxf(s.m1, pm1);
+    const float f0 = __builtin_amdgcn_exp2f(s.m0 - mn0), f1 = __builtin_amdgcn_exp2f(s.m1 - mn1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s.acc[i][0] *= f0;
+      s.acc[i][1] *= f0;
+      s.acc[i][2] *= f1;
+      s.acc[i][3] *= f1;
+    }
+    s.l0 *= f0;
+    s.l1 *= f1;
+    s.m0 = mn0;
+    s.m1 = mn1;
+  }
+  const float p0 = __builtin_amdgcn_exp2f(x0 - s.m0), p1 = __builtin_amdgcn_exp2f(x1 - s.m1);
+  s.l0 += p0;
+  s.l1 += p1;
+
+  // p as fp16 high + low parts at A-tile rows 2g+limb, natural token order
+  const float pt0 = tv ? p0 : 0.0f, pt1 = tv ? p1 : 0.0f;
+  const _Float16 h0 = (_Float16)pt0, h1 = (_Float16)pt1;
+  const _Float16 r0 = (_Float16)(pt0 - (float)h0), r1 = (_Float16)(pt1 - (float)h1);
+  if (has0) {
+    ptile[4 * jg + 0][n] = h0;
+    ptile[4 * jg + 1][n] = r0;
+  }
+  if (has1) {
+    ptile[4 * jg + 2][n] = h1;
+    ptile[4 * jg + 3][n] = r1;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const f16x4 pa = a_row_used ? *(const f16x4*)&ptile[n][4 * jg] : f16x4{0, 0, 0, 0};
+  __builtin_amdgcn_wave_barrier();
+
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t Y = pg.v[q];
+    f16x4 blo, bhi;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f16x2 h2 = cvt_fp4(Y, ue8m0_scale(pg.vp4[r], 8 * q), r);
+      blo[r] = h2[0];
+      bhi[r] = h2[1];
+    }
+    s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, blo, s.acc[2 * q], 0, 0, 0);
+    s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bhi, s.acc[2 * q + 1], 0, 0, 0);
+  }
+}
+
 // Rotate one head's normalised o' (element lane in o0, lane + 64 in o1) back and store it.
 __device__ __forceinline__ void store_head(const DecodeParams& a, float o0, float o1, int b, int h, int lane) {
   float scale = 1.0f;
@@ -243,12 +353,12 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
     return (const uint8_t*)(((uint64_t)hi << 32) | lo);
   };
-  const int koff = 64 * n + 16 * jg, voff = kVCodesOff + 16 * lane, poff = 4 * n;
+  const int koff = 64 * n + 16 * jg, voff = kVCodesOff + 16 * lane, poff = 4 * n, qoff = 16 * jg;
   constexpr int NB = D + 1;  // register buffers: D pages in flight plus the one being processed
-  PageData st[NB];
+  PageData<FMT> st[NB];
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (d < npw) st[d] = load_page(page_base(d), koff, voff, poff);
+    if (d < npw) st[d] = load_page<FMT>(page_base(d), koff, voff, poff, qoff);
 
   // ---- 2. q' = R_b (q_scale q) in registers, then 16-bit fixed point q' ~= delta_g * Q with
   //         |Q| <= 32000, stored as two int8 limbs (Q = 256*hi + lo) in the A-tile byte order ----
@@ -260,6 +370,19 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       fwht_wave(v0, v1, a.had_block, lane);
       v0 *= isb;
       v1 *= isb;
+      if constexpr (FMT == 1) {
+        // fp16 high/low parts; channel (4jg + kk) + 32q + 16e sits at element 2q + e = ch >> 4
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int ch = lane + 64 * e;
+          const float v = e ? v1 : v0;
+          const _Float16 hi = (_Float16)v;
+          const _Float16 lo = (_Float16)(v - (float)hi);
+          sm.qh[0][g][ch & 3][(ch >> 2) & 3][ch >> 4] = hi;
+          sm.qh[1][g][ch & 3][(ch >> 2) & 3][ch >> 4] = lo;
+        }
+        continue;
+      }
       const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
       const float delta = amax > 0.0f ? amax / 32000.0f : 1.0f;
       const int q0 = (int)rintf(v0 / delta), q1 = (int)rintf(v1 / delta);
@@ -285,14 +408,24 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   const int ga = n >> 1;   // A-tile row 2g+limb -> head of this lane's A row
   const int limb = n & 1;  // 0: high limb / high fp16 part, 1: low
   const bool a_row_used = ga < G;
-  i32x4 qa[2];
-#pragma unroll
-  for (int a2 = 0; a2 < 2; ++a2)
-    qa[a2] = a_row_used ? *(const i32x4*)&sm.qlimb[limb][ga][a2][jg][0] : i32x4{0, 0, 0, 0};
   const bool has0 = 2 * jg < G, has1 = 2 * jg + 1 < G;
   const float c2 = a.sm_scale_log2;
-  const float alpha0 = has0 ? sm.qdelta[2 * jg] * c2 : 0.0f, beta0 = has0 ? sm.qsum[2 * jg] * c2 : 0.0f;
-  const float alpha1 = has1 ? sm.qdelta[2 * jg + 1] * c2 : 0.0f, beta1 = has1 ? sm.qsum[2 * jg + 1] * c2 : 0.0f;
+  i32x4 qa[2];
+  f16x8 qh[4];
+  float alpha0 = 0.f, beta0 = 0.f, alpha1 = 0.f, beta1 = 0.f;
+  if constexpr (FMT == 0) {
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2)
+      qa[a2] = a_row_used ? *(const i32x4*)&sm.qlimb[limb][ga][a2][jg][0] : i32x4{0, 0, 0, 0};
+    alpha0 = has0 ? sm.qdelta[2 * jg] * c2 : 0.0f;
+    beta0 = has0 ? sm.qsum[2 * jg] * c2 : 0.0f;
+    alpha1 = has1 ? sm.qdelta[2 * jg + 1] * c2 : 0.0f;
+    beta1 = has1 ? sm.qsum[2 * jg + 1] * c2 : 0.0f;
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qh[kk] = a_row_used ? *(const f16x8*)&sm.qh[limb][ga][kk][jg][0] : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
 
   // ---- 3. stream this wave's pages ----
   WaveState s;
@@ -307,9 +440,13 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       const int i = i0 + d;
       if (i < npw) {
         // page i sits in buffer d; page i + D goes to the buffer freed by page i - 1
-        if (i + D < npw) st[(d + D) % NB] = load_page(page_base(i + D), koff, voff, poff);
-        process_page(st[d], valid0 - i * W * kPage, s, qa, alpha0, beta0, alpha1, beta1, has0, has1, n, jg,
-                     a_row_used, sm.ptile[wave]);
+        if (i + D < npw) st[(d + D) % NB] = load_page<FMT>(page_base(i + D), koff, voff, poff, qoff);
+        if constexpr (FMT == 0)
+          process_page(st[d], valid0 - i * W * kPage, s, qa, alpha0, beta0, alpha1, beta1, has0, has1, n, jg,
+                       a_row_used, sm.ptile[wave]);
+        else
+          process_page_mx(st[d], valid0 - i * W * kPage, s, qh, c2, has0, has1, n, jg, a_row_used,
+                          sm.ptile[wave]);
       }
     }
   }
@@ -323,7 +460,8 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
     for (int e = 0; e < 2; ++e) {
       const int ch = n + 32 * q + 16 * e;
       const f32x4 v = s.acc[2 * q + e];
-      const float sc = e ? 1048576.0f : 16777216.0f;  // 2^24, or 2^24/16 for the high nibbles
+      // INT4: undo the subnormal encoding (2^24, or 2^24/16 for the high nibbles); MXFP4: none
+      const float sc = FMT == 1 ? 1.0f : (e ? 1048576.0f : 16777216.0f);
       if (has0) sm.wo[wave][2 * jg][ch] = sc * (v[0] + v[1]) + pz0;
       if (has1) sm.wo[wave][2 * jg + 1][ch] = sc * (v[2] + v[3]) + pz1;
     }
@@ -448,16 +586,18 @@ void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, in
 }
 
 hipError_t launch_decode(const DecodeParams& p, int fmt, hipStream_t stream) {
-  if (fmt != 0) return hipErrorInvalidValue;  // MXFP4 decode is provided by its own kernel file
   const int64_t units = (int64_t)p.num_seqs * p.hkv;
   const dim3 grid((unsigned)(units * p.plan.nsplit));
-#define KVQ_DECODE_CASE(WV, DV)                                                                  \
-  if (p.plan.waves == WV && p.plan.depth == DV) {                                              \
-    hipLaunchKernelGGL((decode_kernel<0, WV, DV>), grid, dim3(WV * 64), 0, stream, p);          \
+#define KVQ_DECODE_CASE(F, WV, DV)                                                               \
+  if (fmt == F && p.plan.waves == WV && p.plan.depth == DV) {                                  \
+    hipLaunchKernelGGL((decode_kernel<F, WV, DV>), grid, dim3(WV * 64), 0, stream, p);          \
   } else
-  KVQ_DECODE_CASE(4, 2) KVQ_DECODE_CASE(4, 3) KVQ_DECODE_CASE(4, 4)
-  KVQ_DECODE_CASE(8, 2) KVQ_DECODE_CASE(8, 3) KVQ_DECODE_CASE(8, 4)
-  KVQ_DECODE_CASE(16, 2) { return hipErrorInvalidValue; }
+  KVQ_DECODE_CASE(0, 4, 2) KVQ_DECODE_CASE(0, 4, 3) KVQ_DECODE_CASE(0, 4, 4)
+  KVQ_DECODE_CASE(0, 8, 2) KVQ_DECODE_CASE(0, 8, 3) KVQ_DECODE_CASE(0, 8, 4)
+  KVQ_DECODE_CASE(0, 16, 2)
+  KVQ_DECODE_CASE(1, 4, 2) KVQ_DECODE_CASE(1, 4, 3) KVQ_DECODE_CASE(1, 4, 4)
+  KVQ_DECODE_CASE(1, 8, 2) KVQ_DECODE_CASE(1, 8, 3) KVQ_DECODE_CASE(1, 8, 4)
+  KVQ_DECODE_CASE(1, 16, 2) { return hipErrorInvalidValue; }
 #undef KVQ_DECODE_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.plan.nsplit <= 1) return e;

@@ -138,7 +138,6 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, floa
     return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d exceeds max_pages*16 = %lld", max_seq_len, (long long)max_pages * KVQ_PAGE_SIZE);
   if (flags & ~KVQ_OUT_ROTATED) return fail(KVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (!std::isfinite(q_scale) || !std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARG, "q_scale and sm_scale must be finite");
-  if (cache->format != KVQ_FMT_INT4_TOKEN) return fail(KVQ_ERR_UNSUPPORTED, "MXFP4 decode is not built yet");
   if (num_seqs == 0) return KVQ_OK;
   const int hkv = cache->num_kv_heads;
   const int group = num_q_heads / hkv;

@@ -163,3 +163,35 @@ def test_append_deterministic():
                    torch.tensor(start, dtype=torch.int32).cuda(), torch.from_numpy(table).cuda(), 33)
         outs.append(cache.pool.cpu())
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("hb", [1, 128])
+def test_append_mxfp4_ragged(dtype, hb):
+    # e2m1 codes with UE8M0 group-32 scales after the full 128-wide rotation (or none)
+    rng = np.random.default_rng(200 + hb)
+    lens_new = [1, 16, 37, 5, 64, 3, 20]
+    start = [0, 5, 13, 30, 16, 2, 47]
+    hkv = 2
+    table, total = ragged_table(rng, lens_new, start)
+    k, v = rand_kv(rng, sum(lens_new), hkv, dtype)
+    run_append(f"mxfp4/{dtype}/b{hb}", k, v, lens_new, start, table, total, hkv, hb,
+               oracle.FMT_MXFP4, dtype)
+
+
+def test_append_mxfp4_exact_grid():
+    # values +-e2m1 * 2^k with each group's amax in {4, 6} * 2^k: every code and exponent exact
+    rng = np.random.default_rng(201)
+    t, hkv = 40, 1
+    grid = oracle.E2M1_GRID
+    k_exp = rng.integers(-6, 6, (t, hkv, 4))
+    idx = rng.integers(0, 8, (t, hkv, 4, 32))
+    idx[..., 0] = rng.choice([6, 7], (t, hkv, 4))
+    idx = np.minimum(idx, np.where(idx[..., :1] == 6, 6, 7))
+    sign = rng.integers(0, 2, idx.shape)
+    sign[idx == 0] = 0
+    x = (np.where(sign, -1.0, 1.0) * grid[idx] * 2.0 ** k_exp[..., None]).reshape(t, hkv, 128)
+    table = np.array([[0, 1, 2]], np.int32)
+    _, _, flips = run_append("mxfp4-grid", x, x[::-1].copy(), [t], [0], table, 3, hkv, 1,
+                             oracle.FMT_MXFP4, "bf16")
+    assert flips == 0

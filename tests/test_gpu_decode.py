@@ -188,3 +188,35 @@ def test_dequant_pages(hb):
     for got, ref in ((ku, kur), (vu, vur)):
         got = got.cpu().numpy().astype(np.float64)
         assert np.abs(got - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("group,q_dtype", [(8, "e4m3"), (8, "bf16"), (4, "bf16"), (1, "f16")])
+def test_decode_mxfp4(group, q_dtype):
+    rng = np.random.default_rng(60 + group)
+    lens = [1, 17, 300, 1000]
+    hkv = 2
+    pool, table = oracle_cache(rng, lens, hkv, 128, fmt=oracle.FMT_MXFP4)
+    run_decode(f"mxfp4/G{group}/{q_dtype}", pool, table, lens, hkv * group, 128,
+               fmt=oracle.FMT_MXFP4, q_dtype=q_dtype, seed=group)
+
+
+def test_decode_mxfp4_long_splits_and_no_rotation():
+    rng = np.random.default_rng(61)
+    lens = [5000, 700]
+    pool, table = oracle_cache(rng, lens, 1, 128, fmt=oracle.FMT_MXFP4)
+    run_decode("mxfp4/long", pool, table, lens, 8, 128, fmt=oracle.FMT_MXFP4, q_dtype="e4m3")
+    pool1, table1 = oracle_cache(rng, [200], 1, 1, fmt=oracle.FMT_MXFP4)
+    run_decode("mxfp4/b1", pool1, table1, [200], 8, 1, fmt=oracle.FMT_MXFP4)
+
+
+def test_dequant_pages_mxfp4():
+    rng = np.random.default_rng(62)
+    pool, table = oracle_cache(rng, [40, 70], 2, 128, fmt=oracle.FMT_MXFP4)
+    print("[dequant] mxfp4", flush=True)
+    cache = kvq.Cache(pool.shape[0], 2, 128, "mxfp4", pool=torch.from_numpy(pool).cuda())
+    ids = np.array([table[0, 0], table[1, 4], table[1, 1]], np.int32)
+    k, v = kvq.dequant_pages(cache, torch.from_numpy(ids).cuda())
+    kr, vr = oracle.dequant_pages(pool, ids, 128, oracle.FMT_MXFP4)
+    # e2m1 * 2^(E-127) is exact in fp32
+    assert np.array_equal(k.cpu().numpy(), kr.astype(np.float32))
+    assert np.array_equal(v.cpu().numpy(), vr.astype(np.float32))
