@@ -165,8 +165,9 @@ __device__ __forceinline__ void process_page(const PageData<0>& pg, int valid, W
   const float p0 = __builtin_amdgcn_exp2f(x0 - s.m0), p1 = __builtin_amdgcn_exp2f(x1 - s.m1);
   s.l0 += p0;
   s.l1 += p1;
-  s.pz0 = tv ? fmaf(p0, zv, s.pz0) : s.pz0;
-  s.pz1 = tv ? fmaf(p1, zv, s.pz1) : s.pz1;
+  const float zc = fmaf(8.0f, sv, zv);  // zero point of the centred codes (exact: fp16 inputs)
+  s.pz0 = tv ? fmaf(p0, zc, s.pz0) : s.pz0;
+  s.pz1 = tv ? fmaf(p1, zc, s.pz1) : s.pz1;
 
   // p~ = p * sv as fp16 high + low parts, stored at A-tile rows 2g+limb in the k order of the
   // V words (tokens 0, 2, 1, 3 of each quad: bits 0 and 1 of the token swapped)
@@ -189,13 +190,21 @@ __device__ __forceinline__ void process_page(const PageData<0>& pg, int valid, W
   __builtin_amdgcn_wave_barrier();
 
   // V codes as fp16 subnormals: word q of the lane holds row byte 4n+q of 4 tokens.  Low nibbles
-  // (channel n+32q) enter as c*2^-24, high nibbles (channel n+32q+16) are masked in place and
-  // enter as 16c*2^-24; their accumulators carry that factor 16 until the end.
+  // (channel n+32q) are masked to c*2^-24, high nibbles (channel n+32q+16) are masked in place to
+  // 16c*2^-24 (their accumulators carry that factor 16 until the end).  One exact packed fp16
+  // subtraction centres the codes, c -> c - 8: all products p~*c would otherwise share one sign,
+  // and the MFMA accumulation error would not average out (the centre 8*sv moves into the zero
+  // point, zv + 8*sv).
+  typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+  const h2 c8lo = __builtin_bit_cast(h2, 0x00080008u), c8hi = __builtin_bit_cast(h2, 0x00800080u);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t Y = pg.v[q], Y8 = Y >> 8;
-    const f16x4 blo = __builtin_bit_cast(f16x4, u32x2{Y & M16, Y8 & M16});          // tokens 0,2 | 1,3
-    const f16x4 bhi = __builtin_bit_cast(f16x4, u32x2{Y & (M16 << 4), Y8 & (M16 << 4)});
+    const h2 l0 = __builtin_bit_cast(h2, Y & M16) - c8lo, l1 = __builtin_bit_cast(h2, Y8 & M16) - c8lo;
+    const h2 u0 = __builtin_bit_cast(h2, Y & (M16 << 4)) - c8hi;
+    const h2 u1 = __builtin_bit_cast(h2, Y8 & (M16 << 4)) - c8hi;
+    const f16x4 blo = f16x4{l0[0], l0[1], l1[0], l1[1]};  // tokens 0,2 | 1,3
+    const f16x4 bhi = f16x4{u0[0], u0[1], u1[0], u1[1]};
     s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, blo, s.acc[2 * q], 0, 0, 0);
     s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bhi, s.acc[2 * q + 1], 0, 0, 0);
   }
