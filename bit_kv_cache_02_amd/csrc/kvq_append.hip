@@ -3,13 +3,18 @@
 // writes straight into paged KV-cache layouts; UltraQuant article, section on how the method
 // works: Walsh-Hadamard rotation before FP4 quantization with UE8M0 group scales).
 //
-// One wave owns one (sequence, page, kv head, K|V) page-head: the up-to-16 new tokens of that
-// page.  The rotation y*sqrt(b) = X * H_b is a dense +-1 matrix product: it runs on the matrix
-// cores as v_mfma_f32_16x16x32_{bf16,f16} (16 tokens x 128 channels times 128 x 128 signs).  The
-// inputs are exact bf16/fp16 values and the signs are exact, so every product is exact and only
-// the fp32 accumulation rounds.  The MFMA output leaves lane l with tokens 4*(l/16)+r (r = 0..3)
-// and channels 16*nb + l%16 (nb = 0..7); the page layout is chosen so that this is exactly what
-// a lane stores: a 4-byte K row word per token, and a 16-byte V word for a quad of tokens.
+// One wave owns one (sequence, kv head, K|V) and walks kAppendPagesPerWave consecutive pages of
+// it, loading the next page's tokens while it quantizes the current one.  Per page the rotation
+// y*sqrt(b) = H_b^T X^T is a dense +-1 matrix product on the matrix cores
+// (v_mfma_f32_16x16x32_{bf16,f16}: 128 x 128 signs times 128 channels x 16 tokens).  The inputs
+// are exact bf16/fp16 values and the signs are exact, so every product is exact and only the
+// fp32 accumulation rounds.  With the signs as the A operand the output tile nb leaves lane l
+// with channels 16*nb + 4*(l/16) + r (r = 0..3) of token slot l%16: each lane holds 32 channels
+// of one token, so the token-wise min/max is a 32-value in-lane reduction plus two cross-lane
+// steps, and the per-token scale arithmetic runs once per lane.  The same lane holds exactly
+// K row words 4*(l/16) .. 4*(l/16)+3 of its token (word a carries channels a + 16i in nibble i),
+// which it stores as one 16-byte write; V rows are exchanged inside lane quads (DPP) so that
+// each lane writes one 16-byte piece of the token-interleaved V block.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -41,50 +46,60 @@ __device__ __forceinline__ uint32_t e2m1_code(float r) {
   return idx | (r < 0.0f ? 8u : 0u);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
+// 4x4 word transpose across the lanes of a quad: afterwards lane m holds in w[r] what lane r held
+// in w[m].  Two exchange stages (partner m^1, then m^2), each swapping the off-diagonal halves.
+__device__ __forceinline__ void quad_transpose(uint32_t (&w)[4], int m) {
+  const bool b0 = m & 1, b1 = m & 2;
+#pragma unroll
+  for (int r = 0; r < 4; r += 2) {
+    const uint32_t recv = dpp_u<kQuadSwap1>(b0 ? w[r] : w[r + 1]);
+    if (b0) w[r] = recv;
+    else w[r + 1] = recv;
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const uint32_t recv = dpp_u<kQuadSwap2>(b1 ? w[r] : w[r + 2]);
+    if (b1) w[r] = recv;
+    else w[r + 2] = recv;
+  }
+}
+
 }  // namespace
 
 template <bool BF16, int HB, int FMT>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int hk = blockIdx.z * 4 + wave;  // (K|V, kv head) combination
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(thread_id() >> 6);
+  const int hk = block_id_z() * 4 + wave;  // (K|V, kv head) combination
   if (hk >= 2 * a.hkv) return;
   const int is_v = hk >= a.hkv;
   const int h = is_v ? hk - a.hkv : hk;
-  const int b = blockIdx.y;
-  const int j = blockIdx.x;
+  const int b = block_id_y();
 
   const int t0 = a.cu_new[b];
   const int n_new = min(a.cu_new[b + 1] - t0, a.max_new);
   if (n_new <= 0) return;
   const int s0 = a.start_pos[b];
-  const int page_idx = s0 / kPage + j;
-  const int pos0 = page_idx * kPage;
-  if (pos0 >= s0 + n_new) return;
-  const int slot_lo = max(s0 - pos0, 0);
-  const int slot_hi = min(s0 + n_new - pos0, kPage);
-  const int page_id = a.block_table[(int64_t)b * a.max_pages + page_idx];
+  const int end_pos = s0 + n_new;
+  const int pg_begin = s0 / kPage + block_id_x() * kAppendPagesPerWave;
+  const int pg_end = min(pg_begin + kAppendPagesPerWave, (end_pos - 1) / kPage + 1);
+  if (pg_begin >= pg_end) return;
 
-  const int n = lane & 15;   // MFMA column / row of the tile this lane feeds
-  const int kg = lane >> 4;  // lane group
+  // page ids of this wave's pages, one per lane (read back with readlane): one load up front
+  // instead of a dependent load per page
+  const int npg = pg_end - pg_begin;
+  const int page_ids = lane < npg ? a.block_table[(int64_t)b * a.max_pages + pg_begin + lane] : 0;
 
-  // ---- load 16 tokens x 128 channels as the MFMA A operand (zeros for slots not appended) ----
-  const uint8_t* src = is_v ? a.v : a.k;
-  const int slot_a = n;  // A row = token slot
-  const bool valid_a = slot_a >= slot_lo && slot_a < slot_hi;
-  u32x4 xa[4];
-  {
-    const int64_t tok = (int64_t)t0 + pos0 + slot_a - s0;
-    const uint8_t* row = src + (tok * a.hkv + h) * (int64_t)(kHeadDim * 2) + kg * 16;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if (valid_a) xa[kb] = *(const u32x4*)(row + kb * 64);
-      else xa[kb] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
+  const int n = lane & 15;  // token slot of this lane (B column, output column)
+  const int g = lane >> 4;  // lane group: input channels 8g.. of each 32-block, output rows 4g..
 
-  // ---- B tiles: signs of H (or the identity for HB = 1) for this lane's (k, n) entries ----
-  // Entry (k, n) of tile (kb, nb) is H[32kb + k][16nb + n]; the sign factors into a base pattern
+  // ---- A tiles: signs of H (or the identity for HB = 1) for this lane's (row n, k) entries ----
+  // Entry (n, k) of tile (kb, nb) is H[32kb + k][16nb + n]; the sign factors into a base pattern
   // that depends on nb&1 and a global sign that depends on (kb, nb).
   uint32_t tp[2][4], tm[2][4];
 #pragma unroll
@@ -94,7 +109,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
       uint32_t word_p = 0, word_m = 0;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int k = 8 * kg + 2 * w + half;
+        const int k = 8 * g + 2 * w + half;
         uint16_t vp, vm;
         if (HB == 1) {
           vp = (k == 16 * p + n) ? Sign<BF16>::kPlus : 0;
@@ -112,138 +127,184 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
     }
   }
 
-  f32x4 acc[8];
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* src = is_v ? a.v : a.k;
+  const int row_stride = a.hkv * (kHeadDim * 2);  // bytes from one token's row to the next
+  // Every page step issues the same buffer loads and stores whatever its slots: lanes with
+  // nothing to move use an offset past the end of the buffer range (loads return zero, stores
+  // are dropped).  Fixed counts keep the compiler's memory-counter waits exact, so the loads of
+  // the next page stay in flight while the current page is processed and stored.
+  constexpr int kOutOfRange = 0x40000000;
 
+  struct PageIn {
+    u32x4 x[4];  // 16 tokens x 128 channels as the B operand (zeros for slots not appended)
+    u32x4 vold;  // current bytes of this lane's V piece when its quad is only partly appended
+  };
+  auto page_rsrc = [&](int i) {
+    const int page_id = __builtin_amdgcn_readlane(page_ids, i);
+    return make_rsrc(a.pool + ((int64_t)page_id * a.hkv + h) * (int64_t)kPageHeadBytes, kPageHeadBytes);
+  };
+  auto load_page = [&](int i, PageIn& in) {
+    const bool live = i < npg;
+    const int pos0 = (pg_begin + i) * kPage;
+    const int slot_lo = max(s0 - pos0, 0), slot_hi = min(end_pos - pos0, kPage);
+    const uint8_t* base = src + ((int64_t)(t0 + pos0 - s0) * a.hkv + h) * (int64_t)(kHeadDim * 2);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, kPage * row_stride);
+    const int off = (live && n >= slot_lo && n < slot_hi) ? n * row_stride + 16 * g : kOutOfRange;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      bool use;
-      int neg;
-      if (HB == 128) {
-        use = true;
-        neg = popc((uint32_t)(kb & (nb >> 1))) & 1;
-      } else if (HB == 64) {
-        use = (kb >> 1) == (nb >> 2);
-        neg = (kb & 1) & ((nb >> 1) & 1);
-      } else {
-        use = kb == (nb >> 1);
-        neg = 0;
-      }
-      if (!use) continue;
-      const uint32_t* t = neg ? tm[nb & 1] : tp[nb & 1];
-      u32x4 bt = u32x4{t[0], t[1], t[2], t[3]};
-      if (BF16) {
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[kb]),
-                                                          __builtin_bit_cast(bf16x8, bt), acc[nb], 0, 0, 0);
-      } else {
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, xa[kb]),
-                                                         __builtin_bit_cast(f16x8, bt), acc[nb], 0, 0, 0);
-      }
-    }
-  }
+    for (int kb = 0; kb < 4; ++kb)
+      in.x[kb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 64 * kb, 0, 2));
+    const int q0 = n & ~3;
+    const bool partial = is_v && live && q0 + 3 >= slot_lo && q0 < slot_hi && (q0 < slot_lo || q0 + 4 > slot_hi);
+    const int voff = partial ? kVCodesOff + 256 * (n >> 2) + 64 * g + 16 * (n & 3) : kOutOfRange;
+    in.vold = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(live ? i : 0), voff, 0, 0));
+  };
 
-  // acc[nb][r] = sqrt(b) * y[token slot 4*kg + r][channel 16*nb + n]
-  constexpr float inv_sqrt_b = HB == 128 ? 0.08838834764831845f : (HB == 64 ? 0.125f : 1.0f);
-
-  uint32_t rowword[4];   // K-row word of each of this lane's 4 token slots
-  uint32_t paramword[4];
+  auto process = [&](int i, const PageIn& in) {
+    f32x4 acc[8];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (FMT == 0) {
-      // token-wise asymmetric INT4: fp16 scale = (max - min)/15, fp16 zero = min
-      float mn = acc[0][r], mx = acc[0][r];
+    for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nb = 1; nb < 8; ++nb) {
-        mn = fminf(mn, acc[nb][r]);
-        mx = fmaxf(mx, acc[nb][r]);
-      }
-      mn = row_min16(mn);
-      mx = row_max16(mx);
-      const float lo = mn * inv_sqrt_b;
-      const float hi = mx * inv_sqrt_b;
-      const uint32_t s_bits = f32_to_f16_bits((hi - lo) / 15.0f);
-      const uint32_t z_bits = f32_to_f16_bits(lo);
-      const float sf = f16_bits_to_f32(s_bits);
-      const float zf = f16_bits_to_f32(z_bits);
-      const float inv_s = sf > 0.0f ? 1.0f / sf : 0.0f;
-      uint32_t cw[8];
+    for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
-        const float t = fmaf(acc[nb][r], inv_sqrt_b, -zf);
-        const float d = __builtin_amdgcn_fmed3f(t * inv_s, 0.0f, 15.0f);
-        cw[nb] = __float_as_uint(d + 12582912.0f);  // 1.5 * 2^23: round to nearest even
-      }
-      rowword[r] = pack8(cw);
-      paramword[r] = s_bits | (z_bits << 16);
-    } else {
-      // MXFP4: e2m1 codes, UE8M0 exponent per 32 channels (nb pairs {2g, 2g+1})
-      uint32_t cw[8];
-      uint32_t ebytes = 0;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float y0 = acc[2 * g][r] * inv_sqrt_b;
-        const float y1 = acc[2 * g + 1][r] * inv_sqrt_b;
-        const float amax = row_max16(fmaxf(fabsf(y0), fabsf(y1)));
-        const int e = min(max((int)((__float_as_uint(amax) >> 23) & 255u) - 2, 0), 254);
-        ebytes |= (uint32_t)e << (8 * g);
-        cw[2 * g] = e2m1_code(ldexpf(y0, 127 - e));
-        cw[2 * g + 1] = e2m1_code(ldexpf(y1, 127 - e));
-      }
-      uint32_t word = 0;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) word |= cw[nb] << (4 * nb);
-      rowword[r] = word;
-      paramword[r] = ebytes;
-    }
-  }
-
-  // ---- paged stores ----
-  uint8_t* base = a.pool + ((int64_t)page_id * a.hkv + h) * (int64_t)kPageHeadBytes;
-  const int slot0 = 4 * kg;
-  if (!is_v) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int s = slot0 + r;
-      if (s >= slot_lo && s < slot_hi) *(uint32_t*)(base + 64 * s + 4 * n) = rowword[r];
-    }
-  } else {
-    // transpose the 4x4 bytes: V word q holds row byte (4n + q) of slots slot0..slot0+3
-    const uint32_t a01 = perm(rowword[1], rowword[0], 0x05010400u);
-    const uint32_t b01 = perm(rowword[1], rowword[0], 0x07030602u);
-    const uint32_t a23 = perm(rowword[3], rowword[2], 0x05010400u);
-    const uint32_t b23 = perm(rowword[3], rowword[2], 0x07030602u);
-    u32x4 vw;
-    vw[0] = perm(a23, a01, 0x05040100u);
-    vw[1] = perm(a23, a01, 0x07060302u);
-    vw[2] = perm(b23, b01, 0x05040100u);
-    vw[3] = perm(b23, b01, 0x07060302u);
-    uint8_t* dst = base + kVCodesOff + 256 * kg + 16 * n;
-    if (slot0 >= slot_lo && slot0 + 4 <= slot_hi) {
-      *(u32x4*)dst = vw;
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = slot0 + r;
-        if (s >= slot_lo && s < slot_hi) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) dst[4 * q + r] = (uint8_t)(vw[q] >> (8 * r));
+        bool use;
+        int neg;
+        if (HB == 128) {
+          use = true;
+          neg = popc((uint32_t)(kb & (nb >> 1))) & 1;
+        } else if (HB == 64) {
+          use = (kb >> 1) == (nb >> 2);
+          neg = (kb & 1) & ((nb >> 1) & 1);
+        } else {
+          use = kb == (nb >> 1);
+          neg = 0;
+        }
+        if (!use) continue;
+        const uint32_t* t = neg ? tm[nb & 1] : tp[nb & 1];
+        const u32x4 at = u32x4{t[0], t[1], t[2], t[3]};
+        if (BF16) {
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, at),
+                                                            __builtin_bit_cast(bf16x8, in.x[kb]), acc[nb], 0, 0, 0);
+        } else {
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, at),
+                                                           __builtin_bit_cast(f16x8, in.x[kb]), acc[nb], 0, 0, 0);
         }
       }
     }
-  }
-  if (n == 0) {
-    uint8_t* pdst = base + (is_v ? kVParamsOff : kKParamsOff) + 4 * slot0;
-    if (slot0 >= slot_lo && slot0 + 4 <= slot_hi) {
-      *(u32x4*)pdst = u32x4{paramword[0], paramword[1], paramword[2], paramword[3]};
-    } else {
+    // acc[nb][r] = sqrt(b) * y[slot n][channel 16*nb + 4*g + r]
+    constexpr float isb = HB == 128 ? 0.08838834764831845f : (HB == 64 ? 0.125f : 1.0f);
+
+    uint32_t row[4];   // K row words 4g + r of slot n
+    uint32_t param;    // (scale, zero) or four UE8M0 bytes of slot n
+    if (FMT == 0) {
+      // token-wise asymmetric INT4: fp16 scale = (max - min)/15, fp16 zero = min
+      float mn = acc[0][0], mx = acc[0][0];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          mn = fminf(mn, acc[nb][r]);
+          mx = fmaxf(mx, acc[nb][r]);
+        }
+      mn = fminf(mn, __shfl_xor(mn, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mn = fminf(mn, __shfl_xor(mn, 32));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float lo = mn * isb;
+      const float hi = mx * isb;
+      const uint32_t s_bits = f32_to_f16_bits((hi - lo) * (1.0f / 15.0f));
+      const uint32_t z_bits = f32_to_f16_bits(lo);
+      const float sf = f16_bits_to_f32(s_bits);
+      const float zf = f16_bits_to_f32(z_bits);
+      // e = clamp((y - z) / (15 s), 0, 1); the code is rne(15 e), rounded by the magic addend
+      // 1.5 * 2^23 inside one fma.  15 s is exact in fp32 (an fp16 times a 4-bit integer).
+      const float r15 = sf > 0.0f ? __builtin_amdgcn_rcpf(15.0f * sf) : 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int s = slot0 + r;
-        if (s >= slot_lo && s < slot_hi) *(uint32_t*)(pdst + 4 * r) = paramword[r];
+        uint32_t cw[8];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const float t = fmaf(acc[nb][r], isb, -zf);
+          const float e = __builtin_amdgcn_fmed3f(t * r15, 0.0f, 1.0f);
+          cw[nb] = __float_as_uint(fmaf(e, 15.0f, 12582912.0f));
+        }
+        row[r] = pack8(cw);
       }
+      param = s_bits | (z_bits << 16);
+    } else {
+      // MXFP4: e2m1 codes, UE8M0 exponent per 32 channels (tiles nb = 2G, 2G+1)
+      param = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) row[r] = 0;
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        float m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, fmaxf(fabsf(acc[2 * G][r]), fabsf(acc[2 * G + 1][r])));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const float amax = m * isb;
+        const int e = min(max((int)((__float_as_uint(amax) >> 23) & 255u) - 2, 0), 254);
+        param |= (uint32_t)e << (8 * G);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          row[r] |= e2m1_code(ldexpf(acc[2 * G][r] * isb, 127 - e)) << (8 * G);
+          row[r] |= e2m1_code(ldexpf(acc[2 * G + 1][r] * isb, 127 - e)) << (8 * G + 4);
+        }
+      }
+    }
+
+    // ---- paged stores ----
+    const int pos0 = (pg_begin + i) * kPage;
+    const int slot_lo = max(s0 - pos0, 0), slot_hi = min(end_pos - pos0, kPage);
+    const __amdgpu_buffer_rsrc_t pr = page_rsrc(i);
+    const bool valid = n >= slot_lo && n < slot_hi;
+    u32x4 out;
+    int off;
+    if (!is_v) {
+      out = u32x4{row[0], row[1], row[2], row[3]};
+      off = valid ? 64 * n + 16 * g : kOutOfRange;
+    } else {
+      // lane m of the quad takes row word 4g + m of the quad's four slots, then transposes the
+      // bytes: V word q holds row byte (16g + 4m + q) of slots 4(n/4) .. 4(n/4)+3
+      const int m = n & 3, q0 = n & ~3;
+      quad_transpose(row, m);
+      const uint32_t a01 = perm(row[1], row[0], 0x05010400u);
+      const uint32_t b01 = perm(row[1], row[0], 0x07030602u);
+      const uint32_t a23 = perm(row[3], row[2], 0x05010400u);
+      const uint32_t b23 = perm(row[3], row[2], 0x07030602u);
+      out[0] = perm(a23, a01, 0x05040100u);
+      out[1] = perm(a23, a01, 0x07060302u);
+      out[2] = perm(b23, b01, 0x05040100u);
+      out[3] = perm(b23, b01, 0x07060302u);
+      // byte r of every word belongs to slot q0 + r: keep the current bytes of slots outside
+      // the appended range (they were read with this page's inputs)
+      uint32_t keep = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) keep |= (q0 + r >= slot_lo && q0 + r < slot_hi) ? 0u : 0xFFu << (8 * r);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[q] = (out[q] & ~keep) | (in.vold[q] & keep);
+      off = keep != 0xFFFFFFFFu ? kVCodesOff + 256 * (n >> 2) + 64 * g + 16 * m : kOutOfRange;
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(out, pr, off, 0, 0);
+    const int poff = (g == 0 && valid) ? (is_v ? kVParamsOff : kKParamsOff) + 4 * n : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b32(param, pr, poff, 0, 0);
+  };
+
+  // Pages i = 0..npg-1: page i+1 loads while page i is processed.  Each step is nested in the
+  // previous one, so every wait sees the same sequence of earlier loads and stores.
+  static_assert(kAppendPagesPerWave == 4, "the page pipeline below is written out for four pages");
+  PageIn pa, pb;
+  load_page(0, pa);
+  load_page(1, pb);
+  process(0, pa);
+  if (npg > 1) {
+    load_page(2, pa);
+    process(1, pb);
+    if (npg > 2) {
+      load_page(3, pb);
+      process(2, pa);
+      if (npg > 3) process(3, pb);
     }
   }
 }
@@ -257,7 +318,8 @@ static hipError_t launch_t(const AppendParams& p, int grid_x, hipStream_t stream
 
 hipError_t launch_append(const AppendParams& p, bool bf16, int had_block, int fmt, hipStream_t stream) {
   // pages one sequence's new tokens can touch: ceil(max_new/16), plus one when misaligned
-  const int grid_x = (p.max_new + kPage - 1) / kPage + 1;
+  const int pages = (p.max_new + kPage - 1) / kPage + 1;
+  const int grid_x = (pages + kAppendPagesPerWave - 1) / kAppendPagesPerWave;
 #define KVQ_APPEND_CASE(BF, HBV, F) \
   if (bf16 == BF && had_block == HBV && fmt == F) return launch_t<BF, HBV, F>(p, grid_x, stream);
   KVQ_APPEND_CASE(true, 128, 0)

@@ -309,13 +309,13 @@ __device__ __forceinline__ void store_head(const DecodeParams& a, float o0, floa
 template <int FMT, int W, int D>
 __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   __shared__ DecodeSmem<W> sm;
-  const int tid = threadIdx.x;
+  const int tid = thread_id();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nsplit = a.plan.nsplit;
   const int P = a.plan.pages_per_split;
-  const int split = blockIdx.x % nsplit;
-  const int unit = blockIdx.x / nsplit;
+  const int split = block_id_x() % nsplit;
+  const int unit = block_id_x() / nsplit;
   const int kvh = unit % a.hkv;
   const int b = unit / a.hkv;
   const int G = a.group;
@@ -512,9 +512,9 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
 // Merge the split partials of every (sequence, kv head) that was split, rotate back, store.
 // One workgroup per (sequence, kv head); wave w handles heads w, w+4, ...
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams a) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(thread_id() >> 6);
+  const int unit = block_id_x();
   const int kvh = unit % a.hkv, b = unit / a.hkv;
   const int G = a.group;
   const int P = a.plan.pages_per_split;

@@ -25,9 +25,9 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
 // each thread owns channels a + 32q + 16e (q = 0..3, e = 0..1) of slot s, i.e. row bytes 4a..4a+3.
 __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   __shared__ float buf[2][kPage][kHeadDim];
-  const int tid = threadIdx.x;
+  const int tid = thread_id();
   const int s = tid >> 4, col = tid & 15;
-  const int i = blockIdx.x / p.hkv, h = blockIdx.x % p.hkv;
+  const int i = block_id_x() / p.hkv, h = block_id_x() % p.hkv;
   const uint8_t* base = p.pool + ((int64_t)p.page_ids[i] * p.hkv + h) * kPageHeadBytes;
   for (int which = 0; which < 2; ++which) {
     uint32_t word;  // row bytes 4col..4col+3 of slot s
@@ -77,10 +77,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                  int64_t n16) {
+                                                  int64_t n16, int64_t nthreads) {
   // each thread moves 4 x 16 bytes per step, all four loads issued before the stores
-  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = (int64_t)block_id_x() * 256 + thread_id();
   int64_t i = t;
   for (; i + 3 * nthreads < n16; i += 4 * nthreads) {
     const u32x4 a0 = src[i], a1 = src[i + nthreads], a2 = src[i + 2 * nthreads], a3 = src[i + 3 * nthreads];
@@ -102,7 +101,8 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t str
   int64_t blocks = (n16 + 255) / 256;
   if (blocks > 256 * 16) blocks = 256 * 16;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)src, (u32x4*)dst, n16);
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)src, (u32x4*)dst, n16,
+                     blocks * 256);
   return hipGetLastError();
 }
 

@@ -24,7 +24,14 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 // dtype codes (same values as kvq_dtype in kvq.h; duplicated so kernels need no C header)
 enum : int { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2, DT_E4M3 = 3 };
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// Work-item and workgroup ids straight from the hardware registers.  (The threadIdx/blockIdx
+// accessors go through device-library functions that this build's floating-point flags keep
+// from inlining, which would turn every use into a subroutine call.)
+__device__ __forceinline__ int thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int block_id_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int block_id_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+__device__ __forceinline__ int block_id_z() { return (int)__builtin_amdgcn_workgroup_id_z(); }
+__device__ __forceinline__ int lane_id() { return thread_id() & 63; }
 
 // ---- DPP row (16-lane) reductions; every lane of the row ends with the same bits ----
 // All patterns used below read lanes inside the same row, so bound_ctrl never applies; setting it

@@ -6,6 +6,9 @@
 
 namespace kvq {
 
+// consecutive pages of one (sequence, kv head, K|V) that one append wave processes
+constexpr int kAppendPagesPerWave = 4;
+
 struct AppendParams {
   uint8_t* pool;
   const uint8_t* k;
