@@ -238,10 +238,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--profile-run", action="store_true",
-                    help="short run for rocprofv3: few steps, no prefill and no CPU leg")
+                    help="short run for rocprofv3: few decode steps, three prefill appends, no CPU leg")
     args = ap.parse_args()
     if args.profile_run:
-        args.steps, args.warmup, args.no_prefill, args.no_cpu = 20, 5, True, True
+        args.steps, args.warmup, args.no_cpu = 20, 5, True
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -310,7 +310,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_prefill:
         log("[bench] prefill append")
-        res["prefill_append"] = time_prefill_append(dev)
+        res["prefill_append"] = time_prefill_append(dev, repeats=3 if args.profile_run else 10)
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)

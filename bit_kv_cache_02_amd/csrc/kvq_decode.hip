@@ -83,11 +83,20 @@ struct PageData<1> {
   u32x4 vp4;    // UE8M0 bytes of tokens 4jg..4jg+3 (V)
 };
 
+// Offset past the end of every buffer range used here: a load with it returns zeros without a
+// memory access.  Loads that are not needed still issue with it, so every path through a kernel
+// issues the same sequence of loads and the compiler's memory-counter waits stay exact (a load
+// skipped on some path makes it wait for everything issued after the value it needs).
+constexpr int kOutOfRange = 0x40000000;
+
 // `base` is wave-uniform: the buffer descriptor lives in scalar registers and the per-lane offsets
-// are loop invariant, so a page costs no vector address arithmetic.
+// are loop invariant, so a page costs no vector address arithmetic.  `live` false turns the four
+// loads into out-of-range ones.
 template <int FMT>
-__device__ __forceinline__ PageData<FMT> load_page(const uint8_t* base, int koff, int voff, int poff, int qoff) {
+__device__ __forceinline__ PageData<FMT> load_page(const uint8_t* base, bool live, int koff, int voff, int poff,
+                                                   int qoff) {
   const __amdgpu_buffer_rsrc_t r = make_rsrc(base, kPageHeadBytes);
+  if (!live) koff = voff = poff = qoff = kOutOfRange;
   PageData<FMT> d;
   // cache policy 2 = nontemporal: the pages are streamed once per step
   d.k = __builtin_amdgcn_raw_buffer_load_b128(r, koff, 0, 2);
@@ -323,28 +332,44 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   const int n = lane & 15;   // token (QK, softmax) / output column (p.V)
   const int jg = lane >> 4;  // row group: heads 2jg, 2jg+1
 
-  // ---- 0. query loads first (they depend on nothing); wave w holds heads w, w+W, ... ----
+  // ---- 0. loads that depend on nothing: the query words, then this wave's block-table entries
+  //         (the page loads wait for those, and with them for the query words issued just
+  //         before).  Pages are dealt to the waves round-robin (wave w takes pages
+  //         p_begin + w + W*i), so the entries a wave needs do not depend on the sequence length.
+  // Wave w holds heads w, w+W, ...; a wave without a head in a slot loads head G-1 and ignores it.
+  // Each element is fetched as the aligned 32-bit word holding it.
+  const int L = a.seq_lens[b];
   constexpr int kMaxHeadsPerWave = (kMaxG + W - 1) / W;
-  float qv[kMaxHeadsPerWave][2];
+  const int esz = __builtin_amdgcn_readfirstlane(a.q_dtype == DT_F32 ? 4 : (a.q_dtype == DT_E4M3 ? 1 : 2));
+  const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(a.q, a.num_seqs * a.hq * kHeadDim * esz);
+  uint32_t qword[kMaxHeadsPerWave][2];
+  int qshift[kMaxHeadsPerWave][2];
 #pragma unroll
   for (int k = 0; k < kMaxHeadsPerWave; ++k) {
-    const int g = wave + k * W;
-    qv[k][0] = qv[k][1] = 0.0f;
-    if (g < G) {
-      const int64_t qb = ((int64_t)b * a.hq + kvh * G + g) * kHeadDim;
-      qv[k][0] = load_elem(a.q, qb + lane, a.q_dtype);
-      qv[k][1] = load_elem(a.q, qb + lane + 64, a.q_dtype);
+    const int g = min(wave + k * W, G - 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int byte = (((b * a.hq + kvh * G + g) * kHeadDim) + lane + 64 * e) * esz;
+      qword[k][e] = __builtin_amdgcn_raw_buffer_load_b32(q_rsrc, byte & ~3, 0, 0);
+      qshift[k][e] = 8 * (byte & 3);
     }
   }
-
-  // Pages are dealt to the waves round-robin (wave w takes pages p_begin + w + W*i), so the block
-  // table entries a wave needs do not depend on the sequence length and load alongside it.
   const int p_begin = split * P;
   const int pw0 = p_begin + wave;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const int bt_idx = pw0 + W * lane;
-  const int pid_vec = (lane * W < P && bt_idx < a.max_pages) ? bt[bt_idx] : 0;
-  const int L = a.seq_lens[b];
+  const int pid_vec = (int)__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(bt, a.max_pages * 4), lane * W < P ? 4 * bt_idx : kOutOfRange, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);  // all of the above issues before anything waits
+  // converted here, before the page loads are issued: the wait for the block-table entries
+  // covers these words, and none of the page loads has to complete before the query math
+  float qv[kMaxHeadsPerWave][2];
+#pragma unroll
+  for (int k = 0; k < kMaxHeadsPerWave; ++k)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) qv[k][e] = raw_to_f32(qword[k][e] >> qshift[k][e], a.q_dtype) * a.q_scale;
+  __builtin_amdgcn_sched_barrier(0);
+
   const int n_pages = (L + kPage - 1) / kPage;
   if (p_begin >= n_pages) return;  // uniform over the workgroup
   const int p_end = min(p_begin + P, n_pages);
@@ -357,7 +382,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   auto page_base = [&](int i) {
     // uniform by construction; readfirstlane makes that explicit so the buffer descriptor stays in
     // scalar registers
-    const uint64_t addr = (uint64_t)(pool_h + (int64_t)__builtin_amdgcn_readlane(pid_vec, i) * page_stride);
+    const uint64_t addr = (uint64_t)(pool_h + (int64_t)__builtin_amdgcn_readlane(pid_vec, min(i, 63)) * page_stride);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
     return (const uint8_t*)(((uint64_t)hi << 32) | lo);
@@ -366,8 +391,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   constexpr int NB = D + 1;  // register buffers: D pages in flight plus the one being processed
   PageData<FMT> st[NB];
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < npw) st[d] = load_page<FMT>(page_base(d), koff, voff, poff, qoff);
+  for (int d = 0; d < D; ++d) st[d] = load_page<FMT>(page_base(d), d < npw, koff, voff, poff, qoff);
 
   // ---- 2. q' = R_b (q_scale q) in registers, then 16-bit fixed point q' ~= delta_g * Q with
   //         |Q| <= 32000, stored as two int8 limbs (Q = 256*hi + lo) in the A-tile byte order ----
@@ -375,7 +399,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   for (int k = 0; k < kMaxHeadsPerWave; ++k) {
     const int g = wave + k * W;
     if (g < G) {
-      float v0 = qv[k][0] * a.q_scale, v1 = qv[k][1] * a.q_scale;
+      float v0 = qv[k][0], v1 = qv[k][1];
       fwht_wave(v0, v1, a.had_block, lane);
       v0 *= isb;
       v1 *= isb;
@@ -447,9 +471,9 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
 #pragma unroll
     for (int d = 0; d < NB; ++d) {
       const int i = i0 + d;
+      // page i sits in buffer d; page i + D goes to the buffer freed by page i - 1
+      st[(d + D) % NB] = load_page<FMT>(page_base(i + D), i + D < npw, koff, voff, poff, qoff);
       if (i < npw) {
-        // page i sits in buffer d; page i + D goes to the buffer freed by page i - 1
-        if (i + D < npw) st[(d + D) % NB] = load_page<FMT>(page_base(i + D), koff, voff, poff, qoff);
         if constexpr (FMT == 0)
           process_page(st[d], valid0 - i * W * kPage, s, qa, alpha0, beta0, alpha1, beta1, has0, has1, n, jg,
                        a_row_used, sm.ptile[wave]);

@@ -102,6 +102,16 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return s ? -v : v;
 }
 
+// Low bits of `bits` (an element already shifted down from its 32-bit word) as dtype `dt`.
+__device__ __forceinline__ float raw_to_f32(uint32_t bits, int dt) {
+  switch (dt) {
+    case DT_F16: return f16_bits_to_f32(bits & 0xFFFFu);
+    case DT_BF16: return bf16_bits_to_f32(bits & 0xFFFFu);
+    case DT_F32: return __uint_as_float(bits);
+    default: return e4m3_to_f32(bits & 0xFFu);
+  }
+}
+
 __device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
   switch (dt) {
     case DT_F16: return f16_bits_to_f32(((const uint16_t*)p)[i]);
