@@ -323,8 +323,12 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nsplit = a.plan.nsplit;
   const int P = a.plan.pages_per_split;
-  const int split = block_id_x() % nsplit;
-  const int unit = block_id_x() / nsplit;
+  // split-major order: every unit's first split is dispatched before any second split, so the
+  // workgroups that have pages spread over the CUs and the empty ones (splits past a short
+  // sequence's end) come last and exit at once
+  const int units = a.num_seqs * a.hkv;
+  const int split = block_id_x() / units;
+  const int unit = block_id_x() % units;
   const int kvh = unit % a.hkv;
   const int b = unit / a.hkv;
   const int G = a.group;
@@ -534,7 +538,9 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
 }
 
 // Merge the split partials of every (sequence, kv head) that was split, rotate back, store.
-// One workgroup per (sequence, kv head); wave w handles heads w, w+4, ...
+// One workgroup per (sequence, kv head); wave w handles heads w, w+4, ...  Lane s takes split s
+// for the running maxima and weights (64 splits per pass); the partial outputs are then summed
+// with lanes over channels, four splits' loads in flight at a time.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams a) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(thread_id() >> 6);
@@ -547,16 +553,39 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams a) {
   if (nsplit_b <= 1) return;
   const int64_t s0 = (int64_t)unit * a.plan.nsplit;
   for (int g = wave; g < G; g += 4) {
+    const float* ml = a.part_ml + (s0 * G + g) * 2;  // split s at ml[2 G s]
     float M = kNegBig;
-    for (int s = 0; s < nsplit_b; ++s) M = fmaxf(M, a.part_ml[((s0 + s) * G + g) * 2]);
-    float O0 = 0.f, O1 = 0.f, Ls = 0.f;
-    for (int s = 0; s < nsplit_b; ++s) {
-      const float f = exp2f(a.part_ml[((s0 + s) * G + g) * 2] - M);
-      const float* po = a.part_o + ((s0 + s) * G + g) * kHeadDim;
-      O0 = fmaf(f, po[lane], O0);
-      O1 = fmaf(f, po[lane + 64], O1);
-      Ls = fmaf(f, a.part_ml[((s0 + s) * G + g) * 2 + 1], Ls);
+    for (int s = lane; s < nsplit_b; s += 64) M = fmaxf(M, ml[2 * G * s]);
+    M = wave_max(M);
+    float O0 = 0.f, O1 = 0.f, Lp = 0.f;
+    for (int c = 0; c < nsplit_b; c += 64) {
+      const int s = c + lane;
+      const float f = s < nsplit_b ? exp2f(ml[2 * G * s] - M) : 0.0f;
+      if (s < nsplit_b) Lp = fmaf(f, ml[2 * G * s + 1], Lp);
+      const int cnt = min(64, nsplit_b - c);
+      const float* po = a.part_o + ((s0 + c) * G + g) * kHeadDim;
+      int j = 0;
+      for (; j + 4 <= cnt; j += 4) {
+        float x[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x[u][0] = po[(j + u) * G * kHeadDim + lane];
+          x[u][1] = po[(j + u) * G * kHeadDim + lane + 64];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j + u));
+          O0 = fmaf(fj, x[u][0], O0);
+          O1 = fmaf(fj, x[u][1], O1);
+        }
+      }
+      for (; j < cnt; ++j) {
+        const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
+        O0 = fmaf(fj, po[j * G * kHeadDim + lane], O0);
+        O1 = fmaf(fj, po[j * G * kHeadDim + lane + 64], O1);
+      }
     }
+    const float Ls = wave_sum_f(Lp);
     store_head(a, O0 / Ls, O1 / Ls, b, kvh * G + g, lane);
   }
 }

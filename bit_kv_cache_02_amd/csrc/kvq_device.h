@@ -74,6 +74,12 @@ __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, __shfl_xor(x, 32));
   return x;
 }
+__device__ __forceinline__ float wave_sum_f(float x) {
+  x = row_sum16(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
 __device__ __forceinline__ int wave_sum_i(int x) {
   for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
   return x;
