@@ -291,21 +291,18 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
     __builtin_amdgcn_raw_buffer_store_b32(param, pr, poff, 0, 0);
   };
 
-  // Pages i = 0..npg-1: page i+1 loads while page i is processed.  Each step is nested in the
-  // previous one, so every wait sees the same sequence of earlier loads and stores.
-  static_assert(kAppendPagesPerWave == 4, "the page pipeline below is written out for four pages");
-  PageIn pa, pb;
-  load_page(0, pa);
-  load_page(1, pb);
-  process(0, pa);
-  if (npg > 1) {
-    load_page(2, pa);
-    process(1, pb);
-    if (npg > 2) {
-      load_page(3, pb);
-      process(2, pa);
-      if (npg > 3) process(3, pb);
-    }
+  // Pages i = 0..npg-1: page i+1 loads while page i is processed.  The loop is unrolled and each
+  // step is reached only through the previous one, so every wait sees the same sequence of earlier
+  // loads and stores.
+  PageIn buf[2];
+  load_page(0, buf[0]);
+  __builtin_amdgcn_sched_barrier(0);  // page 0's V read-back issues before page 1's loads
+#pragma unroll
+  for (int i = 0; i < kAppendPagesPerWave; ++i) {
+    if (i + 1 < kAppendPagesPerWave) load_page(i + 1, buf[(i + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);  // the next page's loads issue before this page waits
+    process(i, buf[i & 1]);
+    if (i + 1 >= npg) break;
   }
 }
 
