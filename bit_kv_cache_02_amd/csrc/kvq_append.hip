@@ -36,16 +36,6 @@ __device__ __forceinline__ uint32_t pack8(const uint32_t* c) {
   return even | (odd << 4);
 }
 
-// Round |r| (< 8) to the e2m1 grid {0,.5,1,1.5,2,3,4,6}: nearest, ties to the even index,
-// saturating at 6.  Adding then subtracting 2^22/2^23/2^24 rounds to steps 0.5/1/2 (RNE).
-__device__ __forceinline__ uint32_t e2m1_code(float r) {
-  float m = fabsf(r);
-  float c = m < 2.0f ? 4194304.0f : (m < 4.0f ? 8388608.0f : 16777216.0f);
-  float v = __builtin_fminf((m + c) - c, 6.0f);
-  uint32_t idx = v < 1.0f ? (uint32_t)(v * 2.0f) : ((__float_as_uint(v) >> 22) - 252u);
-  return idx | (r < 0.0f ? 8u : 0u);
-}
-
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);

@@ -45,6 +45,11 @@ struct DecodeSmem {
   float wo[W][kMaxG][kHeadDim];
   float wm[W][kMaxG];
   float wl[W][kMaxG];
+  // fused step: codes of the appended K (0) and V (1) vectors, their packed 64-byte rows and
+  // their parameter words
+  uint8_t acode[2][kHeadDim];
+  uint32_t arow[2][16];
+  uint32_t aparam[2];
 };
 
 __device__ __forceinline__ float inv_sqrt_block(int hb) {
@@ -301,6 +306,29 @@ __device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid
   }
 }
 
+// Fused step: put the appended token's bytes (staged in LDS) into the registers of the page that
+// holds it, whatever the page load returned for that slot.
+template <int FMT>
+__device__ __forceinline__ void patch_appended(PageData<FMT>& pg, const uint32_t (&arow)[2][16],
+                                               const uint32_t (&aparam)[2], int slot, int n, int jg) {
+  if (n == slot) {
+    pg.k = u32x4{arow[0][4 * jg], arow[0][4 * jg + 1], arow[0][4 * jg + 2], arow[0][4 * jg + 3]};
+    pg.kp = aparam[0];
+    if constexpr (FMT == 0) pg.vp = aparam[1];
+  }
+  if (jg == (slot >> 2)) {
+    // V word q holds row byte 4n+q of tokens 4jg .. 4jg+3, one byte each
+    const int sh = 8 * (slot & 3);
+    const uint8_t* vrow = (const uint8_t*)arow[1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pg.v[q] = (pg.v[q] & ~(0xFFu << sh)) | ((uint32_t)vrow[4 * n + q] << sh);
+    if constexpr (FMT == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pg.vp4[r] = (slot & 3) == r ? aparam[1] : pg.vp4[r];  // no dynamic index
+    }
+  }
+}
+
 // Rotate one head's normalised o' (element lane in o0, lane + 64 in o1) back and store it.
 __device__ __forceinline__ void store_head(const DecodeParams& a, float o0, float o1, int b, int h, int lane) {
   float scale = 1.0f;
@@ -362,8 +390,32 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   const int pw0 = p_begin + wave;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const int bt_idx = pw0 + W * lane;
-  const int pid_vec = (int)__builtin_amdgcn_raw_buffer_load_b32(
-      make_rsrc(bt, a.max_pages * 4), lane * W < P ? 4 * bt_idx : kOutOfRange, 0, 0);
+  const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(bt, a.max_pages * 4);
+  const int pid_vec = (int)__builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, lane * W < P ? 4 * bt_idx : kOutOfRange, 0, 0);
+
+  // Fused step: the workgroup that holds the sequence's last page appends the new token there,
+  // wave W-1 the K vector and wave W-2 the V vector (their words load here; every wave issues
+  // the loads, out of range where it does not append).
+  const int n_pages = (L + kPage - 1) / kPage;
+  const int last_pg = n_pages - 1;
+  const int app_slot = (L - 1) & (kPage - 1);
+  const bool app_wg = a.append && last_pg >= p_begin && last_pg < p_begin + P;
+  const int app_which = wave == W - 1 ? 0 : 1;  // 0: K, 1: V
+  const bool app_wave = app_wg && wave >= W - 2;
+  uint32_t nword[2];
+  int nshift[2];
+  {
+    // an empty range when this wave does not append: nothing can be read whatever the offset
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(app_which ? a.vnew : a.knew, app_wave ? a.num_seqs * a.hkv * kHeadDim * 2 : 0);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int byte = ((b * a.hkv + kvh) * kHeadDim + lane + 64 * e) * 2;
+      nword[e] = __builtin_amdgcn_raw_buffer_load_b32(r, app_wave ? (byte & ~3) : kOutOfRange, 0, 0);
+      nshift[e] = 8 * (byte & 3);
+    }
+  }
+  const int app_pid_w = (int)__builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, app_wg ? 4 * last_pg : kOutOfRange, 0, 0);
   __builtin_amdgcn_sched_barrier(0);  // all of the above issues before anything waits
   // converted here, before the page loads are issued: the wait for the block-table entries
   // covers these words, and none of the page loads has to complete before the query math
@@ -374,7 +426,6 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
     for (int e = 0; e < 2; ++e) qv[k][e] = raw_to_f32(qword[k][e] >> qshift[k][e], a.q_dtype) * a.q_scale;
   __builtin_amdgcn_sched_barrier(0);
 
-  const int n_pages = (L + kPage - 1) / kPage;
   if (p_begin >= n_pages) return;  // uniform over the workgroup
   const int p_end = min(p_begin + P, n_pages);
   const int nsplit_b = (n_pages + P - 1) / P;
@@ -440,6 +491,65 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       }
     }
   }
+  // ---- 2b. fused step: rotate and quantize the new K / V vector (one per appending wave),
+  //          exactly as the append path defines it, stage its row in LDS for the wave that
+  //          streams the last page, and store it into the page ----
+  uint32_t app_word = 0, app_byte = 0, app_param = 0;
+  if (app_wave) {
+    float x0 = raw_to_f32(nword[0] >> nshift[0], a.kv_dtype), x1 = raw_to_f32(nword[1] >> nshift[1], a.kv_dtype);
+    fwht_wave(x0, x1, a.had_block, lane);
+    x0 *= isb;
+    x1 *= isb;
+    uint32_t c0, c1;
+    if constexpr (FMT == 0) {
+      const float lo = -wave_max(-fminf(x0, x1)), hi = wave_max(fmaxf(x0, x1));
+      const uint32_t s_bits = f32_to_f16_bits((hi - lo) * (1.0f / 15.0f));
+      const uint32_t z_bits = f32_to_f16_bits(lo);
+      const float sf = f16_bits_to_f32(s_bits), zf = f16_bits_to_f32(z_bits);
+      const float r15 = sf > 0.0f ? __builtin_amdgcn_rcpf(15.0f * sf) : 0.0f;
+      c0 = __float_as_uint(fmaf(__builtin_amdgcn_fmed3f((x0 - zf) * r15, 0.0f, 1.0f), 15.0f, 12582912.0f)) & 15u;
+      c1 = __float_as_uint(fmaf(__builtin_amdgcn_fmed3f((x1 - zf) * r15, 0.0f, 1.0f), 15.0f, 12582912.0f)) & 15u;
+      app_param = s_bits | (z_bits << 16);
+    } else {
+      // UE8M0 exponent per 32 channels: lanes 0-31 / 32-63 hold groups 0 / 1 (x0) and 2 / 3 (x1)
+      float m0 = row_max16(fabsf(x0)), m1 = row_max16(fabsf(x1));
+      m0 = fmaxf(m0, __shfl_xor(m0, 16));
+      m1 = fmaxf(m1, __shfl_xor(m1, 16));
+      const int e0 = min(max((int)((__float_as_uint(m0) >> 23) & 255u) - 2, 0), 254);
+      const int e1 = min(max((int)((__float_as_uint(m1) >> 23) & 255u) - 2, 0), 254);
+      c0 = e2m1_code(ldexpf(x0, 127 - e0));
+      c1 = e2m1_code(ldexpf(x1, 127 - e1));
+      app_param = (uint32_t)__builtin_amdgcn_readlane(e0, 0) | ((uint32_t)__builtin_amdgcn_readlane(e0, 32) << 8) |
+                  ((uint32_t)__builtin_amdgcn_readlane(e1, 0) << 16) | ((uint32_t)__builtin_amdgcn_readlane(e1, 32) << 24);
+    }
+    sm.acode[app_which][lane] = (uint8_t)c0;
+    sm.acode[app_which][lane + 64] = (uint8_t)c1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // row byte 4a+q holds channels a+32q (low nibble) and a+32q+16 (high nibble)
+    const int ra = lane >> 2, rq = lane & 3;
+    app_byte = (uint32_t)sm.acode[app_which][ra + 32 * rq] | ((uint32_t)sm.acode[app_which][ra + 32 * rq + 16] << 4);
+    ((uint8_t*)sm.arow[app_which])[lane] = (uint8_t)app_byte;
+    if (lane == 0) sm.aparam[app_which] = app_param;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    app_word = sm.arow[app_which][lane & 15];
+  }
+  {
+    // every wave issues the three stores; out of range unless it appends
+    const int app_pid = __builtin_amdgcn_readfirstlane(app_pid_w);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(a.pool + (int64_t)kvh * kPageHeadBytes + (int64_t)app_pid * page_stride,
+                                               kPageHeadBytes);
+    const int kw = (app_wave && app_which == 0 && lane < 16) ? 64 * app_slot + 4 * lane : kOutOfRange;
+    const int vb = (app_wave && app_which == 1) ? kVCodesOff + 256 * (app_slot >> 2) + 4 * lane + (app_slot & 3)
+                                                : kOutOfRange;
+    const int pw = (app_wave && lane == 0) ? (app_which ? kVParamsOff : kKParamsOff) + 4 * app_slot : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b32(app_word, r, kw, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)app_byte, r, vb, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(app_param, r, pw, 0, 0);
+  }
   __syncthreads();
 
   const int ga = n >> 1;   // A-tile row 2g+limb -> head of this lane's A row
@@ -478,6 +588,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       // page i sits in buffer d; page i + D goes to the buffer freed by page i - 1
       st[(d + D) % NB] = load_page<FMT>(page_base(i + D), i + D < npw, koff, voff, poff, qoff);
       if (i < npw) {
+        if (app_wg && pw0 + W * i == last_pg) patch_appended<FMT>(st[d], sm.arow, sm.aparam, app_slot, n, jg);
         if constexpr (FMT == 0)
           process_page(st[d], valid0 - i * W * kPage, s, qa, alpha0, beta0, alpha1, beta1, has0, has1, n, jg,
                        a_row_used, sm.ptile[wave]);
@@ -630,18 +741,14 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int hkv, int group) {
   if (plan.nsplit <= 1) return 0;
-  const size_t units = (size_t)num_seqs * hkv;
-  const size_t slots = units * plan.nsplit;
-  return align256(units * 4) + align256(slots * group * 2 * 4) + slots * group * kHeadDim * 4;
+  const size_t slots = (size_t)num_seqs * hkv * plan.nsplit;
+  return align256(slots * group * 2 * 4) + slots * group * kHeadDim * 4;
 }
 
-void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, int group,
-                     int32_t** counters, float** part_ml, float** part_o) {
-  const size_t units = (size_t)num_seqs * hkv;
-  const size_t slots = units * plan.nsplit;
+void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, int group, float** part_ml,
+                     float** part_o) {
+  const size_t slots = (size_t)num_seqs * hkv * plan.nsplit;
   uint8_t* p = (uint8_t*)ws;
-  *counters = (int32_t*)p;
-  p += align256(units * 4);
   *part_ml = (float*)p;
   p += align256(slots * group * 2 * 4);
   *part_o = (float*)p;

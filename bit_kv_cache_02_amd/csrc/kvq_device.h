@@ -141,6 +141,16 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 
 __device__ __forceinline__ int popc(uint32_t x) { return __builtin_popcount(x); }
 
+// Round |r| (< 8) to the e2m1 grid {0,.5,1,1.5,2,3,4,6}: nearest, ties to the even index,
+// saturating at 6.  Adding then subtracting 2^22/2^23/2^24 rounds to steps 0.5/1/2 (RNE).
+__device__ __forceinline__ uint32_t e2m1_code(float r) {
+  float m = fabsf(r);
+  float c = m < 2.0f ? 4194304.0f : (m < 4.0f ? 8388608.0f : 16777216.0f);
+  float v = __builtin_fminf((m + c) - c, 6.0f);
+  uint32_t idx = v < 1.0f ? (uint32_t)(v * 2.0f) : ((__float_as_uint(v) >> 22) - 252u);
+  return idx | (r < 0.0f ? 8u : 0u);
+}
+
 // Raw buffer resource over `bytes` bytes at `p` (gfx9 dword3 0x00020000); loads past the end
 // return zero instead of faulting.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {

@@ -33,6 +33,8 @@ int check_cache(const kvq_cache* c) {
   if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache descriptor is NULL");
   if (!c->pool) return fail(KVQ_ERR_INVALID_ARG, "cache->pool is NULL");
   if (c->num_kv_heads < 1) return fail(KVQ_ERR_INVALID_ARG, "num_kv_heads must be >= 1 (got %d)", c->num_kv_heads);
+  // the kernels address a page's 16 token rows through one 32-bit buffer range
+  if (c->num_kv_heads > 1024) return fail(KVQ_ERR_UNSUPPORTED, "num_kv_heads %d above 1024", c->num_kv_heads);
   if (c->num_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "num_pages must be >= 1");
   if (c->reserved != 0) return fail(KVQ_ERR_INVALID_ARG, "cache->reserved must be 0");
   if (c->head_dim != KVQ_HEAD_DIM) return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", c->head_dim);
@@ -83,6 +85,7 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t kv_
   if (kv_dtype != KVQ_F16 && kv_dtype != KVQ_BF16) return fail(KVQ_ERR_UNSUPPORTED, "kv_dtype %d unsupported (F16 or BF16)", kv_dtype);
   if (num_tokens < 0 || num_seqs < 0) return fail(KVQ_ERR_INVALID_ARG, "num_tokens and num_seqs must be >= 0");
   if (max_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (max_pages > (1 << 24)) return fail(KVQ_ERR_UNSUPPORTED, "max_pages %d above 2^24", max_pages);
   if (max_new_tokens < 0) return fail(KVQ_ERR_INVALID_ARG, "max_new_tokens must be >= 0");
   if ((((uintptr_t)k) | ((uintptr_t)v)) & 15) return fail(KVQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
   if (num_seqs > 65535) return fail(KVQ_ERR_UNSUPPORTED, "num_seqs %d above 65535", num_seqs);
@@ -121,12 +124,12 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_q_heads, i
   return kvq::decode_workspace_bytes(plan, num_seqs, cache->num_kv_heads, num_q_heads / cache->num_kv_heads);
 }
 
-int kvq_decode_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, float q_scale,
-                    int32_t num_q_heads, int32_t num_seqs, const int32_t* seq_lens,
-                    int32_t max_seq_len, const int32_t* block_table, int32_t max_pages,
-                    float sm_scale, void* out, int32_t out_dtype, uint32_t flags,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error[0] = 0;
+// Shared body of kvq_decode_attn and kvq_decode_step (knew == NULL: no append).
+static int decode_common(const kvq_cache* cache, const void* knew, const void* vnew, int32_t kv_dtype,
+                         const void* q, int32_t q_dtype, float q_scale, int32_t num_q_heads, int32_t num_seqs,
+                         const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                         int32_t max_pages, float sm_scale, void* out, int32_t out_dtype, uint32_t flags,
+                         void* workspace, size_t workspace_bytes, void* stream, const char* what) {
   int st = decode_geometry(cache, num_q_heads, num_seqs, max_seq_len);
   if (st != KVQ_OK) return st;
   if (!q || !seq_lens || !block_table || !out) return fail(KVQ_ERR_INVALID_ARG, "q, seq_lens, block_table and out must not be NULL");
@@ -134,10 +137,19 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, floa
   if (out_dtype != KVQ_F32 && out_dtype != KVQ_F16 && out_dtype != KVQ_BF16)
     return fail(KVQ_ERR_UNSUPPORTED, "out_dtype %d unsupported (F32, F16 or BF16)", out_dtype);
   if (max_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (max_pages > (1 << 24)) return fail(KVQ_ERR_UNSUPPORTED, "max_pages %d above 2^24", max_pages);
+  // the query (and new K/V) tensors are addressed through one 32-bit buffer range each
+  if ((int64_t)num_seqs * num_q_heads * KVQ_HEAD_DIM * 4 >= (1ll << 30))
+    return fail(KVQ_ERR_UNSUPPORTED, "num_seqs * num_q_heads %lld too large", (long long)num_seqs * num_q_heads);
   if ((int64_t)max_seq_len > (int64_t)max_pages * KVQ_PAGE_SIZE)
     return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d exceeds max_pages*16 = %lld", max_seq_len, (long long)max_pages * KVQ_PAGE_SIZE);
   if (flags & ~KVQ_OUT_ROTATED) return fail(KVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (!std::isfinite(q_scale) || !std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARG, "q_scale and sm_scale must be finite");
+  const bool append = knew != nullptr || vnew != nullptr;
+  if (append) {
+    if (!knew || !vnew) return fail(KVQ_ERR_INVALID_ARG, "k and v must both be given");
+    if (kv_dtype != KVQ_F16 && kv_dtype != KVQ_BF16) return fail(KVQ_ERR_UNSUPPORTED, "kv_dtype %d unsupported (F16 or BF16)", kv_dtype);
+  }
   if (num_seqs == 0) return KVQ_OK;
   const int hkv = cache->num_kv_heads;
   const int group = num_q_heads / hkv;
@@ -150,9 +162,9 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, floa
     if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (workspace_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes given, %zu required", workspace_bytes, need);
     if (((uintptr_t)workspace) & 255) return fail(KVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    kvq::carve_workspace(workspace, plan, num_seqs, hkv, group, &p.counters, &p.part_ml, &p.part_o);
+    kvq::carve_workspace(workspace, plan, num_seqs, hkv, group, &p.part_ml, &p.part_o);
   }
-  p.pool = (const uint8_t*)cache->pool;
+  p.pool = (uint8_t*)cache->pool;
   p.q = q;
   p.seq_lens = seq_lens;
   p.block_table = block_table;
@@ -168,8 +180,35 @@ int kvq_decode_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, floa
   p.out_rotated = (flags & KVQ_OUT_ROTATED) ? 1 : 0;
   p.q_scale = q_scale;
   p.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  p.knew = (const uint8_t*)knew;
+  p.vnew = (const uint8_t*)vnew;
+  p.kv_dtype = append ? kv_dtype : KVQ_BF16;
+  p.append = append ? 1 : 0;
   p.plan = plan;
-  return hip_status(kvq::launch_decode(p, cache->format, (hipStream_t)stream), "kvq_decode_attn launch");
+  return hip_status(kvq::launch_decode(p, cache->format, (hipStream_t)stream), what);
+}
+
+int kvq_decode_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, float q_scale,
+                    int32_t num_q_heads, int32_t num_seqs, const int32_t* seq_lens,
+                    int32_t max_seq_len, const int32_t* block_table, int32_t max_pages,
+                    float sm_scale, void* out, int32_t out_dtype, uint32_t flags,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  return decode_common(cache, nullptr, nullptr, 0, q, q_dtype, q_scale, num_q_heads, num_seqs, seq_lens,
+                       max_seq_len, block_table, max_pages, sm_scale, out, out_dtype, flags, workspace,
+                       workspace_bytes, stream, "kvq_decode_attn launch");
+}
+
+int kvq_decode_step(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype, const void* q,
+                    int32_t q_dtype, float q_scale, int32_t num_q_heads, int32_t num_seqs,
+                    const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                    int32_t max_pages, float sm_scale, void* out, int32_t out_dtype, uint32_t flags,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!k || !v) return fail(KVQ_ERR_INVALID_ARG, "k and v must not be NULL");
+  return decode_common(cache, k, v, kv_dtype, q, q_dtype, q_scale, num_q_heads, num_seqs, seq_lens,
+                       max_seq_len, block_table, max_pages, sm_scale, out, out_dtype, flags, workspace,
+                       workspace_bytes, stream, "kvq_decode_step launch");
 }
 
 int kvq_dequant_page(const kvq_cache* cache, const int32_t* page_ids, int32_t n, float* out_k,

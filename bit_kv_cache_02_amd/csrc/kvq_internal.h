@@ -30,14 +30,13 @@ struct DecodePlan {
 };
 
 struct DecodeParams {
-  const uint8_t* pool;
+  uint8_t* pool;     // written only by the fused step (the appended token's bytes)
   const void* q;
   const int32_t* seq_lens;
   const int32_t* block_table;
   void* out;
   float* part_o;     // [units][nsplit][G][128] split partials (unnormalised o')
   float* part_ml;    // [units][nsplit][G][2]   running max (log2 domain) and sum
-  int32_t* counters; // [units] arrival counters, zero between calls
   int32_t hkv;
   int32_t group;     // q heads per kv head (1..8)
   int32_t hq;
@@ -49,6 +48,12 @@ struct DecodeParams {
   int32_t out_rotated;
   float q_scale;
   float sm_scale_log2;  // sm_scale * log2(e)
+  // fused step (append != 0): token seq_lens[b]-1 of every sequence is appended from
+  // knew/vnew [num_seqs][hkv][128] (kv_dtype F16 or BF16) before it is attended
+  const uint8_t* knew;
+  const uint8_t* vnew;
+  int32_t kv_dtype;
+  int32_t append;
   DecodePlan plan;
 };
 
@@ -67,8 +72,8 @@ struct DequantParams {
 hipError_t launch_append(const AppendParams& p, bool bf16, int had_block, int fmt, hipStream_t stream);
 DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len);
 size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int hkv, int group);
-void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, int group,
-                     int32_t** counters, float** part_ml, float** part_o);
+void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, int group, float** part_ml,
+                     float** part_o);
 hipError_t launch_decode(const DecodeParams& p, int fmt, hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);

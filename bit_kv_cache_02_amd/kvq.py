@@ -55,6 +55,9 @@ SIGNATURES = [
     ("kvq_decode_attn", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _I32, ctypes.c_float, _I32,
                                        _I32, _P, _I32, _P, _I32, ctypes.c_float, _P, _I32,
                                        ctypes.c_uint32, _P, ctypes.c_size_t, _P]),
+    ("kvq_decode_step", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _P, _I32, _P, _I32,
+                                       ctypes.c_float, _I32, _I32, _P, _I32, _P, _I32, ctypes.c_float,
+                                       _P, _I32, ctypes.c_uint32, _P, ctypes.c_size_t, _P]),
     ("kvq_dequant_page", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _I32, _P, _P,
                                         ctypes.c_uint32, _P]),
     ("kvq_strerror", ctypes.c_char_p, [ctypes.c_int]),
@@ -159,11 +162,11 @@ def decode_workspace_bytes(cache: Cache, num_q_heads: int, num_seqs: int, max_se
 
 
 def make_workspace(cache: Cache, num_q_heads: int, num_seqs: int, max_seq_len: int, device="cuda"):
-    """Zero-filled workspace for kvq_decode_attn (None when none is needed)."""
+    """Workspace for kvq_decode_attn / kvq_decode_step (None when none is needed)."""
     n = decode_workspace_bytes(cache, num_q_heads, num_seqs, max_seq_len)
     if n == 0:
         return None
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def decode_attn(cache: Cache, q: torch.Tensor, seq_lens: torch.Tensor, block_table: torch.Tensor,
@@ -190,6 +193,37 @@ def decode_attn(cache: Cache, q: torch.Tensor, seq_lens: torch.Tensor, block_tab
                                _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                _stream())
     _check(st, "kvq_decode_attn")
+    return out
+
+
+def decode_step(cache: Cache, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, seq_lens: torch.Tensor,
+                block_table: torch.Tensor, max_seq_len: int, out: Optional[torch.Tensor] = None,
+                q_scale: float = 1.0, sm_scale: Optional[float] = None, out_dtype=torch.float32,
+                rotated: bool = False, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Append k[b], v[b] at position seq_lens[b]-1, then attend [0, seq_lens[b]) (kvq_decode_step)."""
+    _require(k, "k")
+    _require(v, "v")
+    _require(q, "q")
+    _require(seq_lens, "seq_lens", torch.int32)
+    _require(block_table, "block_table", torch.int32)
+    b, hq, dim = q.shape
+    if k.shape != (b, cache.num_kv_heads, dim) or v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError(f"k and v must both be [{b}][{cache.num_kv_heads}][{dim}] of one dtype")
+    if out is None:
+        out = torch.empty((b, hq, dim), dtype=out_dtype, device=q.device)
+    _require(out, "out")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if workspace is None:
+        workspace = make_workspace(cache, hq, b, max_seq_len, q.device)
+    d = cache.desc()
+    st = lib().kvq_decode_step(ctypes.byref(d), _ptr(k), _ptr(v), _DTYPE_CODE[k.dtype], _ptr(q),
+                               _DTYPE_CODE[q.dtype], float(q_scale), hq, b, _ptr(seq_lens),
+                               int(max_seq_len), _ptr(block_table), block_table.shape[1],
+                               float(sm_scale), _ptr(out), _DTYPE_CODE[out.dtype],
+                               OUT_ROTATED if rotated else 0, _ptr(workspace),
+                               0 if workspace is None else workspace.numel(), _stream())
+    _check(st, "kvq_decode_step")
     return out
 
 

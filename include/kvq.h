@@ -113,11 +113,11 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t kv_
                int32_t max_new_tokens, void* stream);
 
 /*
- * Bytes of workspace kvq_decode_attn needs for these sizes (same arguments as there).
- * The workspace holds split partials and one counter per (sequence, kv head).  It must be
- * zero-filled once before its first use; every call leaves the counters at zero again.
- * Returns 0 when no workspace is needed (then `workspace` may be NULL), or (size_t)-1 on
- * invalid arguments.
+ * Bytes of workspace kvq_decode_attn and kvq_decode_step need for these sizes (same
+ * arguments as there).  The workspace holds the partial results of (sequence, kv head) pairs
+ * split over several workgroups; it needs no initialisation and its contents between calls
+ * are meaningless.  Returns 0 when no workspace is needed (then `workspace` may be NULL), or
+ * (size_t)-1 on invalid arguments.
  */
 size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_q_heads,
                                   int32_t num_seqs, int32_t max_seq_len);
@@ -138,15 +138,40 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_q_heads,
  *   out          device [num_seqs][num_q_heads][128], dtype out_dtype (F32, F16, BF16):
  *                o = R_b * sum_t softmax_t(sm_scale * q'.k^'_t) v^'_t, or the rotated-basis
  *                result with KVQ_OUT_ROTATED.
- *   workspace    device, >= kvq_decode_workspace_bytes(...) bytes, zero-filled before first
- *                use; do not share one workspace between streams.
- * Decode does not append: a decode step is kvq_append then kvq_decode_attn on one stream.
+ *   workspace    device, >= kvq_decode_workspace_bytes(...) bytes, 256-byte aligned; calls
+ *                that overlap in time (other streams) need workspaces of their own.
+ * Decode does not append: a decode step is kvq_append then kvq_decode_attn on one stream, or
+ * kvq_decode_step.
  */
 int kvq_decode_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, float q_scale,
                     int32_t num_q_heads, int32_t num_seqs, const int32_t* seq_lens,
                     int32_t max_seq_len, const int32_t* block_table, int32_t max_pages,
                     float sm_scale, void* out, int32_t out_dtype, uint32_t flags,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_decode_step -- one decode step in one launch: append then attend.
+ * (SAW-INT4 summary, "Summary": the fused rotation-quantization write into the paged layout;
+ * both halves of the method in a single pass over the cache.)
+ *
+ * Same result as kvq_append(cache, k, v, kv_dtype, num_seqs, num_seqs, cu_new = 0..num_seqs,
+ * start_pos = seq_lens - 1, block_table, max_pages, 1) followed by kvq_decode_attn(...) with
+ * the remaining arguments, up to the rounding of the rotation (a butterfly here, a matrix
+ * product there; both fp32, so an appended code may differ where its pre-rounding value lies
+ * within a few 1e-6 of a rounding boundary).
+ *   k, v         device [num_seqs][num_kv_heads][128], dtype kv_dtype (KVQ_F16 or KVQ_BF16):
+ *                the new token of every sequence, written at position seq_lens[b] - 1
+ *                (page block_table[b*max_pages + (seq_lens[b]-1)/16], slot (seq_lens[b]-1)%16).
+ *   seq_lens     device int32[num_seqs], >= 1: tokens attended, including the new one.
+ * All other arguments and the workspace are those of kvq_decode_attn.  The new token's
+ * bytes are the only pool bytes written.
+ */
+int kvq_decode_step(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype,
+                    const void* q, int32_t q_dtype, float q_scale, int32_t num_q_heads,
+                    int32_t num_seqs, const int32_t* seq_lens, int32_t max_seq_len,
+                    const int32_t* block_table, int32_t max_pages, float sm_scale, void* out,
+                    int32_t out_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /*
  * kvq_dequant_page -- dequantize whole pages (all 16 slots, all kv heads) to fp32.

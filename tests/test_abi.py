@@ -120,6 +120,34 @@ def test_decode_rejects_bad_args(kw, status):
     assert _decode(_desc(), **kw) == status
 
 
+def _step(desc, **kw):
+    args = dict(k=FAKE, v=FAKE, kvdt=kvq.BF16, q=FAKE, qdt=kvq.BF16, qs=1.0, hq=8, B=2, sl=FAKE, msl=100,
+                bt=FAKE, mp=8, sm=0.1, out=FAKE, odt=kvq.F32, flags=0, ws=FAKE, wsb=1 << 30)
+    args.update(kw)
+    return kvq.lib().kvq_decode_step(ctypes.byref(desc), args["k"], args["v"], args["kvdt"], args["q"],
+                                     args["qdt"], args["qs"], args["hq"], args["B"], args["sl"], args["msl"],
+                                     args["bt"], args["mp"], args["sm"], args["out"], args["odt"],
+                                     args["flags"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(v=None), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(kvdt=kvq.F32), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(kvdt=kvq.FP8_E4M3), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(hq=3), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(msl=129), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(q=None), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(odt=kvq.FP8_E4M3), kvq.KVQ_ERR_UNSUPPORTED),
+])
+def test_decode_step_rejects_bad_args(kw, status):
+    assert _step(_desc(), **kw) == status
+
+
+def test_decode_step_empty_batch_is_a_no_op():
+    assert _step(_desc(), B=0) == kvq.KVQ_OK
+
+
 def test_decode_workspace_sizing_and_check():
     # a few long sequences are split over several workgroups and need a workspace
     d = _desc(num_kv_heads=8)

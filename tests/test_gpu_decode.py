@@ -153,7 +153,7 @@ def test_decode_gqa_equal_queries_give_equal_rows():
 
 
 def test_decode_workspace_reuse():
-    # the arrival counters are left at zero: repeated calls on one workspace agree
+    # split partials live in the workspace: repeated calls on one (uninitialised) workspace agree
     rng = np.random.default_rng(27)
     lens = [3000, 2000]
     pool, table = oracle_cache(rng, lens, 2, 64)
@@ -166,8 +166,6 @@ def test_decode_workspace_reuse():
     outs = [kvq.decode_attn(cache, q, sl, bt, 3000, workspace=ws).cpu() for _ in range(4)]
     for o in outs[1:]:
         assert torch.equal(outs[0], o)
-    counters = ws[:2 * 2 * 4].cpu()
-    assert not counters.any()
 
 
 @pytest.mark.parametrize("hb", [64, 128])
