@@ -4,14 +4,15 @@
 A step is one decode step of one Llama-3-8B-shaped attention layer: append the new
 token of each of 32 sequences into the paged INT4 cache (block-diagonal Hadamard
 b = 128, token-wise INT4), then decode attention of 32 query heads over 8 kv heads
-and 4096 cached tokens per sequence.  Steps cycle over 8 independent layer caches
+and 4096 tokens per sequence (the new one included).  The step runs as one launch of
+kvq_decode_step, replayed from a HIP graph; steps cycle over 8 independent layer caches
 (8 x 143 MB) so that the 256 MB Infinity Cache cannot serve the pages.
 
-Printed: one JSON line with the whole-step algorithmic throughput (GB/s), the
-decode and append kernel times from HIP events on the launch stream, the decode
-kernel's roofline fraction against 8 TB/s, the measured copy bandwidth, the
-prefill-append throughput (64 x 2048 tokens, with and without rotation) and the
-CPU oracle's rate on a bounded sample.
+Printed: one JSON line with the whole-step algorithmic throughput (GB/s), the step
+kernel's average launch duration from HIP events on its stream and its roofline
+fraction against 8 TB/s, the same step as two launches (kvq_append + kvq_decode_attn),
+the measured copy bandwidth, the prefill-append throughput (64 x 2048 tokens, with and
+without rotation) and the CPU oracle's rate on a bounded sample.
 """
 import argparse
 import hashlib
@@ -31,7 +32,7 @@ from bit_kv_cache_02_amd import kvq, workloads as wl  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 PAGE_HEAD = 2176
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_llama_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "bit_kv_cache_02_amd", "csrc", "kvq_decode.hip")
 
 
@@ -81,34 +82,88 @@ def build_layers(w, n_layers, dev):
     return caches, step, lens, table
 
 
-def time_decode_steps(w, caches, step, lens, steps, warmup):
+def time_two_call_steps(w, caches, step, lens, steps, warmup):
+    """The step as two launches (kvq_append, kvq_decode_attn), eager; per-launch event times."""
+    dev = step["q"].device
+    max_len = int(lens.max())
+    ws = kvq.make_workspace(caches[0], w.num_q_heads, w.batch, max_len, dev)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps + warmup)]
+    for i in range(steps + warmup):
+        c = caches[i % len(caches)]
+        ev[i][0].record()
+        kvq.append(c, step["k"], step["v"], step["cu"], step["start"], step["bt"], 1)
+        ev[i][1].record()
+        kvq.decode_attn(c, step["q"], step["lens"], step["bt"], max_len, out=out, workspace=ws)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    app = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup, warmup + steps)]) * 1e3
+    dec = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(warmup, warmup + steps)]) * 1e3
+    # decode launches back to back: average launch duration over the region
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        kvq.decode_attn(caches[i % len(caches)], step["q"], step["lens"], step["bt"], max_len, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    return app, dec, e0.elapsed_time(e1) * 1e3 / steps
+
+
+def step_graphs(w, caches, step, lens):
+    """HIP graphs of kvq_decode_step launches: one holding a step on every layer cache in turn,
+    and one per layer cache (for a step count that is not a multiple of the layer count)."""
     dev = step["q"].device
     max_len = int(lens.max())
     ws = kvq.make_workspace(caches[0], w.num_q_heads, w.batch, max_len, dev)
     out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
 
-    def one(i):
-        c = caches[i % len(caches)]
-        kvq.append(c, step["k"], step["v"], step["cu"], step["start"], step["bt"], 1)
-        ev[i][1].record()
-        kvq.decode_attn(c, step["q"], step["lens"], step["bt"], max_len, out=out, workspace=ws)
+    def one(c):
+        kvq.decode_step(c, step["k"], step["v"], step["q"], step["lens"], step["bt"], max_len, out=out,
+                        workspace=ws)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps + warmup)]
-    for i in range(warmup):
-        ev[i][0].record()
-        one(i)
-        ev[i][2].record()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in caches:
+            one(c)
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    every = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(every):
+        for c in caches:
+            one(c)
+    single = []
+    for c in caches:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one(c)
+        single.append(g)
+    torch.cuda.synchronize()
+    return every, single
+
+
+def time_graph_steps(every, single, steps, warmup):
+    """Exactly `steps` steps: steps // L replays of the all-layers graph, then the remaining
+    steps from the per-layer graphs.  Returns the wall time and the launch stream's event time
+    per step over the same region."""
+    n_layers = len(single)
+
+    def run(n):
+        for _ in range(n // n_layers):
+            every.replay()
+        for i in range(n % n_layers):
+            single[i].replay()
+
+    run(warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(warmup, warmup + steps):
-        ev[i][0].record()
-        one(i)
-        ev[i][2].record()
+    e0.record()
+    run(steps)
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    app = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup, warmup + steps)]) * 1e3
-    dec = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(warmup, warmup + steps)]) * 1e3
-    return wall, app, dec
+    return wall, e0.elapsed_time(e1) * 1e3 / steps
 
 
 def time_prefill_append(dev, repeats=10):
@@ -215,7 +270,7 @@ def cpu_baseline(w, budget_s=12.0, n_seqs=4):
 
 
 def traffic_entry(algo_bytes):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE,
+    """HBM bytes per step launch from committed rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE,
     each scaled by what the counter reads for the bench's 1 GiB copy), if the decode kernel source
     has not changed since."""
     try:
@@ -231,17 +286,18 @@ def traffic_entry(algo_bytes):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=800)
+    ap.add_argument("--warmup", type=int, default=800)
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--profile-run", action="store_true",
-                    help="short run for rocprofv3: few decode steps, three prefill appends, no CPU leg")
+                    help="short run for rocprofv3: 24 fused steps, the copy probe, three prefill "
+                         "appends, no two-launch step and no CPU leg")
     args = ap.parse_args()
     if args.profile_run:
-        args.steps, args.warmup, args.no_cpu = 20, 5, True
+        args.steps, args.warmup, args.no_cpu = 24, 8, True
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -254,15 +310,31 @@ def main():
     w = wl.WORKLOADS["llama"]
     log("[bench] building 8 layer caches (llama shape)")
     caches, step, lens, _ = build_layers(w, args.layers, dev)
-    log("[bench] timing decode steps")
-    wall, app_us, dec_us = time_decode_steps(w, caches, step, lens, args.steps, args.warmup)
-    ms_per_step = wall * 1e3 / args.steps
     dbytes = decode_step_bytes(w, lens)
     abytes = append_bytes(w.batch, w.num_kv_heads)
     step_bytes = dbytes + abytes
+    res = {}
+    # a few milliseconds of the step first, so that clocks have settled before anything is timed
+    for i in range(8 * max(1, 256 // args.layers)):
+        kvq.decode_attn(caches[i % len(caches)], step["q"], step["lens"], step["bt"], int(lens.max()))
+    torch.cuda.synchronize()
+    if not args.profile_run:
+        log("[bench] two-launch step (kvq_append + kvq_decode_attn)")
+        app_us, dec_us, dec_avg_us = time_two_call_steps(w, caches, step, lens, min(args.steps, 200), 20)
+        res["two_launch_step"] = {
+            "append_us": round(float(app_us.mean()), 3),
+            "decode_us": round(float(dec_us.mean()), 3),
+            "decode_back_to_back_avg_us": round(dec_avg_us, 3),
+            "decode_GBps": round(dbytes / dec_avg_us / 1e3, 1),
+            "decode_frac_of_hbm_peak": round(dbytes / dec_avg_us / 1e3 / HBM_PEAK_GBPS, 4),
+        }
+    log("[bench] capturing the fused step into HIP graphs")
+    every, single = step_graphs(w, caches, step, lens)
+    log("[bench] timing fused steps")
+    wall, step_us = time_graph_steps(every, single, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_mean = float(dec_us.mean())
-    achieved = dbytes / dec_mean / 1e3
+    achieved = step_bytes / step_us / 1e3
     from bit_kv_cache_02_amd.kvq import decode_workspace_bytes
     res = {
         "metric": "INT4-KV append GB/s + paged INT4 decode-attn us/step, % of HBM peak",
@@ -280,32 +352,33 @@ def main():
         "config": {
             "workload": "Llama-3-8B layer decode step: batch 32 x context 4096, 32 q / 8 kv heads, "
                         "head_dim 128, page 16, bf16 K/V/q, token-wise INT4 (fp16 scale+zero), Hadamard "
-                        "block 128; append 1 token per sequence + decode attention; 8 layer caches cycled",
+                        "block 128; append 1 token per sequence + decode attention in one launch "
+                        "(kvq_decode_step), one HIP graph replay per 8 steps; 8 layer caches cycled",
             "batch": w.batch, "context": int(lens[0]), "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads, "had_block": w.had_block, "layers_cycled": args.layers,
             "out_dtype": "bf16",
         },
-        "decode_us": round(dec_mean, 3),
-        "decode_us_median": round(float(np.median(dec_us)), 3),
-        "decode_GBps": round(achieved, 1),
-        "append_step_us": round(float(app_us.mean()), 3),
-        "append_step_GBps": round(abytes / float(app_us.mean()) / 1e3, 2),
-        "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
-        "algorithmic_bytes": {"decode": dbytes, "append_step": abytes},
+        "step_us": round(step_us, 3),
+        "step_GBps": round(achieved, 1),
+        "step_frac_of_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(w.batch / (ms_per_step * 1e-3), 1),
+        "algorithmic_bytes": {"decode": dbytes, "append": abytes, "step": step_bytes},
         "decode_workspace_bytes": decode_workspace_bytes(caches[0], w.num_q_heads, w.batch, int(lens.max())),
         "roofline": {
             "bound": "hbm",
-            "kernel": "kvq::decode_kernel (kvq_decode_attn, INT4)",
+            "kernel": "kvq::decode_kernel<0, 8, 3> (kvq_decode_step: append + decode attention, INT4)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic_entry(dbytes),
+            "traffic": traffic_entry(step_bytes),
         },
+        **res,
     }
+    del every, single
     log("[bench] HBM copy probe")
     res["hbm_copy_GBps"] = round(hbm_copy_probe(dev), 1)
-    res["decode_frac_of_copy_bw"] = round(achieved / res["hbm_copy_GBps"], 4)
+    res["step_frac_of_copy_bw"] = round(achieved / res["hbm_copy_GBps"], 4)
     del caches
     torch.cuda.empty_cache()
     if not args.no_prefill:

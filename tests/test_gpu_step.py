@@ -166,3 +166,55 @@ def test_step_repeated_calls_grow_the_cache():
         ref = oracle.decode_attention(gpu_pool, q_t.float().numpy(), lens, table, hb)
         assert parity.attn_row_error(out.cpu().numpy(), ref).max() <= parity.ATTN_TOL
         ref_pool = gpu_pool.copy()  # the next step builds on the GPU's bytes
+
+
+def test_step_graph_replays_match_eager():
+    # the step captured in a HIP graph and replayed several times, with eager work and
+    # synchronisations in between: every replay gives the eager result bit for bit
+    rng = np.random.default_rng(8)
+    hkv, group, hb = 2, 4, 128
+    lens = np.array([700, 33, 5000], np.int64)
+    n_pages = [-(-int(n) // 16) for n in lens]
+    total = sum(n_pages)
+    table = np.zeros((3, max(n_pages)), np.int32)
+    ids = rng.permutation(total)
+    off = 0
+    for i, n in enumerate(n_pages):
+        table[i, :n] = ids[off:off + n]
+        off += n
+    k, v = _vectors(rng, int(lens.sum()), hkv, "bf16")
+    pool = np.full((total, hkv, 2176), SENT, np.uint8)
+    cu = np.concatenate([[0], np.cumsum(lens - 1)])
+    sel = np.concatenate([np.arange(s, s + n - 1) for s, n in zip(np.concatenate([[0], np.cumsum(lens)])[:-1], lens)])
+    oracle.append(pool, k[sel], v[sel], cu, np.zeros(3, np.int64), table, hb)
+    last = np.cumsum(lens) - 1
+    dev = torch.device("cuda")
+    kn = torch.from_numpy(k[last]).bfloat16().to(dev)
+    vn = torch.from_numpy(v[last]).bfloat16().to(dev)
+    q = torch.from_numpy(rng.standard_normal((3, hkv * group, 128)).astype(np.float32)).bfloat16().to(dev)
+    sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    bt = torch.from_numpy(table).to(dev)
+    cache = kvq.Cache(total, hkv, hb, pool=torch.from_numpy(pool).to(dev))
+    ws = kvq.make_workspace(cache, hkv * group, 3, int(lens.max()), dev)
+    out = torch.empty((3, hkv * group, 128), dtype=torch.float32, device=dev)
+    kvq.decode_step(cache, kn, vn, q, sl, bt, int(lens.max()), out=out, workspace=ws)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    eager_pool = cache.pool.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kvq.decode_step(cache, kn, vn, q, sl, bt, int(lens.max()), out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kvq.decode_step(cache, kn, vn, q, sl, bt, int(lens.max()), out=out, workspace=ws)
+    for r in range(4):
+        out.zero_()
+        scratch = torch.randn(1 << 20, device=dev).sum()  # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager step"
+        assert torch.equal(cache.pool, eager_pool), f"replay {r} wrote different bytes"
+        del scratch
