@@ -34,6 +34,8 @@ HBM_PEAK_GBPS = 8000.0
 PAGE_HEAD = 2176
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_llama_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "bit_kv_cache_02_amd", "csrc", "kvq_decode.hip")
+APPEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_prefill_traffic.json")
+APPEND_SRC = os.path.join(ROOT, "bit_kv_cache_02_amd", "csrc", "kvq_append.hip")
 
 
 def log(*a):
@@ -269,14 +271,14 @@ def cpu_baseline(w, budget_s=12.0, n_seqs=4):
     }
 
 
-def traffic_entry(algo_bytes):
-    """HBM bytes per step launch from committed rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE,
-    each scaled by what the counter reads for the bench's 1 GiB copy), if the decode kernel source
-    has not changed since."""
+def traffic_entry(algo_bytes, path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_source_sha256"):
+    """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE, each
+    scaled by what the counter reads for the bench's 1 GiB copy), if the kernel source has not
+    changed since they were taken."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
-        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-        if rec.get("decode_source_sha256") != src:
+        rec = json.load(open(path))
+        src = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
+        if rec.get(key) != src:
             return None
         return int(rec["hbm_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
@@ -293,11 +295,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--profile-run", action="store_true",
-                    help="short run for rocprofv3: 24 fused steps, the copy probe, three prefill "
-                         "appends, no two-launch step and no CPU leg")
+                    help="run for rocprofv3: the fused steps as timed by default, the copy probe, "
+                         "three prefill appends; no two-launch step and no CPU leg")
     args = ap.parse_args()
     if args.profile_run:
-        args.steps, args.warmup, args.no_cpu = 24, 8, True
+        args.no_cpu = True
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -315,8 +317,9 @@ def main():
     step_bytes = dbytes + abytes
     res = {}
     # a few milliseconds of the step first, so that clocks have settled before anything is timed
-    for i in range(8 * max(1, 256 // args.layers)):
-        kvq.decode_attn(caches[i % len(caches)], step["q"], step["lens"], step["bt"], int(lens.max()))
+    for i in range(256):
+        kvq.decode_step(caches[i % len(caches)], step["k"], step["v"], step["q"], step["lens"], step["bt"],
+                        int(lens.max()))
     torch.cuda.synchronize()
     if not args.profile_run:
         log("[bench] two-launch step (kvq_append + kvq_decode_attn)")
@@ -384,6 +387,8 @@ def main():
     if not args.no_prefill:
         log("[bench] prefill append")
         res["prefill_append"] = time_prefill_append(dev, repeats=3 if args.profile_run else 10)
+        res["prefill_append"]["traffic"] = traffic_entry(res["prefill_append"]["algorithmic_bytes"],
+                                                         APPEND_TRAFFIC_FILE, APPEND_SRC, "append_source_sha256")
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)
