@@ -271,13 +271,23 @@ def cpu_baseline(w, budget_s=12.0, n_seqs=4):
     }
 
 
+def code_sha256(path):
+    """sha256 of a source file's code: comment-only edits leave it unchanged."""
+    lines = []
+    for line in open(path, encoding="utf-8"):
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def traffic_entry(algo_bytes, path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_source_sha256"):
     """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE, each
-    scaled by what the counter reads for the bench's 1 GiB copy), if the kernel source has not
+    scaled by what the counter reads for the bench's 1 GiB copy), if the kernel's code has not
     changed since they were taken."""
     try:
         rec = json.load(open(path))
-        src = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
+        src = code_sha256(src_path)
         if rec.get(key) != src:
             return None
         return int(rec["hbm_bytes_per_launch"])

@@ -9,11 +9,17 @@
 //            a 16-bit fixed-point number split into two int8 limbs (rows 2g, 2g+1 of the A tile),
 //            so the contraction is exact integer arithmetic;
 //   softmax  online, in the log2 domain; DPP row reductions over the 16 tokens;
-//   p.V      O'[g][ch] += sum_t (p_t sv_t) c_t[ch] + sum_t p_t zv_t
-//            sum_t (p_t sv_t) c_t runs on v_mfma_f32_16x16x16_f16: the codes enter as the exact
-//            fp16 subnormals c * 2^-24 (a mask of the nibbles, no conversion), p_t*sv_t enters
-//            split into an fp16 high part and an fp16 low part (rows 2g and 2g+1), which keeps
-//            ~22 bits of it.
+//   p.V      O'[g][ch] += sum_t (p_t sv_t) (c_t[ch] - 8) + sum_t p_t (zv_t + 8 sv_t)
+//            the first sum runs on v_mfma_f32_16x16x16_f16: the codes enter as the exact fp16
+//            subnormals c * 2^-24 (a mask of the nibbles, no conversion), centred by one exact
+//            packed fp16 subtraction so that the fp32 accumulation sees terms of both signs;
+//            p_t*sv_t enters split into an fp16 high part and an fp16 low part (rows 2g and
+//            2g+1), which keeps ~22 bits of it.
+// MXFP4 pages convert to fp16 tiles with the group scale applied (v_cvt_scalef32_pk_f16_fp4) and
+// run both contractions on the f16 matrix cores.
+// kvq_decode_step runs the same kernel with the append folded in: the workgroup that streams a
+// sequence's last page also rotates and quantizes that step's new K/V token (a wave butterfly),
+// writes it into the page, and substitutes its bytes into the page registers it streams.
 // The page layout puts V codes of four consecutive tokens in one 32-bit word per row byte, which
 // is the B-operand shape of the p.V MFMA, so one 16-byte load per lane feeds it directly.
 // Each wave streams its pages through a register prefetch pipeline (the query loads and the
