@@ -711,23 +711,29 @@ DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len) {
   DecodePlan plan;
   const int max_pg = (max_seq_len + kPage - 1) / kPage;
   const int64_t units = (int64_t)num_seqs * hkv;
-  // Wide batches (a (sequence, kv head) per CU or more): 8-wave workgroups, one per unit when it
-  // fits (no split, no combine).  Narrow batches of long sequences: 4-wave workgroups over 128-page
-  // splits, so that the CUs fill up.  Measured on the decode workloads of the benchmark.
+  // One (sequence, kv head) per CU (at most 256 units of at most 512 pages): 8-wave workgroups,
+  // no split.  More units or longer sequences than that: 4-wave workgroups over 256-page splits,
+  // three of which share a CU, so that one workgroup's start and end latency overlap another's
+  // streaming.  Narrow batches of long sequences: 4-wave workgroups over 128-page splits (halved
+  // until the grid has 512 workgroups).  Measured on the decode workloads of the benchmark.
   int W, P;
-  if (units >= 256) {
+  if (units >= 256 && units * ((max_pg + 511) / 512) <= 256) {
     W = 8;
     P = 512;
+  } else if (units >= 256) {
+    W = 4;
+    P = 256;
   } else {
     W = 4;
     P = 128;
     while (P > 16 && units * ((max_pg + P - 1) / P) < 512) P /= 2;
   }
   int D = 3;
-  // tuning overrides, read once per process
-  static const int env_w = getenv("KVQ_DECODE_WAVES") ? atoi(getenv("KVQ_DECODE_WAVES")) : 0;
-  static const int env_p = getenv("KVQ_DECODE_PAGES_PER_SPLIT") ? atoi(getenv("KVQ_DECODE_PAGES_PER_SPLIT")) : 0;
-  static const int env_d = getenv("KVQ_DECODE_DEPTH") ? atoi(getenv("KVQ_DECODE_DEPTH")) : 0;
+  // tuning overrides (read on every call, so a sweep can change them between calls)
+  const char* ew = getenv("KVQ_DECODE_WAVES");
+  const char* ep = getenv("KVQ_DECODE_PAGES_PER_SPLIT");
+  const char* ed = getenv("KVQ_DECODE_DEPTH");
+  const int env_w = ew ? atoi(ew) : 0, env_p = ep ? atoi(ep) : 0, env_d = ed ? atoi(ed) : 0;
   if (env_w) W = env_w;
   if (env_p) P = env_p;
   if (env_d) D = env_d;
