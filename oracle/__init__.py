@@ -38,9 +38,10 @@ from .mxfp4 import quantize_mxfp4, dequantize_mxfp4, E2M1_GRID
 from .layout import (PAGE_SIZE, HEAD_DIM, PAGE_HEAD_BYTES, K_CODES_OFF, V_CODES_OFF,
                      K_PARAMS_OFF, V_PARAMS_OFF, nibble_position, pack_row, unpack_row)
 from .paged import (append, dequant_pages, read_token, FMT_INT4, FMT_MXFP4)
-from .attention import decode_attention, decode_attention_one
+from .attention import decode_attention, decode_attention_one, prefill_attention
 
 __all__ = [
+    "prefill_attention",
     "sylvester", "rotation", "quantize_int4", "dequantize_int4", "quantize_mxfp4",
     "dequantize_mxfp4", "E2M1_GRID", "PAGE_SIZE", "HEAD_DIM", "PAGE_HEAD_BYTES",
     "K_CODES_OFF", "V_CODES_OFF", "K_PARAMS_OFF", "V_PARAMS_OFF", "nibble_position",

@@ -20,6 +20,15 @@ For each sequence b and query head h (kv head g = h // (Hq / Hkv)):
 
 k^', v^' are the dequantized cached vectors (rotated basis), read through the
 block table: position t lives on page block_table[b][t // 16], slot t % 16.
+
+Chunked prefill over the same cache (``prefill_attention``): the UltraQuant
+article (section on what it showed) credits its gains to prefixes that stay
+resident in the 4-bit cache, so that a new turn does not re-run the prefill of
+the prefix; the new turn's tokens then attend over the resident prefix and,
+causally, over each other.  Reading: the chunk of sequence b is its last
+n_b = cu_q[b+1] - cu_q[b] positions, already appended to the cache; query token
+j of the chunk sits at position p_j = seq_lens[b] - n_b + j and attends
+positions 0..p_j -- exactly the decode formula above with seq_len p_j + 1.
 """
 
 import numpy as np
@@ -75,4 +84,27 @@ def decode_attention(pool, q, seq_lens, block_table, had_block: int, fmt: int = 
         k_rot, v_rot = gather_sequence(pool, block_table[b], int(seq_lens[b]), had_block, fmt)
         out[b] = decode_attention_one(q[b], k_rot, v_rot, had_block, q_scale, sm_scale,
                                       out_rotated)
+    return out
+
+
+def prefill_attention(pool, q, cu_q, seq_lens, block_table, had_block: int, fmt: int = FMT_INT4,
+                      q_scale: float = 1.0, sm_scale: float = None, out_rotated: bool = False,
+                      seqs=None):
+    """o[T][Hq][128] (fp64) for the chunk tokens of the sequences in ``seqs`` (default: all;
+    other rows NaN).  Token i of sequence b (cu_q[b] <= i < cu_q[b+1]) attends positions
+    0 .. seq_lens[b] - (cu_q[b+1] - cu_q[b]) + (i - cu_q[b])."""
+    q = np.asarray(q, dtype=np.float64)
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    out = np.full(q.shape, np.nan)
+    for b in (range(len(seq_lens)) if seqs is None else seqs):
+        length = int(seq_lens[b])
+        n = int(cu_q[b + 1] - cu_q[b])
+        if n == 0:
+            continue
+        k_rot, v_rot = gather_sequence(pool, block_table[b], length, had_block, fmt)
+        for j in range(n):
+            pos = length - n + j
+            i = int(cu_q[b]) + j
+            out[i] = decode_attention_one(q[i], k_rot[:, :pos + 1], v_rot[:, :pos + 1], had_block, q_scale,
+                                          sm_scale, out_rotated)
     return out

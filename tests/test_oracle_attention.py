@@ -116,3 +116,54 @@ def test_attention_on_lossless_rotated_cache_equals_exact_attention():
     p = np.exp(s - s.max(0))
     p /= p.sum(0)
     assert np.allclose(o64[0], (p.T @ xv), atol=1e-12)
+
+
+@pytest.mark.parametrize("hb,fmt", [(64, FMT_INT4), (128, FMT_MXFP4)])
+def test_prefill_matches_torch_sdpa_causal_fp64(hb, fmt):
+    # Chunked prefill against a library routine: SDPA with an explicit causal mask over the
+    # unrotated dequantized cache; the chunk is the last n positions of each sequence.
+    from oracle import prefill_attention
+    rng = np.random.default_rng(43)
+    lens = [40, 17, 5]
+    chunk = [9, 17, 1]
+    hkv, hq = 2, 4
+    pool, table = _filled_cache(rng, lens, hkv, hb, fmt)
+    cu_q = np.concatenate([[0], np.cumsum(chunk)])
+    q = rng.standard_normal((int(cu_q[-1]), hq, 128))
+    out = prefill_attention(pool, q, cu_q, lens, table, hb, fmt, q_scale=0.5, sm_scale=0.2)
+    r = rotation(hb)
+    for b, (length, n) in enumerate(zip(lens, chunk)):
+        k_rot, v_rot = gather_sequence(pool, table[b], length, hb, fmt)
+        k_un = torch.from_numpy(k_rot @ r.T)
+        v_un = torch.from_numpy(v_rot @ r.T)
+        qq = torch.from_numpy(0.5 * q[cu_q[b]:cu_q[b + 1]]).permute(1, 0, 2)      # [Hq][n][128]
+        qq = qq.reshape(hkv, hq // hkv, n, 128)
+        pos = np.arange(length - n, length)
+        mask = torch.from_numpy(np.arange(length)[None, :] <= pos[:, None])        # [n][L]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq, k_un[:, None].expand(hkv, hq // hkv, length, 128),
+            v_un[:, None].expand(hkv, hq // hkv, length, 128), attn_mask=mask, scale=0.2)
+        ref = ref.reshape(hq, n, 128).permute(1, 0, 2).numpy()
+        assert np.allclose(out[cu_q[b]:cu_q[b + 1]], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_is_causal_and_reduces_to_decode():
+    from oracle import prefill_attention
+    rng = np.random.default_rng(44)
+    hb, hkv, hq = 128, 1, 4
+    lens = [50]
+    pool, table = _filled_cache(rng, lens, hkv, hb, permute=False)
+    n = 10
+    q = rng.standard_normal((n, hq, 128))
+    out = prefill_attention(pool, q, [0, n], lens, table, hb)
+    # the last chunk token sees the whole sequence: the decode result
+    dec = decode_attention(pool, q[-1:], lens, table, hb)
+    assert np.allclose(out[-1], dec[0], rtol=1e-13, atol=1e-13)
+    # overwriting positions after token j's position leaves token j's output unchanged
+    pool2 = pool.copy()
+    rest = np.full((lens[0] - 45, hkv, 128), 3.0)
+    append(pool2, rest, -rest, np.array([0, len(rest)]), np.array([45]), table, hb)
+    out2 = prefill_attention(pool2, q, [0, n], lens, table, hb)
+    p_first_changed = 45 - (lens[0] - n)            # chunk index of position 45
+    assert np.array_equal(out2[:p_first_changed], out[:p_first_changed])
+    assert not np.allclose(out2[p_first_changed:], out[p_first_changed:])
