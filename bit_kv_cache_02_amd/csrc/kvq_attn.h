@@ -1,0 +1,314 @@
+// Device pieces shared by the attention kernels of libkvq (decode and chunked prefill): the
+// page-head load, the per-page INT4 / MXFP4 score + online softmax + p.V step on the matrix
+// cores, and the wave-level Walsh-Hadamard butterfly.  See kvq_decode.hip for the method.
+#pragma once
+
+#include "kvq_device.h"
+
+namespace kvq {
+namespace attn {
+
+
+constexpr int kMaxG = 8;
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ float inv_sqrt_block(int hb) {
+  return hb == 128 ? 0.08838834764831845f : (hb == 64 ? 0.125f : 1.0f);
+}
+
+// Walsh-Hadamard transform of one 128-vector held by a wave, element `lane` in x0 and element
+// `lane + 64` in x1 (unnormalised, blocks of hb channels, natural Sylvester order).  Cross-lane
+// stages use lane shuffles, so no workgroup barrier is needed.
+__device__ __forceinline__ void fwht_wave(float& x0, float& x1, int hb, int lane) {
+  for (int len = 1; len < hb && len < 64; len <<= 1) {
+    const float y0 = __shfl_xor(x0, len), y1 = __shfl_xor(x1, len);
+    const bool upper = (lane & len) != 0;
+    x0 = upper ? y0 - x0 : x0 + y0;
+    x1 = upper ? y1 - x1 : x1 + y1;
+  }
+  if (hb == 128) {
+    const float t = x0;
+    x0 = t + x1;
+    x1 = t - x1;
+  }
+}
+
+// The same transform of R vectors at once (row r in x0[r], x1[r]): each stage issues the
+// shuffles of all rows back to back, so their latencies overlap.
+template <int R>
+__device__ __forceinline__ void fwht_rows(float (&x0)[R], float (&x1)[R], int hb, int lane) {
+  for (int len = 1; len < hb && len < 64; len <<= 1) {
+    float y0[R], y1[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      y0[r] = __shfl_xor(x0[r], len);
+      y1[r] = __shfl_xor(x1[r], len);
+    }
+    const bool upper = (lane & len) != 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      x0[r] = upper ? y0[r] - x0[r] : x0[r] + y0[r];
+      x1[r] = upper ? y1[r] - x1[r] : x1[r] + y1[r];
+    }
+  }
+  if (hb == 128) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float t = x0[r];
+      x0[r] = t + x1[r];
+      x1[r] = t - x1[r];
+    }
+  }
+}
+
+template <int FMT>
+struct PageData {
+  u32x4 k;      // K row bytes 16*jg..16*jg+15 of token n
+  u32x4 v;      // V words: row bytes 4n..4n+3 of tokens 4jg..4jg+3
+  uint32_t kp;  // K params of token n
+  uint32_t vp;  // INT4: V params of token n
+};
+template <>
+struct PageData<1> {
+  u32x4 k;
+  u32x4 v;
+  uint32_t kp;  // UE8M0 bytes of token n (K)
+  u32x4 vp4;    // UE8M0 bytes of tokens 4jg..4jg+3 (V)
+};
+
+// Offset past the end of every buffer range used here: a load with it returns zeros without a
+// memory access.  Loads that are not needed still issue with it, so every path through a kernel
+// issues the same sequence of loads and the compiler's memory-counter waits stay exact (a load
+// skipped on some path makes it wait for everything issued after the value it needs).
+constexpr int kOutOfRange = 0x40000000;
+
+// `base` is wave-uniform: the buffer descriptor lives in scalar registers and the per-lane offsets
+// are loop invariant, so a page costs no vector address arithmetic.  `live` false turns the four
+// loads into out-of-range ones.
+template <int FMT>
+__device__ __forceinline__ PageData<FMT> load_page(const uint8_t* base, bool live, int koff, int voff, int poff,
+                                                   int qoff) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, kPageHeadBytes);
+  if (!live) koff = voff = poff = qoff = kOutOfRange;
+  PageData<FMT> d;
+  // cache policy 2 = nontemporal: the pages are streamed once per step
+  d.k = __builtin_amdgcn_raw_buffer_load_b128(r, koff, 0, 2);
+  d.v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2);
+  d.kp = __builtin_amdgcn_raw_buffer_load_b32(r, poff, kKParamsOff, 2);
+  if constexpr (FMT == 0) d.vp = __builtin_amdgcn_raw_buffer_load_b32(r, poff, kVParamsOff, 2);
+  else d.vp4 = __builtin_amdgcn_raw_buffer_load_b128(r, qoff, kVParamsOff, 2);
+  return d;
+}
+
+// 2^(E-127) for the UE8M0 byte E at bit `shift` of w (E = 0 gives 0: an all-zero or sub-2^-125 group)
+__device__ __forceinline__ float ue8m0_scale(uint32_t w, int shift) {
+  return __uint_as_float(((w >> shift) & 0xFFu) << 23);
+}
+
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+// Two e2m1 codes of byte `sel` of w -> two fp16 values times `scale` (low nibble first).
+__device__ __forceinline__ f16x2 cvt_fp4(uint32_t w, float scale, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3);
+  }
+}
+
+// Per-wave streaming state.
+struct WaveState {
+  float m0, m1, l0, l1, pz0, pz1;
+  f32x4 acc[8];
+};
+
+// valid0 / valid1: tokens of the page that rows x0 / x1 attend (decode: the same count).
+__device__ __forceinline__ void process_page(const PageData<0>& pg, int valid0, int valid1, WaveState& s,
+                                             const i32x4 (&qa)[2],
+                                             float alpha0, float beta0, float alpha1, float beta1,
+                                             bool has0, bool has1, int n, int jg, bool a_row_used,
+                                             _Float16 (*ptile)[kPage]) {
+  const uint32_t M4 = 0x0F0F0F0Fu, M16 = 0x000F000Fu;
+  const bool tv0 = n < valid0, tv1 = n < valid1;
+
+  // q'.c_t on the integer matrix cores
+  const i32x4 kb0 = i32x4{(int)(pg.k[0] & M4), (int)(pg.k[1] & M4), (int)(pg.k[2] & M4), (int)(pg.k[3] & M4)};
+  const i32x4 kb1 = i32x4{(int)((pg.k[0] >> 4) & M4), (int)((pg.k[1] >> 4) & M4), (int)((pg.k[2] >> 4) & M4),
+                          (int)((pg.k[3] >> 4) & M4)};
+  i32x4 sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], kb0, i32x4{0, 0, 0, 0}, 0, 0, 0);
+  sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], kb1, sc, 0, 0, 0);
+
+  const float sk = f16_bits_to_f32(pg.kp & 0xFFFFu), zk = f16_bits_to_f32(pg.kp >> 16);
+  float x0 = fmaf((float)(sc[0] * 256 + sc[1]) * alpha0, sk, zk * beta0);
+  float x1 = fmaf((float)(sc[2] * 256 + sc[3]) * alpha1, sk, zk * beta1);
+  x0 = tv0 ? x0 : -INFINITY;
+  x1 = tv1 ? x1 : -INFINITY;
+
+  const float pm0 = row_max16(x0), pm1 = row_max16(x1);
+  const float sv = f16_bits_to_f32(pg.vp & 0xFFFFu), zv = f16_bits_to_f32(pg.vp >> 16);
+  // The reference max m only moves when a score exceeds it by more than 2^8 (or when p~ = p * sv
+  // could leave the fp16 range): any m gives the same softmax, and p <= 2^8 keeps the fp16 and
+  // fp32 partial sums in range.  exp2 of very negative arguments may flush to zero: harmless here.
+  if (__any(pm0 > s.m0 + 8.0f || pm1 > s.m1 + 8.0f || ((pm0 > s.m0 || pm1 > s.m1) && sv > 128.0f))) {
+    const float mn0 = fmaxf(s.m0, pm0), mn1 = fmaxf(s.m1, pm1);
+    const float f0 = __builtin_amdgcn_exp2f(s.m0 - mn0), f1 = __builtin_amdgcn_exp2f(s.m1 - mn1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s.acc[i][0] *= f0;
+      s.acc[i][1] *= f0;
+      s.acc[i][2] *= f1;
+      s.acc[i][3] *= f1;
+    }
+    s.l0 *= f0;
+    s.l1 *= f1;
+    s.pz0 *= f0;
+    s.pz1 *= f1;
+    s.m0 = mn0;
+    s.m1 = mn1;
+  }
+  const float p0 = __builtin_amdgcn_exp2f(x0 - s.m0), p1 = __builtin_amdgcn_exp2f(x1 - s.m1);
+  s.l0 += p0;
+  s.l1 += p1;
+  const float zc = fmaf(8.0f, sv, zv);  // zero point of the centred codes (exact: fp16 inputs)
+  s.pz0 = tv0 ? fmaf(p0, zc, s.pz0) : s.pz0;
+  s.pz1 = tv1 ? fmaf(p1, zc, s.pz1) : s.pz1;
+
+  // p~ = p * sv as fp16 high + low parts, stored at A-tile rows 2g+limb in the k order of the
+  // V words (tokens 0, 2, 1, 3 of each quad: bits 0 and 1 of the token swapped)
+  const float pt0 = tv0 ? p0 * sv : 0.0f, pt1 = tv1 ? p1 * sv : 0.0f;
+  const _Float16 h0 = (_Float16)pt0, h1 = (_Float16)pt1;
+  const _Float16 r0 = (_Float16)(pt0 - (float)h0), r1 = (_Float16)(pt1 - (float)h1);
+  const int pos = (n & ~3) | ((n & 1) << 1) | ((n >> 1) & 1);
+  if (has0) {
+    ptile[4 * jg + 0][pos] = h0;
+    ptile[4 * jg + 1][pos] = r0;
+  }
+  if (has1) {
+    ptile[4 * jg + 2][pos] = h1;
+    ptile[4 * jg + 3][pos] = r1;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const f16x4 pa = a_row_used ? *(const f16x4*)&ptile[n][4 * jg] : f16x4{0, 0, 0, 0};
+  __builtin_amdgcn_wave_barrier();
+
+  // V codes as fp16 subnormals: word q of the lane holds row byte 4n+q of 4 tokens.  Low nibbles
+  // (channel n+32q) are masked to c*2^-24, high nibbles (channel n+32q+16) are masked in place to
+  // 16c*2^-24 (their accumulators carry that factor 16 until the end).  One exact packed fp16
+  // subtraction centres the codes, c -> c - 8: all products p~*c would otherwise share one sign,
+  // and the MFMA accumulation error would not average out (the centre 8*sv moves into the zero
+  // point, zv + 8*sv).
+  typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+  const h2 c8lo = __builtin_bit_cast(h2, 0x00080008u), c8hi = __builtin_bit_cast(h2, 0x00800080u);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t Y = pg.v[q], Y8 = Y >> 8;
+    const h2 l0 = __builtin_bit_cast(h2, Y & M16) - c8lo, l1 = __builtin_bit_cast(h2, Y8 & M16) - c8lo;
+    const h2 u0 = __builtin_bit_cast(h2, Y & (M16 << 4)) - c8hi;
+    const h2 u1 = __builtin_bit_cast(h2, Y8 & (M16 << 4)) - c8hi;
+    const f16x4 blo = f16x4{l0[0], l0[1], l1[0], l1[1]};  // tokens 0,2 | 1,3
+    const f16x4 bhi = f16x4{u0[0], u0[1], u1[0], u1[1]};
+    s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, blo, s.acc[2 * q], 0, 0, 0);
+    s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bhi, s.acc[2 * q + 1], 0, 0, 0);
+  }
+}
+
+// MXFP4 page: K and V are dequantized to fp16 tiles with their UE8M0 group scales by the gfx950
+// fp4 conversion (two codes of one byte -> two fp16), then both contractions run on f16 MFMA.
+//   q.K: v_mfma_f32_16x16x32_f16, A = q' as fp16 high/low parts (rows 2g, 2g+1), B = K tile;
+//        dword kk of the lane's K chunk feeds MFMA kk: byte q -> channels (4jg+kk)+32q (+16),
+//        all in channel group q (one scale).
+//   p.V: v_mfma_f32_16x16x16_f16, A = p split high/low, B = V tile: byte r of V word q is token
+//        4jg+r, channels n+32q and n+32q+16 (group q), repacked so one register holds two tokens.
+__device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid0, int valid1, WaveState& s,
+                                                const f16x8 (&qh)[4], float c2, bool has0, bool has1,
+                                                int n, int jg, bool a_row_used, _Float16 (*ptile)[kPage]) {
+  const bool tv0 = n < valid0, tv1 = n < valid1;
+  f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const uint32_t w = pg.k[kk];
+    f16x8 kb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f16x2 h2 = cvt_fp4(w, ue8m0_scale(pg.kp, 8 * q), q);
+      kb[2 * q] = h2[0];
+      kb[2 * q + 1] = h2[1];
+    }
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[kk], kb, sc, 0, 0, 0);
+  }
+  float x0 = (sc[0] + sc[1]) * c2, x1 = (sc[2] + sc[3]) * c2;
+  x0 = tv0 ? x0 : -INFINITY;
+  x1 = tv1 ? x1 : -INFINITY;
+
+  const float pm0 = row_max16(x0), pm1 = row_max16(x1);
+  // p <= 2^8 stays far inside fp16 (no value scale is folded into p here)
+  if (__any(pm0 > s.m0 + 8.0f || pm1 > s.m1 + 8.0f)) {
+    const float mn0 = fmaxf(s.m0, pm0), mn1 = fmaxf(s.m1, pm1);
+    const float f0 = __builtin_amdgcn_exp2f(s.m0 - mn0), f1 = __builtin_amdgcn_exp2f(s.m1 - mn1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s.acc[i][0] *= f0;
+      s.acc[i][1] *= f0;
+      s.acc[i][2] *= f1;
+      s.acc[i][3] *= f1;
+    }
+    s.l0 *= f0;
+    s.l1 *= f1;
+    s.m0 = mn0;
+    s.m1 = mn1;
+  }
+  const float p0 = __builtin_amdgcn_exp2f(x0 - s.m0), p1 = __builtin_amdgcn_exp2f(x1 - s.m1);
+  s.l0 += p0;
+  s.l1 += p1;
+
+  // p as fp16 high + low parts at A-tile rows 2g+limb, natural token order
+  const float pt0 = tv0 ? p0 : 0.0f, pt1 = tv1 ? p1 : 0.0f;
+  const _Float16 h0 = (_Float16)pt0, h1 = (_Float16)pt1;
+  const _Float16 r0 = (_Float16)(pt0 - (float)h0), r1 = (_Float16)(pt1 - (float)h1);
+  if (has0) {
+    ptile[4 * jg + 0][n] = h0;
+    ptile[4 * jg + 1][n] = r0;
+  }
+  if (has1) {
+    ptile[4 * jg + 2][n] = h1;
+    ptile[4 * jg + 3][n] = r1;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const f16x4 pa = a_row_used ? *(const f16x4*)&ptile[n][4 * jg] : f16x4{0, 0, 0, 0};
+  __builtin_amdgcn_wave_barrier();
+
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t Y = pg.v[q];
+    f16x4 blo, bhi;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f16x2 h2 = cvt_fp4(Y, ue8m0_scale(pg.vp4[r], 8 * q), r);
+      blo[r] = h2[0];
+      bhi[r] = h2[1];
+    }
+    s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, blo, s.acc[2 * q], 0, 0, 0);
+    s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bhi, s.acc[2 * q + 1], 0, 0, 0);
+  }
+}
+
+// Rotate one row's normalised o' (element lane in o0, lane + 64 in o1) back and store it at
+// row `row` of a [rows][128] output of dtype `out_dtype`.
+__device__ __forceinline__ void store_row(void* out, int64_t row, int out_dtype, int rotated, int had_block,
+                                          float o0, float o1, int lane) {
+  float scale = 1.0f;
+  if (!rotated) {
+    fwht_wave(o0, o1, had_block, lane);
+    scale = inv_sqrt_block(had_block);
+  }
+  const int64_t base = row * kHeadDim;
+  store_elem(out, base + lane, out_dtype, o0 * scale);
+  store_elem(out, base + lane + 64, out_dtype, o1 * scale);
+}
+
+}  // namespace attn
+}  // namespace kvq

@@ -211,6 +211,59 @@ int kvq_decode_step(const kvq_cache* cache, const void* k, const void* v, int32_
                        workspace_bytes, stream, "kvq_decode_step launch");
 }
 
+int kvq_prefill_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, float q_scale, int32_t num_q_heads,
+                     int32_t num_tokens, int32_t num_seqs, const int32_t* cu_q, const int32_t* seq_lens,
+                     int32_t max_seq_len, int32_t max_q_len, const int32_t* block_table, int32_t max_pages,
+                     float sm_scale, void* out, int32_t out_dtype, uint32_t flags, void* stream) {
+  g_last_error[0] = 0;
+  int st = decode_geometry(cache, num_q_heads, num_seqs, max_seq_len);
+  if (st != KVQ_OK) return st;
+  const int group = num_q_heads / cache->num_kv_heads;
+  if (8 % group) return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d unsupported by prefill (1, 2, 4 or 8)", group);
+  if (!q || !cu_q || !seq_lens || !block_table || !out)
+    return fail(KVQ_ERR_INVALID_ARG, "q, cu_q, seq_lens, block_table and out must not be NULL");
+  if (q_dtype < KVQ_F16 || q_dtype > KVQ_FP8_E4M3) return fail(KVQ_ERR_UNSUPPORTED, "q_dtype %d unknown", q_dtype);
+  if (out_dtype != KVQ_F32 && out_dtype != KVQ_F16 && out_dtype != KVQ_BF16)
+    return fail(KVQ_ERR_UNSUPPORTED, "out_dtype %d unsupported (F32, F16 or BF16)", out_dtype);
+  if (num_tokens < 0 || max_q_len < 0) return fail(KVQ_ERR_INVALID_ARG, "num_tokens and max_q_len must be >= 0");
+  if (max_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (max_pages > (1 << 24)) return fail(KVQ_ERR_UNSUPPORTED, "max_pages %d above 2^24", max_pages);
+  if ((int64_t)max_seq_len > (int64_t)max_pages * KVQ_PAGE_SIZE)
+    return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d exceeds max_pages*16 = %lld", max_seq_len, (long long)max_pages * KVQ_PAGE_SIZE);
+  if (max_seq_len > 131072) return fail(KVQ_ERR_UNSUPPORTED, "prefill attends at most 131072 positions (max_seq_len %d)", max_seq_len);
+  if (max_q_len > max_seq_len) return fail(KVQ_ERR_INVALID_ARG, "max_q_len %d exceeds max_seq_len %d", max_q_len, max_seq_len);
+  if ((int64_t)num_tokens * num_q_heads * KVQ_HEAD_DIM * 4 >= (1ll << 30))
+    return fail(KVQ_ERR_UNSUPPORTED, "num_tokens * num_q_heads %lld too large", (long long)num_tokens * num_q_heads);
+  if (flags & ~KVQ_OUT_ROTATED) return fail(KVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (!std::isfinite(q_scale) || !std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARG, "q_scale and sm_scale must be finite");
+  if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return KVQ_OK;
+  const int tpt = kvq::prefill_tokens_per_tile(group);
+  const int64_t tiles = (max_q_len + tpt - 1) / tpt;
+  if ((int64_t)num_seqs * cache->num_kv_heads * tiles > 0x7FFFFFFF) return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
+  kvq::PrefillParams p;
+  memset(&p, 0, sizeof(p));
+  p.pool = (const uint8_t*)cache->pool;
+  p.q = q;
+  p.cu_q = cu_q;
+  p.seq_lens = seq_lens;
+  p.block_table = block_table;
+  p.out = out;
+  p.hkv = cache->num_kv_heads;
+  p.group = group;
+  p.hq = num_q_heads;
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_tokens;
+  p.max_pages = max_pages;
+  p.had_block = cache->had_block;
+  p.q_dtype = q_dtype;
+  p.out_dtype = out_dtype;
+  p.out_rotated = (flags & KVQ_OUT_ROTATED) ? 1 : 0;
+  p.tiles = (int32_t)tiles;
+  p.q_scale = q_scale;
+  p.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  return hip_status(kvq::launch_prefill(p, cache->format, (hipStream_t)stream), "kvq_prefill_attn launch");
+}
+
 int kvq_dequant_page(const kvq_cache* cache, const int32_t* page_ids, int32_t n, float* out_k,
                      float* out_v, uint32_t flags, void* stream) {
   g_last_error[0] = 0;

@@ -57,6 +57,28 @@ struct DecodeParams {
   DecodePlan plan;
 };
 
+struct PrefillParams {
+  const uint8_t* pool;
+  const void* q;             // [num_tokens][hq][128]
+  const int32_t* cu_q;       // [num_seqs + 1]: chunk tokens of sequence b
+  const int32_t* seq_lens;   // [num_seqs]: positions in the cache, the chunk included
+  const int32_t* block_table;
+  void* out;                 // [num_tokens][hq][128]
+  int32_t hkv;
+  int32_t group;
+  int32_t hq;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t max_pages;
+  int32_t had_block;
+  int32_t q_dtype;
+  int32_t out_dtype;
+  int32_t out_rotated;
+  int32_t tiles;             // query tiles per (sequence, kv head)
+  float q_scale;
+  float sm_scale_log2;
+};
+
 struct DequantParams {
   const uint8_t* pool;
   const int32_t* page_ids;
@@ -76,6 +98,8 @@ void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, in
                      float** part_o);
 hipError_t launch_decode(const DecodeParams& p, int fmt, hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
+int prefill_tokens_per_tile(int group);
+hipError_t launch_prefill(const PrefillParams& p, int fmt, hipStream_t stream);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 }  // namespace kvq

@@ -1,0 +1,260 @@
+// kvq_prefill_attn: chunked-prefill attention over the rotated 4-bit paged cache (UltraQuant
+// article, section on what it showed: prefixes stay resident in the 4-bit cache, so a new turn
+// attends over them instead of re-running their prefill; SAW-INT4 summary, "Summary": attention
+// served straight from the paged 4-bit cache).
+//
+// The chunk of sequence b is its last n_b positions, already appended (kvq_append); chunk token
+// j sits at position p_j = seq_lens[b] - n_b + j and attends positions 0 .. p_j.
+//
+// A workgroup (W waves) owns (sequence, kv head, tile of W * 8/G chunk tokens).  Wave w takes 8
+// rows: its 8/G chunk tokens times the G query heads of the kv head.  Each wave streams every page
+// its rows attend through the per-page step that decode uses (kvq_attn.h): the 8 rows fill the 8
+// row pairs of the matrix-core tiles, and each row pair carries its own causal limit.  The waves
+// of a workgroup read the same pages close together in time, so the caches serve all but the
+// first read of each page; the sequence's block-table entries are staged in LDS once per
+// workgroup.  Query rotation and the final rotation back run for the 8 rows of a wave at once.
+#include "kvq_attn.h"
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+namespace {
+
+using namespace attn;
+
+constexpr int kRows = 8;              // rows (chunk token x query head) per wave
+constexpr int kMaxTablePages = 8192;  // staged block-table entries: positions < 131072
+
+template <int W>
+struct PrefillSmem {
+  union {
+    uint8_t qlimb[W][2][kRows][2][4][16];  // INT4: q' limbs per wave, as in decode
+    _Float16 qh[W][2][kRows][4][4][8];     // MXFP4: q' fp16 high/low parts per wave
+  };
+  float qdelta[W][kRows];
+  float qsum[W][kRows];
+  _Float16 ptile[W][2 * kRows][kPage];
+  float wo[W][kRows][kHeadDim];
+  int32_t table[kMaxTablePages];
+};
+
+}  // namespace
+
+template <int FMT, int W, int D>
+__global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
+  __shared__ PrefillSmem<W> sm;
+  const int tid = thread_id();
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, jg = lane >> 4;
+  const int G = a.group;
+  const int tpw = kRows / G;  // chunk tokens per wave
+  const int units = a.num_seqs * a.hkv;
+  const int tile = block_id_x() / units, unit = block_id_x() % units;  // tile-major order
+  const int kvh = unit % a.hkv, b = unit / a.hkv;
+  const float isb = inv_sqrt_block(a.had_block);
+
+  const int qbeg = a.cu_q[b], nq = a.cu_q[b + 1] - qbeg;
+  const int L = a.seq_lens[b];
+  const int t0 = tile * W * tpw;  // first chunk token of the tile
+  if (t0 >= nq) return;           // uniform over the workgroup
+  const int pos0 = L - nq;        // position of chunk token 0
+  const int n_pages_tile = (pos0 + min(t0 + W * tpw, nq) - 1) / kPage + 1;
+  const int tw0 = t0 + wave * tpw;  // first chunk token of this wave
+  const bool wave_live = tw0 < nq;
+  const int npw = wave_live ? (pos0 + min(tw0 + tpw, nq) - 1) / kPage + 1 : 0;
+
+  // ---- 0. the query words of this wave's rows (row r: token tw0 + r/G, head r%G; rows past the
+  //         chunk load its last token and are ignored), and the tile's block-table entries ----
+  const int esz = __builtin_amdgcn_readfirstlane(a.q_dtype == DT_F32 ? 4 : (a.q_dtype == DT_E4M3 ? 1 : 2));
+  const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(a.q, a.num_tokens * a.hq * kHeadDim * esz);
+  uint32_t qword[kRows][2];
+  int qshift[kRows][2];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int t = min(tw0 + r / G, nq - 1);
+    const int row = (qbeg + t) * a.hq + kvh * G + r % G;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int byte = (row * kHeadDim + lane + 64 * e) * esz;
+      qword[r][e] = __builtin_amdgcn_raw_buffer_load_b32(q_rsrc, byte & ~3, 0, 0);
+      qshift[r][e] = 8 * (byte & 3);
+    }
+  }
+  // one 4-byte load per entry (entries past the tile's pages read as zero), all in flight at once
+  constexpr int kTableLoads = kMaxTablePages / (W * 64);
+  uint32_t tw[kTableLoads];
+  {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(a.block_table + (int64_t)b * a.max_pages, n_pages_tile * 4);
+#pragma unroll
+    for (int k = 0; k < kTableLoads; ++k) tw[k] = __builtin_amdgcn_raw_buffer_load_b32(r, (k * W * 64 + tid) * 4, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < kTableLoads; ++k) sm.table[k * W * 64 + tid] = (int32_t)tw[k];
+
+  // ---- 1. q' = R_b (q_scale q) for the 8 rows, then the decode's operand encodings ----
+  {
+    float v0[kRows], v1[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      v0[r] = raw_to_f32(qword[r][0] >> qshift[r][0], a.q_dtype) * a.q_scale;
+      v1[r] = raw_to_f32(qword[r][1] >> qshift[r][1], a.q_dtype) * a.q_scale;
+    }
+    fwht_rows<kRows>(v0, v1, a.had_block, lane);
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      v0[r] *= isb;
+      v1[r] *= isb;
+      if constexpr (FMT == 1) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int ch = lane + 64 * e;
+          const float v = e ? v1[r] : v0[r];
+          const _Float16 hi = (_Float16)v;
+          const _Float16 lo = (_Float16)(v - (float)hi);
+          sm.qh[wave][0][r][ch & 3][(ch >> 2) & 3][ch >> 4] = hi;
+          sm.qh[wave][1][r][ch & 3][(ch >> 2) & 3][ch >> 4] = lo;
+        }
+      } else {
+        const float amax = wave_max(fmaxf(fabsf(v0[r]), fabsf(v1[r])));
+        const float delta = amax > 0.0f ? amax / 32000.0f : 1.0f;
+        const int q0 = (int)rintf(v0[r] / delta), q1 = (int)rintf(v1[r] / delta);
+        const int qs = wave_sum_i(q0 + q1);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int ch = lane + 64 * e, Q = e ? q1 : q0;
+          const int hi = (Q + 128) >> 8, lo = Q - 256 * hi;
+          const int c16 = ch & 15, c_hi = ch >> 4;
+          uint8_t* dst = &sm.qlimb[wave][0][r][c_hi & 1][c16 >> 2][4 * (c16 & 3) + (c_hi >> 1)];
+          dst[0] = (uint8_t)(hi & 255);
+          dst[sizeof(sm.qlimb[0][0])] = (uint8_t)(lo & 255);
+        }
+        if (lane == 0) {
+          sm.qdelta[wave][r] = delta;
+          sm.qsum[wave][r] = delta * (float)qs;
+        }
+      }
+    }
+  }
+  __syncthreads();  // block-table entries and query operands staged
+
+  const int ga = n >> 1, limb = n & 1;  // A-tile row 2g+limb of this lane
+  const int t_a = tw0 + ga / G;         // chunk token of the lane's A row
+  const bool a_row_used = t_a < nq;
+  const int t_row0 = tw0 + (2 * jg) / G, t_row1 = tw0 + (2 * jg + 1) / G;  // tokens of rows x0, x1
+  const bool has0 = t_row0 < nq, has1 = t_row1 < nq;
+  const float c2 = a.sm_scale_log2;
+  i32x4 qa[2];
+  f16x8 qh[4];
+  float alpha0 = 0.f, beta0 = 0.f, alpha1 = 0.f, beta1 = 0.f;
+  if constexpr (FMT == 0) {
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2)
+      qa[a2] = a_row_used ? *(const i32x4*)&sm.qlimb[wave][limb][ga][a2][jg][0] : i32x4{0, 0, 0, 0};
+    alpha0 = has0 ? sm.qdelta[wave][2 * jg] * c2 : 0.0f;
+    beta0 = has0 ? sm.qsum[wave][2 * jg] * c2 : 0.0f;
+    alpha1 = has1 ? sm.qdelta[wave][2 * jg + 1] * c2 : 0.0f;
+    beta1 = has1 ? sm.qsum[wave][2 * jg + 1] * c2 : 0.0f;
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qh[kk] = a_row_used ? *(const f16x8*)&sm.qh[wave][limb][ga][kk][jg][0] : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  // ---- 2. stream pages 0 .. npw-1 (the positions this wave's rows attend) ----
+  const uint8_t* pool_h = a.pool + (int64_t)kvh * kPageHeadBytes;
+  const int64_t page_stride = (int64_t)a.hkv * kPageHeadBytes;
+  auto page_base = [&](int i) {
+    const int id = sm.table[min(i, kMaxTablePages - 1)];
+    const uint64_t addr = (uint64_t)(pool_h + (int64_t)id * page_stride);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+  };
+  const int koff = 64 * n + 16 * jg, voff = kVCodesOff + 16 * lane, poff = 4 * n, qoff = 16 * jg;
+  constexpr int NB = D + 1;
+  PageData<FMT> st[NB];
+#pragma unroll
+  for (int d = 0; d < D; ++d) st[d] = load_page<FMT>(page_base(d), d < npw, koff, voff, poff, qoff);
+  WaveState s;
+  s.m0 = s.m1 = kNegBig;
+  s.l0 = s.l1 = s.pz0 = s.pz1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // tokens of page i that row x attends: (p_x + 1) - 16 i
+  const int lim0 = pos0 + t_row0 + 1, lim1 = pos0 + t_row1 + 1;
+  for (int i0 = 0; i0 < npw; i0 += NB) {
+#pragma unroll
+    for (int d = 0; d < NB; ++d) {
+      const int i = i0 + d;
+      st[(d + D) % NB] = load_page<FMT>(page_base(i + D), i + D < npw, koff, voff, poff, qoff);
+      if (i < npw) {
+        if constexpr (FMT == 0)
+          process_page(st[d], lim0 - i * kPage, lim1 - i * kPage, s, qa, alpha0, beta0, alpha1, beta1, has0, has1,
+                       n, jg, a_row_used, sm.ptile[wave]);
+        else
+          process_page_mx(st[d], lim0 - i * kPage, lim1 - i * kPage, s, qh, c2, has0, has1, n, jg, a_row_used,
+                          sm.ptile[wave]);
+      }
+    }
+  }
+
+  // ---- 3. normalise the 8 rows, rotate them back, store ----
+  const float l0 = row_sum16(s.l0), l1 = row_sum16(s.l1);
+  const float pz0 = row_sum16(s.pz0), pz1 = row_sum16(s.pz1);
+  const float il0 = has0 ? 1.0f / l0 : 0.0f, il1 = has1 ? 1.0f / l1 : 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int ch = n + 32 * q + 16 * e;
+      const f32x4 v = s.acc[2 * q + e];
+      const float sc = FMT == 1 ? 1.0f : (e ? 1048576.0f : 16777216.0f);
+      sm.wo[wave][2 * jg][ch] = (sc * (v[0] + v[1]) + pz0) * il0;
+      sm.wo[wave][2 * jg + 1][ch] = (sc * (v[2] + v[3]) + pz1) * il1;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float o0[kRows], o1[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    o0[r] = sm.wo[wave][r][lane];
+    o1[r] = sm.wo[wave][r][lane + 64];
+  }
+  float scale = 1.0f;
+  if (!a.out_rotated) {
+    fwht_rows<kRows>(o0, o1, a.had_block, lane);
+    scale = isb;
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int t = tw0 + r / G;
+    if (t < nq) {
+      const int64_t base = ((int64_t)(qbeg + t) * a.hq + kvh * G + r % G) * kHeadDim;
+      store_elem(a.out, base + lane, a.out_dtype, o0[r] * scale);
+      store_elem(a.out, base + lane + 64, a.out_dtype, o1[r] * scale);
+    }
+  }
+}
+
+namespace {
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillDepth = 3;
+}  // namespace
+
+int prefill_tokens_per_tile(int group) { return kPrefillWaves * (kRows / group); }
+
+hipError_t launch_prefill(const PrefillParams& p, int fmt, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)p.num_seqs * p.hkv * p.tiles));
+  if (fmt == 0)
+    hipLaunchKernelGGL((prefill_kernel<0, kPrefillWaves, kPrefillDepth>), grid, dim3(kPrefillWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<1, kPrefillWaves, kPrefillDepth>), grid, dim3(kPrefillWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

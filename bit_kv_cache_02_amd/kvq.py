@@ -58,6 +58,9 @@ SIGNATURES = [
     ("kvq_decode_step", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _P, _I32, _P, _I32,
                                        ctypes.c_float, _I32, _I32, _P, _I32, _P, _I32, ctypes.c_float,
                                        _P, _I32, ctypes.c_uint32, _P, ctypes.c_size_t, _P]),
+    ("kvq_prefill_attn", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _I32, ctypes.c_float, _I32, _I32,
+                                        _I32, _P, _P, _I32, _I32, _P, _I32, ctypes.c_float, _P, _I32,
+                                        ctypes.c_uint32, _P]),
     ("kvq_dequant_page", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _I32, _P, _P,
                                         ctypes.c_uint32, _P]),
     ("kvq_strerror", ctypes.c_char_p, [ctypes.c_int]),
@@ -224,6 +227,31 @@ def decode_step(cache: Cache, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
                                OUT_ROTATED if rotated else 0, _ptr(workspace),
                                0 if workspace is None else workspace.numel(), _stream())
     _check(st, "kvq_decode_step")
+    return out
+
+
+def prefill_attn(cache: Cache, q: torch.Tensor, cu_q: torch.Tensor, seq_lens: torch.Tensor,
+                 block_table: torch.Tensor, max_seq_len: int, max_q_len: int,
+                 out: Optional[torch.Tensor] = None, q_scale: float = 1.0, sm_scale: Optional[float] = None,
+                 out_dtype=torch.float32, rotated: bool = False) -> torch.Tensor:
+    """Causal attention of each sequence's chunk (its last cu_q[b+1]-cu_q[b] positions, already
+    appended) over the paged cache (kvq_prefill_attn)."""
+    _require(q, "q")
+    _require(cu_q, "cu_q", torch.int32)
+    _require(seq_lens, "seq_lens", torch.int32)
+    _require(block_table, "block_table", torch.int32)
+    t, hq, dim = q.shape
+    if out is None:
+        out = torch.empty((t, hq, dim), dtype=out_dtype, device=q.device)
+    _require(out, "out")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    d = cache.desc()
+    st = lib().kvq_prefill_attn(ctypes.byref(d), _ptr(q), _DTYPE_CODE[q.dtype], float(q_scale), hq, t,
+                                seq_lens.numel(), _ptr(cu_q), _ptr(seq_lens), int(max_seq_len), int(max_q_len),
+                                _ptr(block_table), block_table.shape[1], float(sm_scale), _ptr(out),
+                                _DTYPE_CODE[out.dtype], OUT_ROTATED if rotated else 0, _stream())
+    _check(st, "kvq_prefill_attn")
     return out
 
 

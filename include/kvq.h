@@ -174,6 +174,34 @@ int kvq_decode_step(const kvq_cache* cache, const void* k, const void* v, int32_
                     void* stream);
 
 /*
+ * kvq_prefill_attn -- chunked-prefill attention over the 4-bit cache: the new tokens of a turn
+ * attend over the resident prefix and, causally, over each other.
+ * (UltraQuant article, section on what it showed: prefixes kept resident in the 4-bit cache
+ * spare the re-prefill of later turns; SAW-INT4 summary, "Summary": attention served from the
+ * paged 4-bit cache.)
+ *
+ *   q            device [num_tokens][num_q_heads][128], dtype q_dtype (F16, BF16, F32,
+ *                FP8_E4M3); the kernel uses q_scale * q.
+ *   num_q_heads  as for kvq_decode_attn, with G = num_q_heads/num_kv_heads in {1, 2, 4, 8}.
+ *   cu_q         device int32[num_seqs+1], non-decreasing, cu_q[0] = 0, cu_q[num_seqs] <=
+ *                num_tokens: tokens cu_q[b] .. cu_q[b+1]-1 are the chunk of sequence b.
+ *   seq_lens     device int32[num_seqs]: positions in the cache, the chunk included (the
+ *                chunk's K/V must already be appended): chunk token j of sequence b sits at
+ *                position seq_lens[b] - (cu_q[b+1]-cu_q[b]) + j and attends positions 0 .. that.
+ *   max_seq_len  host hint >= every seq_lens[b], <= max_pages*16 and <= 131072.
+ *   max_q_len    host hint >= every cu_q[b+1]-cu_q[b] (sizes the grid).
+ *   out          device [num_tokens][num_q_heads][128], dtype out_dtype (F32, F16, BF16); rows
+ *                of tokens outside every chunk are not written.
+ *   flags        0 or KVQ_OUT_ROTATED, as for kvq_decode_attn.
+ * Needs no workspace and writes nothing but `out`.
+ */
+int kvq_prefill_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, float q_scale,
+                     int32_t num_q_heads, int32_t num_tokens, int32_t num_seqs,
+                     const int32_t* cu_q, const int32_t* seq_lens, int32_t max_seq_len,
+                     int32_t max_q_len, const int32_t* block_table, int32_t max_pages,
+                     float sm_scale, void* out, int32_t out_dtype, uint32_t flags, void* stream);
+
+/*
  * kvq_dequant_page -- dequantize whole pages (all 16 slots, all kv heads) to fp32.
  *   page_ids     device int32[n], each < num_pages.
  *   out_k, out_v device float[n][num_kv_heads][16][128]; channel order is natural.

@@ -148,6 +148,36 @@ def test_decode_step_empty_batch_is_a_no_op():
     assert _step(_desc(), B=0) == kvq.KVQ_OK
 
 
+def _prefill(desc, **kw):
+    args = dict(q=FAKE, qdt=kvq.BF16, qs=1.0, hq=8, T=10, B=2, cu=FAKE, sl=FAKE, msl=100, mq=10, bt=FAKE, mp=8,
+                sm=0.1, out=FAKE, odt=kvq.F32, flags=0)
+    args.update(kw)
+    return kvq.lib().kvq_prefill_attn(ctypes.byref(desc), args["q"], args["qdt"], args["qs"], args["hq"], args["T"],
+                                      args["B"], args["cu"], args["sl"], args["msl"], args["mq"], args["bt"],
+                                      args["mp"], args["sm"], args["out"], args["odt"], args["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=6), kvq.KVQ_ERR_UNSUPPORTED),          # group 3: rows per wave not a multiple
+    (dict(hq=3), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(cu=None), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(q=None), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(msl=129), kvq.KVQ_ERR_INVALID_ARG),       # > max_pages * 16
+    (dict(msl=140000, mp=9000), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(mq=101), kvq.KVQ_ERR_INVALID_ARG),        # chunk longer than the sequence bound
+    (dict(T=-1), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(odt=kvq.FP8_E4M3), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(flags=8), kvq.KVQ_ERR_INVALID_ARG),
+])
+def test_prefill_rejects_bad_args(kw, status):
+    assert _prefill(_desc(), **kw) == status
+
+
+def test_prefill_empty_is_a_no_op():
+    assert _prefill(_desc(), T=0) == kvq.KVQ_OK
+    assert _prefill(_desc(), B=0) == kvq.KVQ_OK
+
+
 def test_decode_workspace_sizing_and_check():
     # a few long sequences are split over several workgroups and need a workspace
     d = _desc(num_kv_heads=8)
