@@ -33,9 +33,10 @@ from bit_kv_cache_02_amd import kvq, workloads as wl  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 PAGE_HEAD = 2176
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_llama_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "bit_kv_cache_02_amd", "csrc", "kvq_decode.hip")
+CSRC = os.path.join(ROOT, "bit_kv_cache_02_amd", "csrc")
+DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_attn.h", "kvq_device.h")]
 APPEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_prefill_traffic.json")
-APPEND_SRC = os.path.join(ROOT, "bit_kv_cache_02_amd", "csrc", "kvq_append.hip")
+APPEND_SRC = [os.path.join(CSRC, f) for f in ("kvq_append.hip", "kvq_device.h")]
 
 
 def log(*a):
@@ -213,6 +214,46 @@ def time_prefill_append(dev, repeats=10):
     }
 
 
+def time_prefill_attention(w, caches, lens, dev, chunk=512, repeats=20):
+    """Chunked-prefill attention on the layer caches: every sequence's last `chunk` positions
+    (a new turn over the resident prefix) attend causally, 32 q / 8 kv heads."""
+    b = w.batch
+    gen = torch.Generator().manual_seed(7)
+    q = torch.randn((b * chunk, w.num_q_heads, 128), generator=gen).to(torch.bfloat16).to(dev)
+    cu_q = torch.arange(0, b * chunk + 1, chunk, dtype=torch.int32, device=dev)
+    sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    table, _ = wl.block_table(w, lens)
+    bt = torch.from_numpy(table).to(dev)
+    out = torch.empty((b * chunk, w.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    max_len = int(lens.max())
+    for i in range(3):
+        kvq.prefill_attn(caches[i % len(caches)], q, cu_q, sl, bt, max_len, chunk, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(repeats):
+        kvq.prefill_attn(caches[i % len(caches)], q, cu_q, sl, bt, max_len, chunk, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / repeats
+    # scores and p.V: 2 x 2 x 128 flop per (query row, attended position)
+    attended = sum(int(L) - chunk + j + 1 for L in lens for j in range(chunk))
+    flops = 4 * 128 * attended * w.num_q_heads
+    kv_bytes = int(sum(lens)) * w.num_kv_heads * 136
+    tflops = flops / us / 1e6
+    return {
+        "workload": f"chunked prefill: {b} seqs x {chunk}-token chunk over a {int(lens[0]) - chunk}-token "
+                    f"resident prefix, 32 q / 8 kv heads, INT4, Hadamard 128 (layer caches of the decode bench)",
+        "us": round(us, 2),
+        "tokens_per_s": round(b * chunk / us * 1e6, 1),
+        "TFLOPs": round(tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None},
+        "algorithmic_flops": flops,
+        "kv_bytes_once": kv_bytes,
+    }
+
+
 def hbm_copy_probe(dev, nbytes=1 << 30, repeats=10):
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
@@ -271,13 +312,14 @@ def cpu_baseline(w, budget_s=12.0, n_seqs=4):
     }
 
 
-def code_sha256(path):
-    """sha256 of a source file's code: comment-only edits leave it unchanged."""
+def code_sha256(paths):
+    """sha256 of the code of the given source files: comment-only edits leave it unchanged."""
     lines = []
-    for line in open(path, encoding="utf-8"):
-        code = line.split("//", 1)[0].rstrip()
-        if code:
-            lines.append(code)
+    for path in paths:
+        for line in open(path, encoding="utf-8"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                lines.append(code)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
@@ -389,6 +431,9 @@ def main():
         **res,
     }
     del every, single
+    if not args.no_prefill:
+        log("[bench] chunked-prefill attention")
+        res["prefill_attention"] = time_prefill_attention(w, caches, lens, dev)
     log("[bench] HBM copy probe")
     res["hbm_copy_GBps"] = round(hbm_copy_probe(dev), 1)
     res["step_frac_of_copy_bw"] = round(achieved / res["hbm_copy_GBps"], 4)
