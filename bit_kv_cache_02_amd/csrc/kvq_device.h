@@ -52,13 +52,6 @@ __device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp_f<kRowMirror>(x));
   return x;
 }
-__device__ __forceinline__ float row_min16(float x) {
-  x = fminf(x, dpp_f<kQuadSwap1>(x));
-  x = fminf(x, dpp_f<kQuadSwap2>(x));
-  x = fminf(x, dpp_f<kRowHalfMirror>(x));
-  x = fminf(x, dpp_f<kRowMirror>(x));
-  return x;
-}
 __device__ __forceinline__ float row_sum16(float x) {
   x = x + dpp_f<kQuadSwap1>(x);
   x = x + dpp_f<kQuadSwap2>(x);
@@ -118,14 +111,6 @@ __device__ __forceinline__ float raw_to_f32(uint32_t bits, int dt) {
   }
 }
 
-__device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
-  switch (dt) {
-    case DT_F16: return f16_bits_to_f32(((const uint16_t*)p)[i]);
-    case DT_BF16: return bf16_bits_to_f32(((const uint16_t*)p)[i]);
-    case DT_F32: return ((const float*)p)[i];
-    default: return e4m3_to_f32(((const uint8_t*)p)[i]);
-  }
-}
 __device__ __forceinline__ void store_elem(void* p, int64_t i, int dt, float x) {
   switch (dt) {
     case DT_F16: ((uint16_t*)p)[i] = (uint16_t)f32_to_f16_bits(x); break;
