@@ -327,6 +327,15 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   for (int i = 0; i < 8; ++i) s.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int valid0 = L - pw0 * kPage;
   for (int i0 = 0; i0 < npw; i0 += NB) {
+    // The waves of a workgroup hold equal shares of the pages, but the issue arbiter favours
+    // older waves, which would finish first and leave the last pages to fewer waves (fewer loads
+    // in flight).  A wave's priority falls as it progresses, so the waves that are behind get
+    // the issue slots.
+    const int progress = 4 * i0;  // compared with 3 npw, 2 npw, npw
+    if (progress < npw) __builtin_amdgcn_s_setprio(3);
+    else if (progress < 2 * npw) __builtin_amdgcn_s_setprio(2);
+    else if (progress < 3 * npw) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int d = 0; d < NB; ++d) {
       const int i = i0 + d;
