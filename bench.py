@@ -169,6 +169,60 @@ def time_graph_steps(every, single, steps, warmup):
     return wall, e0.elapsed_time(e1) * 1e3 / steps
 
 
+def time_mxfp4_decode(dev, repeats=40):
+    """MXFP4 decode, 64 x 16K contexts, 64 q / 8 kv heads, fp8 e4m3 queries, over 2 alternating
+    pools (2.3 GB, beyond the Infinity Cache): q.K on f16 tiles vs the scaled FP8 x FP4 MFMA."""
+    from concurrent.futures import ThreadPoolExecutor
+    w = wl.WORKLOADS["mxfp4"]
+    lens = wl.seq_lens(w)
+    table, num_pages = wl.block_table(w, lens)
+    bt = torch.from_numpy(table).to(dev)
+    caches = [kvq.Cache(num_pages, w.num_kv_heads, w.had_block, "mxfp4", device=dev) for _ in range(2)]
+    zeros = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    with ThreadPoolExecutor(8) as ex:
+        for b0 in range(0, w.batch, 8):
+            seqs = list(ex.map(lambda b: wl.sequence_kv(w, b, int(lens[b])), range(b0, b0 + 8)))
+            cnt = np.zeros(w.batch, np.int64)
+            cnt[b0:b0 + 8] = lens[b0:b0 + 8]
+            cu = torch.from_numpy(np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)).to(dev)
+            k = torch.from_numpy(np.concatenate([x[0] for x in seqs])).to(torch.bfloat16).to(dev)
+            v = torch.from_numpy(np.concatenate([x[1] for x in seqs])).to(torch.bfloat16).to(dev)
+            kvq.append(caches[0], k, v, cu, zeros, bt, int(lens.max()))
+            del seqs, k, v
+    caches[1].pool.copy_(caches[0].pool)
+    q = torch.from_numpy(wl.queries(w)).to(torch.float8_e4m3fn).to(dev)
+    sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    max_len = int(lens.max())
+    ws = kvq.make_workspace(caches[0], w.num_q_heads, w.batch, max_len, dev)
+    for i in range(30):
+        kvq.decode_attn(caches[i % 2], q, sl, bt, max_len, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    times = {False: [], True: []}
+    for scaled in (False, True, False, True):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(repeats):
+            kvq.decode_attn(caches[i % 2], q, sl, bt, max_len, out=out, workspace=ws, scaled_mfma=scaled)
+        e1.record()
+        torch.cuda.synchronize()
+        times[scaled].append(e0.elapsed_time(e1) * 1e3 / repeats)
+    nbytes = int(lens.sum()) * w.num_kv_heads * 136 + w.batch * w.num_q_heads * 128 * 3 + \
+        int(sum(-(-int(n) // 16) for n in lens)) * 4 + w.batch * 4
+    f16_us, sc_us = float(np.mean(times[False])), float(np.mean(times[True]))
+    del caches
+    return {
+        "workload": "MXFP4 decode: 64 seqs x context 16384, 64 q / 8 kv heads, fp8 e4m3 queries, e2m1 + "
+                    "UE8M0/32 after the Hadamard 128 rotation, bf16 out; 2 pools alternated",
+        "us_f16_tiles": round(f16_us, 2),
+        "us_scaled_mfma": round(sc_us, 2),
+        "GBps": round(nbytes / f16_us / 1e3, 1),
+        "frac_of_hbm_peak": round(nbytes / f16_us / 1e3 / HBM_PEAK_GBPS, 4),
+        "GBps_scaled_mfma": round(nbytes / sc_us / 1e3, 1),
+        "algorithmic_bytes": nbytes,
+    }
+
+
 def time_prefill_append(dev, repeats=10):
     """64 x 2048 heavy-tailed bf16 tokens into 2 alternating pools; rotation b=128 vs none."""
     w = wl.WORKLOADS["prefill"]
@@ -186,7 +240,7 @@ def time_prefill_append(dev, repeats=10):
     start = torch.zeros(w.batch, dtype=torch.int32, device=dev)
     bt = torch.from_numpy(table).to(dev)
     res = {}
-    for hb in (128, 1):
+    for hb in (128, 64, 1):
         pools = [kvq.Cache(num_pages, w.num_kv_heads, hb, device=dev) for _ in range(2)]
         for c in pools:
             kvq.append(c, k, v, cu, start, bt, int(lens.max()))
@@ -205,6 +259,7 @@ def time_prefill_append(dev, repeats=10):
     return {
         "workload": "prefill append: 64 seqs x 2048 new tokens, 8 kv heads, bf16 Student-t(3), page 16",
         "us_rotated_b128": round(res[128], 2),
+        "us_rotated_b64": round(res[64], 2),
         "us_plain_int4": round(res[1], 2),
         "rotation_overhead_pct": round(100.0 * (res[128] / res[1] - 1.0), 2),
         "GBps": round(nbytes / res[128] / 1e3, 1),
@@ -345,6 +400,7 @@ def main():
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--profile-run", action="store_true",
                     help="run for rocprofv3: the fused steps as timed by default, the copy probe, "
@@ -444,6 +500,10 @@ def main():
         res["prefill_append"] = time_prefill_append(dev, repeats=3 if args.profile_run else 10)
         res["prefill_append"]["traffic"] = traffic_entry(res["prefill_append"]["algorithmic_bytes"],
                                                          APPEND_TRAFFIC_FILE, APPEND_SRC, "append_source_sha256")
+        torch.cuda.empty_cache()
+    if not args.no_mxfp4 and not args.profile_run:
+        log("[bench] MXFP4 decode (f16-tile and scaled-MFMA q.K)")
+        res["mxfp4_decode"] = time_mxfp4_decode(dev)
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)

@@ -221,10 +221,7 @@ __device__ __forceinline__ void process_page(const PageData<0>& pg, int valid0, 
 //        all in channel group q (one scale).
 //   p.V: v_mfma_f32_16x16x16_f16, A = p split high/low, B = V tile: byte r of V word q is token
 //        4jg+r, channels n+32q and n+32q+16 (group q), repacked so one register holds two tokens.
-__device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid0, int valid1, WaveState& s,
-                                                const f16x8 (&qh)[4], float c2, bool has0, bool has1,
-                                                int n, int jg, bool a_row_used, _Float16 (*ptile)[kPage]) {
-  const bool tv0 = n < valid0, tv1 = n < valid1;
+__device__ __forceinline__ f32x4 scores_mx(const PageData<1>& pg, const f16x8 (&qh)[4]) {
   f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -238,6 +235,110 @@ __device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid
     }
     sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[kk], kb, sc, 0, 0, 0);
   }
+  return sc;
+}
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+// The q.K scores of an MXFP4 page on the scaled matrix cores (UltraQuant article, section on how
+// the method works: FP8 queries against FP4 KV with UE8M0 group scales on CDNA4's native scaled
+// MFMA): v_mfma_scale_f32_16x16x128_f8f6f4 with A = q' as MXFP8 (e4m3 elements, one UE8M0 scale
+// per 32 channels) and B = the stored e2m1 K codes with their stored UE8M0 bytes, no conversion.
+//
+// The MFMA takes one scale per (B column, 32-long K block), so a lane's 32 B nibbles must all be
+// codes of one channel group.  A code row word a carries channel a + 16i in nibble i: byte q of
+// every word belongs to group q.  group_codes() turns the 16 row bytes a lane loads (words
+// 4jg..4jg+3 of token n) into the 32 codes of group jg of token n: a 4x4 byte transpose inside
+// the lane (byte q of the four words -> dword q) and a 4x4 dword transpose across the four
+// 16-lane rows (two permlane swap stages).  Dword k then holds byte jg of words 4k..4k+3, so B
+// nibble i = 8k + 2w + h is channel 4k + w + 32jg + 16h; mxfp8_k_index() gives the A tiles the
+// same order.
+__device__ __forceinline__ u32x4 group_codes(const u32x4& w) {
+  const uint32_t p01l = perm(w[1], w[0], 0x05010400u), p01h = perm(w[1], w[0], 0x07030602u);
+  const uint32_t p23l = perm(w[3], w[2], 0x05010400u), p23h = perm(w[3], w[2], 0x07030602u);
+  uint32_t s0 = perm(p23l, p01l, 0x05040100u), s1 = perm(p23l, p01l, 0x07060302u);
+  uint32_t s2 = perm(p23h, p01h, 0x05040100u), s3 = perm(p23h, p01h, 0x07060302u);
+  // dword q of lane row r is element (r, q) of a 4x4 matrix; transpose it: swap the off-diagonal
+  // 2x2 blocks (rows 2,3 of dwords 0,1 <-> rows 0,1 of dwords 2,3), then the off-diagonal
+  // elements inside each block (odd rows of dwords 0 / 2 <-> even rows of dwords 1 / 3)
+  const auto x = __builtin_amdgcn_permlane32_swap(s0, s2, false, false);
+  const auto y = __builtin_amdgcn_permlane32_swap(s1, s3, false, false);
+  const auto u = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+  const auto v = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+  return u32x4{u[0], u[1], v[0], v[1]};
+}
+
+// K index of channel ch in the scaled q.K contraction (the inverse of the order above)
+__device__ __forceinline__ int mxfp8_k_index(int ch) {
+  return (ch & ~31) + 8 * ((ch >> 2) & 3) + 2 * (ch & 3) + ((ch >> 4) & 1);
+}
+
+// q' of one head (channel `lane` in v0, `lane + 64` in v1) as three MXFP8 limbs: limb t is q'
+// minus the limbs before it, in e4m3 with one UE8M0 scale per 32 channels (OCP MX rule:
+// 2^(floor(log2 amax) - 8), elements rounded to nearest even and clamped at 448), subtracted as the
+// matrix cores will decode it.  Limb t goes to A tile t/2, row 2g + t%2, bytes in K order;
+// q8s[tile][row][group] gets its scales.  One scaled MFMA pass sums its products to ~2^-14 of the
+// largest one, so three limbs (~12 bits) keep the scores as exact as that pass allows.
+__device__ __forceinline__ void mxfp8_limbs(float v0, float v1, int g, int lane, uint8_t (*q8)[16][kHeadDim],
+                                            uint8_t (*q8s)[16][4]) {
+  // lanes 0-31 / 32-63 of v0 hold channel groups 0 / 1, of v1 groups 2 / 3
+  const int k0 = mxfp8_k_index(lane), k1 = mxfp8_k_index(lane + 64);
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    float m0 = row_max16(fabsf(v0)), m1 = row_max16(fabsf(v1));
+    m0 = fmaxf(m0, __shfl_xor(m0, 16));
+    m1 = fmaxf(m1, __shfl_xor(m1, 16));
+    const int e0 = min(max((int)((__float_as_uint(m0) >> 23) & 255u) - 8, 0), 254);
+    const int e1 = min(max((int)((__float_as_uint(m1) >> 23) & 255u) - 8, 0), 254);
+    const float y0 = fminf(fmaxf(ldexpf(v0, 127 - e0), -448.0f), 448.0f);
+    const float y1 = fminf(fmaxf(ldexpf(v1, 127 - e1), -448.0f), 448.0f);
+    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+    v0 -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 0), e0 - 127);
+    v1 -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 1), e1 - 127);
+    const int tile = t >> 1, row = 2 * g + (t & 1);
+    q8[tile][row][k0] = (uint8_t)(pk & 255);
+    q8[tile][row][k1] = (uint8_t)((pk >> 8) & 255);
+    if ((lane & 31) == 0) {
+      q8s[tile][row][lane >> 5] = (uint8_t)e0;
+      q8s[tile][row][2 + (lane >> 5)] = (uint8_t)e1;
+    }
+  }
+}
+
+// A tiles of lane (jg, n): fp8 A operands hold K 16jg..16jg+15 in bytes 0-15 and K 64+16jg..
+// in bytes 16-31, row n; the lane's scale is that of row n, K block (channel group) jg.  Tile 1
+// uses its even rows only.
+__device__ __forceinline__ void mxfp8_a_tiles(const uint8_t (*q8)[16][kHeadDim], const uint8_t (*q8s)[16][4],
+                                              bool a_row_used, int limb, int n, int jg, i32x8 (&qa8)[2],
+                                              int (&qsa)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const bool used = a_row_used && (t == 0 || limb == 0);
+    const u32x4 lo = used ? *(const u32x4*)&q8[t][n][16 * jg] : u32x4{0, 0, 0, 0};
+    const u32x4 hi = used ? *(const u32x4*)&q8[t][n][64 + 16 * jg] : u32x4{0, 0, 0, 0};
+    qa8[t] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    qsa[t] = used ? (int)q8s[t][n][jg] : 127;
+  }
+}
+
+__device__ __forceinline__ f32x4 scores_mx_scaled(const PageData<1>& pg, const i32x8 (&qa8)[2],
+                                                  const int (&qsa)[2], int jg) {
+  const int sb = (int)(pg.kp >> (8 * jg));  // the MFMA reads bits 7:0: group jg of token n
+  const u32x4 c = group_codes(pg.k);
+  const i32x8 kb = i32x8{(int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0, 0, 0};
+  // format codes: 0 = fp8 e4m3 (A), 4 = fp4 e2m1 (B)
+  f32x4 sc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa8[0], kb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0,
+                                                               qsa[0], 0, sb);
+  sc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa8[1], kb, sc, 0, 4, 0, qsa[1], 0, sb);
+  return sc;
+}
+
+// Online softmax and p.V of an MXFP4 page, from its q.K scores (C layout: column n = token n,
+// rows 4jg..4jg+3 = A rows 2g+part of heads 2jg, 2jg+1).
+__device__ __forceinline__ void softmax_pv_mx(const PageData<1>& pg, f32x4 sc, int valid0, int valid1,
+                                              WaveState& s, float c2, bool has0, bool has1, int n, int jg,
+                                              bool a_row_used, _Float16 (*ptile)[kPage]) {
+  const bool tv0 = n < valid0, tv1 = n < valid1;
   float x0 = (sc[0] + sc[1]) * c2, x1 = (sc[2] + sc[3]) * c2;
   x0 = tv0 ? x0 : -INFINITY;
   x1 = tv1 ? x1 : -INFINITY;
@@ -294,6 +395,20 @@ __device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid
     s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, blo, s.acc[2 * q], 0, 0, 0);
     s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bhi, s.acc[2 * q + 1], 0, 0, 0);
   }
+}
+
+__device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid0, int valid1, WaveState& s,
+                                                const f16x8 (&qh)[4], float c2, bool has0, bool has1,
+                                                int n, int jg, bool a_row_used, _Float16 (*ptile)[kPage]) {
+  softmax_pv_mx(pg, scores_mx(pg, qh), valid0, valid1, s, c2, has0, has1, n, jg, a_row_used, ptile);
+}
+
+__device__ __forceinline__ void process_page_mx_scaled(const PageData<1>& pg, int valid0, int valid1, WaveState& s,
+                                                       const i32x8 (&qa8)[2], const int (&qsa)[2], float c2,
+                                                       bool has0, bool has1, int n, int jg, bool a_row_used,
+                                                       _Float16 (*ptile)[kPage]) {
+  softmax_pv_mx(pg, scores_mx_scaled(pg, qa8, qsa, jg), valid0, valid1, s, c2, has0, has1, n, jg, a_row_used,
+                ptile);
 }
 
 // Rotate one row's normalised o' (element lane in o0, lane + 64 in o1) back and store it at

@@ -45,6 +45,10 @@ struct DecodeSmem {
   uint8_t qlimb[2][kMaxG][2][4][16];
   // MXFP4: q' as fp16 high/low parts in the A-tile order of the f16 q.K MFMA: [part][g][kk][jg][8]
   _Float16 qh[2][kMaxG][4][4][8];
+  // MXFP4 on the scaled matrix cores: q' limbs as the e4m3 A tiles [tile][row][K] and their
+  // UE8M0 scales [tile][row][channel group] (row 2g+t: limb t+1; tile 1 row 2g: limb 3)
+  uint8_t q8[2][16][kHeadDim];
+  uint8_t q8s[2][16][4];
   float qdelta[kMaxG];
   float qsum[kMaxG];
   _Float16 ptile[W][2 * kMaxG][kPage];  // p~ split into fp16 high/low parts, A-tile rows 2g+limb
@@ -88,8 +92,10 @@ __device__ __forceinline__ void store_head(const DecodeParams& a, float o0, floa
 
 }  // namespace
 
+// FMT: 0 INT4; 1 MXFP4 (f16 tiles); 2 MXFP4 with q.K on the scaled FP8 x FP4 matrix cores
 template <int FMT, int W, int D>
 __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
+  constexpr int PF = FMT == 0 ? 0 : 1;  // page format
   __shared__ DecodeSmem<W> sm;
   const int tid = thread_id();
   const int lane = tid & 63;
@@ -189,9 +195,9 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   };
   const int koff = 64 * n + 16 * jg, voff = kVCodesOff + 16 * lane, poff = 4 * n, qoff = 16 * jg;
   constexpr int NB = D + 1;  // register buffers: D pages in flight plus the one being processed
-  PageData<FMT> st[NB];
+  PageData<PF> st[NB];
 #pragma unroll
-  for (int d = 0; d < D; ++d) st[d] = load_page<FMT>(page_base(d), d < npw, koff, voff, poff, qoff);
+  for (int d = 0; d < D; ++d) st[d] = load_page<PF>(page_base(d), d < npw, koff, voff, poff, qoff);
 
   // ---- 2. q' = R_b (q_scale q) in registers, then 16-bit fixed point q' ~= delta_g * Q with
   //         |Q| <= 32000, stored as two int8 limbs (Q = 256*hi + lo) in the A-tile byte order ----
@@ -203,6 +209,10 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       fwht_wave(v0, v1, a.had_block, lane);
       v0 *= isb;
       v1 *= isb;
+      if constexpr (FMT == 2) {
+        mxfp8_limbs(v0, v1, g, lane, sm.q8, sm.q8s);
+        continue;
+      }
       if constexpr (FMT == 1) {
         // fp16 high/low parts; channel (4jg + kk) + 32q + 16e sits at element 2q + e = ch >> 4
 #pragma unroll
@@ -304,6 +314,8 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   const float c2 = a.sm_scale_log2;
   i32x4 qa[2];
   f16x8 qh[4];
+  i32x8 qa8[2];
+  int qsa[2];
   float alpha0 = 0.f, beta0 = 0.f, alpha1 = 0.f, beta1 = 0.f;
   if constexpr (FMT == 0) {
 #pragma unroll
@@ -313,10 +325,12 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
     beta0 = has0 ? sm.qsum[2 * jg] * c2 : 0.0f;
     alpha1 = has1 ? sm.qdelta[2 * jg + 1] * c2 : 0.0f;
     beta1 = has1 ? sm.qsum[2 * jg + 1] * c2 : 0.0f;
-  } else {
+  } else if constexpr (FMT == 1) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
       qh[kk] = a_row_used ? *(const f16x8*)&sm.qh[limb][ga][kk][jg][0] : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  } else {
+    mxfp8_a_tiles(sm.q8, sm.q8s, a_row_used, limb, n, jg, qa8, qsa);
   }
 
   // ---- 3. stream this wave's pages ----
@@ -340,15 +354,18 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
     for (int d = 0; d < NB; ++d) {
       const int i = i0 + d;
       // page i sits in buffer d; page i + D goes to the buffer freed by page i - 1
-      st[(d + D) % NB] = load_page<FMT>(page_base(i + D), i + D < npw, koff, voff, poff, qoff);
+      st[(d + D) % NB] = load_page<PF>(page_base(i + D), i + D < npw, koff, voff, poff, qoff);
       if (i < npw) {
-        if (app_wg && pw0 + W * i == last_pg) patch_appended<FMT>(st[d], sm.arow, sm.aparam, app_slot, n, jg);
+        if (app_wg && pw0 + W * i == last_pg) patch_appended<PF>(st[d], sm.arow, sm.aparam, app_slot, n, jg);
         if constexpr (FMT == 0)
           process_page(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, s, qa, alpha0, beta0, alpha1, beta1,
                        has0, has1, n, jg, a_row_used, sm.ptile[wave]);
-        else
+        else if constexpr (FMT == 1)
           process_page_mx(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, s, qh, c2, has0, has1, n, jg,
                           a_row_used, sm.ptile[wave]);
+        else
+          process_page_mx_scaled(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, s, qa8, qsa, c2, has0,
+                                 has1, n, jg, a_row_used, sm.ptile[wave]);
       }
     }
   }
@@ -363,7 +380,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       const int ch = n + 32 * q + 16 * e;
       const f32x4 v = s.acc[2 * q + e];
       // INT4: undo the subnormal encoding (2^24, or 2^24/16 for the high nibbles); MXFP4: none
-      const float sc = FMT == 1 ? 1.0f : (e ? 1048576.0f : 16777216.0f);
+      const float sc = FMT != 0 ? 1.0f : (e ? 1048576.0f : 16777216.0f);
       if (has0) sm.wo[wave][2 * jg][ch] = sc * (v[0] + v[1]) + pz0;
       if (has1) sm.wo[wave][2 * jg + 1][ch] = sc * (v[2] + v[3]) + pz1;
     }
@@ -514,7 +531,8 @@ void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, in
   *part_o = (float*)p;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int fmt, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int variant, hipStream_t stream) {
+  const int fmt = variant;
   const int64_t units = (int64_t)p.num_seqs * p.hkv;
   const dim3 grid((unsigned)(units * p.plan.nsplit));
 #define KVQ_DECODE_CASE(F, WV, DV)                                                               \
@@ -526,7 +544,10 @@ hipError_t launch_decode(const DecodeParams& p, int fmt, hipStream_t stream) {
   KVQ_DECODE_CASE(0, 16, 2)
   KVQ_DECODE_CASE(1, 4, 2) KVQ_DECODE_CASE(1, 4, 3) KVQ_DECODE_CASE(1, 4, 4)
   KVQ_DECODE_CASE(1, 8, 2) KVQ_DECODE_CASE(1, 8, 3) KVQ_DECODE_CASE(1, 8, 4)
-  KVQ_DECODE_CASE(1, 16, 2) { return hipErrorInvalidValue; }
+  KVQ_DECODE_CASE(1, 16, 2)
+  KVQ_DECODE_CASE(2, 4, 2) KVQ_DECODE_CASE(2, 4, 3) KVQ_DECODE_CASE(2, 4, 4)
+  KVQ_DECODE_CASE(2, 8, 2) KVQ_DECODE_CASE(2, 8, 3) KVQ_DECODE_CASE(2, 8, 4)
+  KVQ_DECODE_CASE(2, 16, 2) { return hipErrorInvalidValue; }
 #undef KVQ_DECODE_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.plan.nsplit <= 1) return e;

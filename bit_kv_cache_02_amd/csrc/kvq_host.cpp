@@ -143,7 +143,9 @@ static int decode_common(const kvq_cache* cache, const void* knew, const void* v
     return fail(KVQ_ERR_UNSUPPORTED, "num_seqs * num_q_heads %lld too large", (long long)num_seqs * num_q_heads);
   if ((int64_t)max_seq_len > (int64_t)max_pages * KVQ_PAGE_SIZE)
     return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d exceeds max_pages*16 = %lld", max_seq_len, (long long)max_pages * KVQ_PAGE_SIZE);
-  if (flags & ~KVQ_OUT_ROTATED) return fail(KVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (flags & ~(KVQ_OUT_ROTATED | KVQ_MX_SCALED_MFMA)) return fail(KVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((flags & KVQ_MX_SCALED_MFMA) && cache->format != KVQ_FMT_MXFP4_G32)
+    return fail(KVQ_ERR_UNSUPPORTED, "KVQ_MX_SCALED_MFMA needs an MXFP4 cache");
   if (!std::isfinite(q_scale) || !std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARG, "q_scale and sm_scale must be finite");
   const bool append = knew != nullptr || vnew != nullptr;
   if (append) {
@@ -185,7 +187,9 @@ static int decode_common(const kvq_cache* cache, const void* knew, const void* v
   p.kv_dtype = append ? kv_dtype : KVQ_BF16;
   p.append = append ? 1 : 0;
   p.plan = plan;
-  return hip_status(kvq::launch_decode(p, cache->format, (hipStream_t)stream), what);
+  // kernel variant 2: MXFP4 with q.K on the scaled matrix cores
+  const int variant = (flags & KVQ_MX_SCALED_MFMA) ? 2 : cache->format;
+  return hip_status(kvq::launch_decode(p, variant, (hipStream_t)stream), what);
 }
 
 int kvq_decode_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, float q_scale,

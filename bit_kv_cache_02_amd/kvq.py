@@ -20,6 +20,7 @@ KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP
 FMT_INT4, FMT_MXFP4 = 0, 1
 F16, BF16, F32, FP8_E4M3 = 0, 1, 2, 3
 OUT_ROTATED = 1
+MX_SCALED_MFMA = 2
 UNROTATE = 1
 HEAD_DIM = 128
 PAGE_SIZE = 16
@@ -172,11 +173,18 @@ def make_workspace(cache: Cache, num_q_heads: int, num_seqs: int, max_seq_len: i
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _flags(rotated: bool, scaled_mfma: bool) -> int:
+    return (OUT_ROTATED if rotated else 0) | (MX_SCALED_MFMA if scaled_mfma else 0)
+
+
 def decode_attn(cache: Cache, q: torch.Tensor, seq_lens: torch.Tensor, block_table: torch.Tensor,
                 max_seq_len: int, out: Optional[torch.Tensor] = None, q_scale: float = 1.0,
                 sm_scale: Optional[float] = None, out_dtype=torch.float32, rotated: bool = False,
-                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """softmax(q'.K'^T) V' over the paged cache, rotated back (kvq_decode_attn)."""
+                workspace: Optional[torch.Tensor] = None, scaled_mfma: bool = False) -> torch.Tensor:
+    """softmax(q'.K'^T) V' over the paged cache, rotated back (kvq_decode_attn).
+
+    scaled_mfma (MXFP4 caches): q.K on the scaled FP8 x FP4 matrix cores (KVQ_MX_SCALED_MFMA).
+    """
     _require(q, "q")
     _require(seq_lens, "seq_lens", torch.int32)
     _require(block_table, "block_table", torch.int32)
@@ -192,7 +200,7 @@ def decode_attn(cache: Cache, q: torch.Tensor, seq_lens: torch.Tensor, block_tab
     st = lib().kvq_decode_attn(ctypes.byref(d), _ptr(q), _DTYPE_CODE[q.dtype], float(q_scale), hq, b,
                                _ptr(seq_lens), int(max_seq_len), _ptr(block_table),
                                block_table.shape[1], float(sm_scale), _ptr(out),
-                               _DTYPE_CODE[out.dtype], OUT_ROTATED if rotated else 0,
+                               _DTYPE_CODE[out.dtype], _flags(rotated, scaled_mfma),
                                _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                _stream())
     _check(st, "kvq_decode_attn")
@@ -202,7 +210,8 @@ def decode_attn(cache: Cache, q: torch.Tensor, seq_lens: torch.Tensor, block_tab
 def decode_step(cache: Cache, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, seq_lens: torch.Tensor,
                 block_table: torch.Tensor, max_seq_len: int, out: Optional[torch.Tensor] = None,
                 q_scale: float = 1.0, sm_scale: Optional[float] = None, out_dtype=torch.float32,
-                rotated: bool = False, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                rotated: bool = False, workspace: Optional[torch.Tensor] = None,
+                scaled_mfma: bool = False) -> torch.Tensor:
     """Append k[b], v[b] at position seq_lens[b]-1, then attend [0, seq_lens[b]) (kvq_decode_step)."""
     _require(k, "k")
     _require(v, "v")
@@ -224,7 +233,7 @@ def decode_step(cache: Cache, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
                                _DTYPE_CODE[q.dtype], float(q_scale), hq, b, _ptr(seq_lens),
                                int(max_seq_len), _ptr(block_table), block_table.shape[1],
                                float(sm_scale), _ptr(out), _DTYPE_CODE[out.dtype],
-                               OUT_ROTATED if rotated else 0, _ptr(workspace),
+                               _flags(rotated, scaled_mfma), _ptr(workspace),
                                0 if workspace is None else workspace.numel(), _stream())
     _check(st, "kvq_decode_step")
     return out

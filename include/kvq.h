@@ -66,6 +66,7 @@ typedef enum { KVQ_F16 = 0, KVQ_BF16 = 1, KVQ_F32 = 2, KVQ_FP8_E4M3 = 3 } kvq_dt
 
 /* kvq_decode_attn flags */
 #define KVQ_OUT_ROTATED 1u /* leave the output in the rotated basis (skip the final R_b) */
+#define KVQ_MX_SCALED_MFMA 2u /* MXFP4 caches: q.K on the scaled FP8 x FP4 matrix cores    */
 /* kvq_dequant_page flags */
 #define KVQ_UNROTATE 1u    /* return R_b * y^ (the original basis) instead of y^          */
 
@@ -138,6 +139,13 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_q_heads,
  *   out          device [num_seqs][num_q_heads][128], dtype out_dtype (F32, F16, BF16):
  *                o = R_b * sum_t softmax_t(sm_scale * q'.k^'_t) v^'_t, or the rotated-basis
  *                result with KVQ_OUT_ROTATED.
+ *   flags        KVQ_OUT_ROTATED (above) and, for MXFP4 caches only, KVQ_MX_SCALED_MFMA: the
+ *                q.K contraction then runs on v_mfma_scale_f32_16x16x128_f8f6f4 straight on the
+ *                stored e2m1 K codes and their UE8M0 bytes (UltraQuant article, section on how the
+ *                method works: FP8 queries, FP4 KV, UE8M0 group scales, native scaled MFMA on
+ *                CDNA4), with q' carried as three MXFP8 limbs; p.V is unchanged.  The result
+ *                agrees with the default path to the same tolerance.  KVQ_ERR_UNSUPPORTED on an
+ *                INT4 cache; any other bit is KVQ_ERR_INVALID_ARG.
  *   workspace    device, >= kvq_decode_workspace_bytes(...) bytes, 256-byte aligned; calls
  *                that overlap in time (other streams) need workspaces of their own.
  * Decode does not append: a decode step is kvq_append then kvq_decode_attn on one stream, or

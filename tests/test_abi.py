@@ -114,6 +114,7 @@ def _decode(desc, **kw):
     (dict(odt=kvq.FP8_E4M3), kvq.KVQ_ERR_UNSUPPORTED),
     (dict(qdt=9), kvq.KVQ_ERR_UNSUPPORTED),
     (dict(flags=4), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(flags=kvq.MX_SCALED_MFMA), kvq.KVQ_ERR_UNSUPPORTED),  # the scaled FP8 x FP4 path on an INT4 cache
     (dict(sm=float("nan")), kvq.KVQ_ERR_INVALID_ARG),
 ])
 def test_decode_rejects_bad_args(kw, status):
@@ -139,6 +140,8 @@ def _step(desc, **kw):
     (dict(msl=129), kvq.KVQ_ERR_INVALID_ARG),
     (dict(q=None), kvq.KVQ_ERR_INVALID_ARG),
     (dict(odt=kvq.FP8_E4M3), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(flags=kvq.MX_SCALED_MFMA), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(flags=kvq.MX_SCALED_MFMA | 4), kvq.KVQ_ERR_INVALID_ARG),
 ])
 def test_decode_step_rejects_bad_args(kw, status):
     assert _step(_desc(), **kw) == status

@@ -90,15 +90,19 @@ def _check_decode_workload(name, sample):
             torch.from_numpy(pool_o[pages]).to(dev)
     q = wl.queries(w)
     q_t = torch.from_numpy(q).to(QDT[w.q_dtype])
-    out = kvq.decode_attn(cache, q_t.to(dev), torch.from_numpy(lens.astype(np.int32)).to(dev),
-                          torch.from_numpy(table).to(dev), int(lens.max()), out_dtype=torch.float32)
-    torch.cuda.synchronize()
-    got = out.cpu().numpy()
     ref = oracle.decode_attention(pool_o, q_t.float().numpy(), lens, table, w.had_block, FMT[w.fmt],
                                   seqs=sample)
-    err = parity.attn_row_error(got[sample], ref[sample])
-    print(f"[config] {name}: decode max row err {err.max():.3e} on sequences {sample}", flush=True)
-    assert err.max() <= parity.ATTN_TOL
+    # MXFP4: also the path with q.K on the scaled FP8 x FP4 matrix cores
+    for scaled in ((False, True) if w.fmt == "mxfp4" else (False,)):
+        out = kvq.decode_attn(cache, q_t.to(dev), torch.from_numpy(lens.astype(np.int32)).to(dev),
+                              torch.from_numpy(table).to(dev), int(lens.max()), out_dtype=torch.float32,
+                              scaled_mfma=scaled)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        err = parity.attn_row_error(got[sample], ref[sample])
+        print(f"[config] {name}: decode (scaled={scaled}) max row err {err.max():.3e} on sequences {sample}",
+              flush=True)
+        assert err.max() <= parity.ATTN_TOL
 
 
 def test_config_tiny():

@@ -42,7 +42,7 @@ def oracle_cache(rng, lens, hkv, hb, fmt=oracle.FMT_INT4, permute=True, dist="ll
 
 def run_decode(label, pool, table, lens, hq, hb, fmt=oracle.FMT_INT4, q=None, q_dtype="bf16",
                q_scale=1.0, sm_scale=None, out_dtype=torch.float32, rotated=False, seed=0,
-               check=True):
+               check=True, scaled_mfma=False):
     print(f"[decode] {label}", flush=True)
     rng = np.random.default_rng(seed)
     b = len(lens)
@@ -56,7 +56,8 @@ def run_decode(label, pool, table, lens, hq, hb, fmt=oracle.FMT_INT4, q=None, q_
     max_len = int(max(lens))
     out = kvq.decode_attn(cache, q.cuda(), torch.tensor(lens, dtype=torch.int32).cuda(),
                           torch.from_numpy(table).cuda(), max_len, q_scale=q_scale,
-                          sm_scale=sm_scale, out_dtype=out_dtype, rotated=rotated)
+                          sm_scale=sm_scale, out_dtype=out_dtype, rotated=rotated,
+                          scaled_mfma=scaled_mfma)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     if not check:
@@ -188,14 +189,33 @@ def test_dequant_pages(hb):
         assert np.abs(got - ref).max() <= 1e-6 * np.abs(ref).max()
 
 
+@pytest.mark.parametrize("scaled", [False, True])
 @pytest.mark.parametrize("group,q_dtype", [(8, "e4m3"), (8, "bf16"), (4, "bf16"), (1, "f16")])
-def test_decode_mxfp4(group, q_dtype):
+def test_decode_mxfp4(group, q_dtype, scaled):
     rng = np.random.default_rng(60 + group)
     lens = [1, 17, 300, 1000]
     hkv = 2
     pool, table = oracle_cache(rng, lens, hkv, 128, fmt=oracle.FMT_MXFP4)
-    run_decode(f"mxfp4/G{group}/{q_dtype}", pool, table, lens, hkv * group, 128,
-               fmt=oracle.FMT_MXFP4, q_dtype=q_dtype, seed=group)
+    run_decode(f"mxfp4/G{group}/{q_dtype}/scaled={scaled}", pool, table, lens, hkv * group, 128,
+               fmt=oracle.FMT_MXFP4, q_dtype=q_dtype, seed=group, scaled_mfma=scaled)
+
+
+def test_decode_mxfp4_scaled_mfma_matches_f16_path():
+    """The scaled FP8 x FP4 q.K path (q' as three MXFP8 limbs) against the f16-tile path and the
+    oracle on the outlier-heavy workload shape (fp8 queries, G = 8), over several page splits,
+    b = 1 (no rotation) and query magnitudes that push the limb scales to both ends."""
+    rng = np.random.default_rng(63)
+    lens = [4096, 2500, 33, 1]
+    pool, table = oracle_cache(rng, lens, 2, 128, fmt=oracle.FMT_MXFP4)
+    for scale in (1.0, 2.0 ** -20, 2.0 ** 12):
+        q = rng.standard_normal((len(lens), 16, 128)).astype(np.float32)
+        a = run_decode(f"mxfp4/f16 path/q x {scale}", pool, table, lens, 16, 128, fmt=oracle.FMT_MXFP4,
+                       q=q, q_dtype="f32", q_scale=scale, seed=1)
+        c = run_decode(f"mxfp4/scaled/q x {scale}", pool, table, lens, 16, 128, fmt=oracle.FMT_MXFP4,
+                       q=q, q_dtype="f32", q_scale=scale, seed=1, scaled_mfma=True)
+        assert parity.attn_row_error(c, a.astype(np.float64)).max() <= parity.ATTN_TOL
+    pool1, table1 = oracle_cache(rng, [300], 1, 1, fmt=oracle.FMT_MXFP4)
+    run_decode("mxfp4/b1/scaled", pool1, table1, [300], 8, 1, fmt=oracle.FMT_MXFP4, scaled_mfma=True)
 
 
 def test_decode_mxfp4_long_splits_and_no_rotation():

@@ -35,7 +35,8 @@ def _vectors(rng, t, hkv, kv_dtype):
     return k, v
 
 
-def run_step(label, lens, hkv, group, hb, fmt="int4", kv_dtype="bf16", q_dtype="bf16", seed=0):
+def run_step(label, lens, hkv, group, hb, fmt="int4", kv_dtype="bf16", q_dtype="bf16", seed=0,
+             scaled_mfma=False):
     print(f"[step] {label}", flush=True)
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens, np.int64)
@@ -70,7 +71,8 @@ def run_step(label, lens, hkv, group, hb, fmt="int4", kv_dtype="bf16", q_dtype="
 
     cache = kvq.Cache(total, hkv, hb, fmt, pool=torch.from_numpy(pool0).to(dev))
     out = kvq.decode_step(cache, torch.from_numpy(knew).to(TDT[kv_dtype]).to(dev),
-                          torch.from_numpy(vnew).to(TDT[kv_dtype]).to(dev), q_t.to(dev), **args)
+                          torch.from_numpy(vnew).to(TDT[kv_dtype]).to(dev), q_t.to(dev), **args,
+                          scaled_mfma=scaled_mfma)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     gpu_pool = cache.pool.cpu().numpy()
@@ -126,10 +128,11 @@ def test_step_int4_wide_batch():
     run_step("int4/wide", lens, hkv=4, group=4, hb=128, seed=5)
 
 
+@pytest.mark.parametrize("scaled", [False, True])
 @pytest.mark.parametrize("group,q_dtype", [(8, "e4m3"), (1, "bf16")])
-def test_step_mxfp4(group, q_dtype):
-    run_step(f"mxfp4/G{group}", [1, 16, 17, 300, 2000], hkv=2, group=group, hb=128, fmt="mxfp4",
-             q_dtype=q_dtype, seed=60 + group)
+def test_step_mxfp4(group, q_dtype, scaled):
+    run_step(f"mxfp4/G{group}/scaled={scaled}", [1, 16, 17, 300, 2000], hkv=2, group=group, hb=128,
+             fmt="mxfp4", q_dtype=q_dtype, seed=60 + group, scaled_mfma=scaled)
 
 
 def test_step_repeated_calls_grow_the_cache():
