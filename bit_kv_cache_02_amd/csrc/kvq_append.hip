@@ -140,9 +140,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
     const uint8_t* base = src + ((int64_t)(t0 + pos0 - s0) * a.hkv + h) * (int64_t)(kHeadDim * 2);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base, kPage * row_stride);
     const int off = (live && n >= slot_lo && n < slot_hi) ? n * row_stride + 16 * g : kOutOfRange;
+    // default cache policy for the inputs, nontemporal for the page stores below: of the
+    // combinations measured on the prefill append this one is the fastest (~4% over nontemporal
+    // loads with default stores)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      in.x[kb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 64 * kb, 0, 2));
+      in.x[kb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 64 * kb, 0, 0));
     const int q0 = n & ~3;
     const bool partial = is_v && live && q0 + 3 >= slot_lo && q0 < slot_hi && (q0 < slot_lo || q0 + 4 > slot_hi);
     const int voff = partial ? kVCodesOff + 256 * (n >> 2) + 64 * g + 16 * (n & 3) : kOutOfRange;
@@ -276,9 +279,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
       for (int q = 0; q < 4; ++q) out[q] = (out[q] & ~keep) | (in.vold[q] & keep);
       off = keep != 0xFFFFFFFFu ? kVCodesOff + 256 * (n >> 2) + 64 * g + 16 * m : kOutOfRange;
     }
-    __builtin_amdgcn_raw_buffer_store_b128(out, pr, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(out, pr, off, 0, 2);  // 2: nontemporal
     const int poff = (g == 0 && valid) ? (is_v ? kVParamsOff : kKParamsOff) + 4 * n : kOutOfRange;
-    __builtin_amdgcn_raw_buffer_store_b32(param, pr, poff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(param, pr, poff, 0, 2);
   };
 
   // Pages i = 0..npg-1: page i+1 loads while page i is processed.  The loop is unrolled and each
