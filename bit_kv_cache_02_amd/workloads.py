@@ -30,6 +30,7 @@ _TAG_LENS = 7001
 _TAG_PAGES = 7002
 _TAG_OUTLIERS = 7003
 _TAG_QUERY = 7004
+_TAG_QUATERNIONS = 7005
 
 
 @dataclass(frozen=True)
@@ -185,3 +186,15 @@ def small_variant(w: Workload, batch: int, context: int) -> Workload:
     from dataclasses import replace
     return replace(w, name=f"{w.name}-small", batch=batch, context=context,
                    context_range=None, new_tokens=None if w.new_tokens is None else context)
+
+
+def unit_quaternions(seed: int, full: bool = False) -> np.ndarray:
+    """Random unit quaternions (w, x, y, z) for the quaternion block rotation of a 128-vector:
+    fp32[32][4] (one per 4-channel block) or, for ``full``, fp32[32][8] (left then right).
+
+    Uniform on the unit 3-sphere: a 4-vector of independent normals, normalised in fp64, then
+    rounded to fp32 -- the values both the kernels and the oracle receive."""
+    g = _rng(seed, _TAG_QUATERNIONS, int(full)).standard_normal((32, 2 if full else 1, 4))
+    g /= np.linalg.norm(g, axis=-1, keepdims=True)
+    return g.reshape(32, -1).astype(np.float32)
+

@@ -25,6 +25,9 @@ What it computes, and the passages it follows:
 * ``attention`` -- decode attention over the paged cache with the query rotated
   by the same orthogonal transform (inner products are preserved by an
   orthogonal rotation: IsoQuant abstract, "orthogonal feature decorrelation").
+* ``quaternion`` -- the alternative rotation stage: IsoQuant's block-4
+  rotation v -> q_L v conj(q_R) of every 4-channel block (IsoQuant abstract),
+  accepted wherever a Hadamard block width is.
 
 Every floating-point step runs in fp64 unless the method fixes the precision
 (the fp16 scale/zero, the e2m1 grid, the UE8M0 scale).  Functions whose result
@@ -32,7 +35,8 @@ no independent pin checks say "parity unpinned" in their docstring; at present
 there are none.
 """
 
-from .hadamard import sylvester, rotation
+from .hadamard import sylvester, rotation, rotation_matrix
+from .quaternion import hamilton, conj, left_matrix, right_matrix, block_matrix, QuatRotation
 from .int4 import quantize_int4, dequantize_int4
 from .mxfp4 import quantize_mxfp4, dequantize_mxfp4, E2M1_GRID
 from .layout import (PAGE_SIZE, HEAD_DIM, PAGE_HEAD_BYTES, K_CODES_OFF, V_CODES_OFF,
@@ -41,7 +45,8 @@ from .paged import (append, dequant_pages, read_token, FMT_INT4, FMT_MXFP4)
 from .attention import decode_attention, decode_attention_one, prefill_attention
 
 __all__ = [
-    "prefill_attention",
+    "prefill_attention", "rotation_matrix", "hamilton", "conj", "left_matrix", "right_matrix",
+    "block_matrix", "QuatRotation",
     "sylvester", "rotation", "quantize_int4", "dequantize_int4", "quantize_mxfp4",
     "dequantize_mxfp4", "E2M1_GRID", "PAGE_SIZE", "HEAD_DIM", "PAGE_HEAD_BYTES",
     "K_CODES_OFF", "V_CODES_OFF", "K_PARAMS_OFF", "V_PARAMS_OFF", "nibble_position",

@@ -33,7 +33,7 @@ positions 0..p_j -- exactly the decode formula above with seq_len p_j + 1.
 
 import numpy as np
 
-from .hadamard import rotation
+from .hadamard import rotation_matrix
 from .layout import PAGE_SIZE, HEAD_DIM
 from .paged import dequant_block, FMT_INT4
 
@@ -60,7 +60,7 @@ def decode_attention_one(q_heads, k_rot, v_rot, had_block: int, q_scale: float =
     group = hq // hkv
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(HEAD_DIM)
-    r = rotation(had_block, HEAD_DIM)
+    r = rotation_matrix(had_block, HEAD_DIM)
     out = np.empty((hq, HEAD_DIM))
     for h in range(hq):
         g = h // group
@@ -69,7 +69,7 @@ def decode_attention_one(q_heads, k_rot, v_rot, had_block: int, q_scale: float =
         p = np.exp(s - s.max())
         p /= p.sum()
         o_rot = p @ v_rot[g]
-        out[h] = o_rot if out_rotated else r @ o_rot
+        out[h] = o_rot if out_rotated else r.T @ o_rot
     return out
 
 

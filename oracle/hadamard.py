@@ -44,3 +44,13 @@ def rotation(had_block: int, dim: int = 128) -> np.ndarray:
     for start in range(0, dim, had_block):
         r[start:start + had_block, start:start + had_block] = blk
     return r
+
+
+def rotation_matrix(rot, dim: int = 128) -> np.ndarray:
+    """The rotation R (y = R x) named by ``rot``: a Hadamard block width (int) or an object
+    with a ``matrix()`` method (the quaternion block rotation).  R is orthogonal; only the
+    Hadamard one is also symmetric, so the way back is R^T."""
+    if isinstance(rot, (int, np.integer)):
+        return rotation(int(rot), dim)
+    return rot.matrix()
+

@@ -16,7 +16,7 @@ Only the bytes of the appended slots are written.
 
 import numpy as np
 
-from .hadamard import rotation
+from .hadamard import rotation_matrix
 from .int4 import quantize_int4, dequantize_int4
 from .mxfp4 import quantize_mxfp4, dequantize_mxfp4
 from .layout import (PAGE_SIZE, HEAD_DIM, K_PARAMS_OFF, V_PARAMS_OFF, pack_row,
@@ -32,7 +32,7 @@ def encode(x: np.ndarray, had_block: int, fmt: int):
     Returns (row_bytes uint8[..., 64], param_bytes uint8[..., 4], info) where
     ``info`` holds the intermediate values the parity rules need.
     """
-    r = rotation(had_block, HEAD_DIM)
+    r = rotation_matrix(had_block, HEAD_DIM)
     y = np.asarray(x, dtype=np.float64) @ r.T
     if fmt == FMT_INT4:
         codes, s16, z16, delta = quantize_int4(y)
@@ -41,7 +41,7 @@ def encode(x: np.ndarray, had_block: int, fmt: int):
              z16.astype("<f2").view(np.uint8).reshape(z16.shape + (2,))], axis=-1)
         info = {"y": y, "codes": codes, "s16": s16, "z16": z16, "delta": delta}
     elif fmt == FMT_MXFP4:
-        if had_block not in (1, 128):
+        if isinstance(had_block, (int, np.integer)) and had_block not in (1, 128):
             raise ValueError("MXFP4 uses the full 128-wide rotation (or none, for tests)")
         codes, e, rr = quantize_mxfp4(y)
         params = e.astype(np.uint8)
@@ -116,18 +116,18 @@ def dequant_pages(pool, page_ids, had_block: int, fmt: int = FMT_INT4, unrotate:
     """Dequantize whole pages: returns (k, v) fp64[n][Hkv][16][128].
 
     In the rotated basis by default; with ``unrotate`` the rotation is undone
-    (R_b is symmetric and orthogonal, so x^ = R_b y^).
+    (R is orthogonal, so x^ = R^T y^; R_b is also symmetric).
     """
     page_ids = np.asarray(page_ids, dtype=np.int64)
     hkv = pool.shape[1]
     out = {}
-    r = rotation(had_block, HEAD_DIM)
+    r = rotation_matrix(had_block, HEAD_DIM)
     for which in ("k", "v"):
         vals = np.empty((len(page_ids), hkv, PAGE_SIZE, HEAD_DIM), dtype=np.float64)
         for n, p in enumerate(page_ids):
             for h in range(hkv):
                 vals[n, h] = dequant_block(pool[p, h], which, fmt)
         if unrotate:
-            vals = vals @ r.T
+            vals = vals @ r  # rows: (R^T y)^T = y^T R
         out[which] = vals
     return out["k"], out["v"]
