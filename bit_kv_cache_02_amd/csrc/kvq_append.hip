@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
       for (int half = 0; half < 2; ++half) {
         const int k = 8 * g + 2 * w + half;
         uint16_t vp, vm;
-        if (HB == 1) {
+        if (HB == 1 || HB == kQuatBlock) {
           vp = (k == 16 * p + n) ? Sign<BF16>::kPlus : 0;
           vm = vp;
         } else {
@@ -115,6 +115,23 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
       tp[p][w] = word_p;
       tm[p][w] = word_m;
     }
+  }
+
+  // quaternion block rotation: each wave stages the 32 block matrices in its own LDS slice (lane
+  // k < 32 builds block k), so no workgroup barrier is needed after the early exits above
+  __shared__ __attribute__((aligned(16))) float qm[HB == kQuatBlock ? 4 : 1][HB == kQuatBlock ? kHeadDim / 4 : 1][4][4];
+  if constexpr (HB == kQuatBlock) {
+    if (lane < kHeadDim / 4) {
+      float c[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        quat_coeffs(a.quat, a.quat_full, lane, r, false, c);
+        *(f32x4*)&qm[wave][lane][r][0] = f32x4{c[0], c[1], c[2], c[3]};
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
   const uint8_t* src = is_v ? a.v : a.k;
@@ -184,7 +201,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
         }
       }
     }
-    // acc[nb][r] = sqrt(b) * y[slot n][channel 16*nb + 4*g + r]
+    if constexpr (HB == kQuatBlock) {
+      // acc[nb] holds channels 16nb + 4g .. +3 of slot n: block 4nb + g, rotated in fp32
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const f32x4 x = acc[nb];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 m = *(const f32x4*)&qm[wave][4 * nb + g][r][0];
+          acc[nb][r] = fmaf(m[3], x[3], fmaf(m[2], x[2], fmaf(m[1], x[1], m[0] * x[0])));
+        }
+      }
+    }
+    // acc[nb][r] = sqrt(b) * y[slot n][channel 16*nb + 4*g + r]  (b = 1: no Hadamard)
     constexpr float isb = HB == 128 ? 0.08838834764831845f : (HB == 64 ? 0.125f : 1.0f);
 
     uint32_t row[4];   // K row words 4g + r of slot n
@@ -322,6 +351,10 @@ hipError_t launch_append(const AppendParams& p, bool bf16, int had_block, int fm
   KVQ_APPEND_CASE(true, 1, 1)
   KVQ_APPEND_CASE(false, 128, 1)
   KVQ_APPEND_CASE(false, 1, 1)
+  KVQ_APPEND_CASE(true, kQuatBlock, 0)
+  KVQ_APPEND_CASE(false, kQuatBlock, 0)
+  KVQ_APPEND_CASE(true, kQuatBlock, 1)
+  KVQ_APPEND_CASE(false, kQuatBlock, 1)
 #undef KVQ_APPEND_CASE
   return hipErrorInvalidValue;
 }

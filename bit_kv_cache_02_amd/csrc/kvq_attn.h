@@ -61,6 +61,67 @@ __device__ __forceinline__ void fwht_rows(float (&x0)[R], float (&x1)[R], int hb
   }
 }
 
+// The quaternion block rotation of one 128-vector held by a wave (element lane in x0, lane + 64
+// in x1): the four lanes of a quad hold one 4-channel block.  inverse: the transpose.
+__device__ __forceinline__ void quat_wave(float& x0, float& x1, const float* quat, int full, int lane,
+                                          bool inverse) {
+  float c0[4], c1[4];
+  quat_coeffs(quat, full, lane >> 2, lane & 3, inverse, c0);
+  quat_coeffs(quat, full, 16 + (lane >> 2), lane & 3, inverse, c1);
+  x0 = quat_apply_quad(x0, c0);
+  x1 = quat_apply_quad(x1, c1);
+}
+
+// y = R x for the cache's rotation (normalised Hadamard of width hb, or the quaternion block
+// rotation when hb is kQuatBlock), wave layout as above.
+__device__ __forceinline__ void rotate_wave(float& x0, float& x1, int hb, const float* quat, int full, int lane) {
+  if (hb == kQuatBlock) {
+    quat_wave(x0, x1, quat, full, lane, false);
+    return;
+  }
+  fwht_wave(x0, x1, hb, lane);
+  const float isb = inv_sqrt_block(hb);
+  x0 *= isb;
+  x1 *= isb;
+}
+
+// x = R^T y (R_b is symmetric)
+__device__ __forceinline__ void unrotate_wave(float& x0, float& x1, int hb, const float* quat, int full,
+                                              int lane) {
+  if (hb == kQuatBlock) {
+    quat_wave(x0, x1, quat, full, lane, true);
+    return;
+  }
+  fwht_wave(x0, x1, hb, lane);
+  const float isb = inv_sqrt_block(hb);
+  x0 *= isb;
+  x1 *= isb;
+}
+
+// Rows r = 0..R-1 at once (x0[r], x1[r]); the coefficients are shared by the rows.
+template <int R>
+__device__ __forceinline__ void rotate_rows(float (&x0)[R], float (&x1)[R], int hb, const float* quat, int full,
+                                            int lane, bool inverse) {
+  if (hb == kQuatBlock) {
+    float c0[4], c1[4];
+    quat_coeffs(quat, full, lane >> 2, lane & 3, inverse, c0);
+    quat_coeffs(quat, full, 16 + (lane >> 2), lane & 3, inverse, c1);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      x0[r] = quat_apply_quad(x0[r], c0);
+      x1[r] = quat_apply_quad(x1[r], c1);
+    }
+    return;
+  }
+  fwht_rows<R>(x0, x1, hb, lane);
+  const float isb = inv_sqrt_block(hb);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    x0[r] *= isb;
+    x1[r] *= isb;
+  }
+}
+
 template <int FMT>
 struct PageData {
   u32x4 k;      // K row bytes 16*jg..16*jg+15 of token n
@@ -414,15 +475,11 @@ __device__ __forceinline__ void process_page_mx_scaled(const PageData<1>& pg, in
 // Rotate one row's normalised o' (element lane in o0, lane + 64 in o1) back and store it at
 // row `row` of a [rows][128] output of dtype `out_dtype`.
 __device__ __forceinline__ void store_row(void* out, int64_t row, int out_dtype, int rotated, int had_block,
-                                          float o0, float o1, int lane) {
-  float scale = 1.0f;
-  if (!rotated) {
-    fwht_wave(o0, o1, had_block, lane);
-    scale = inv_sqrt_block(had_block);
-  }
+                                          const float* quat, int quat_full, float o0, float o1, int lane) {
+  if (!rotated) unrotate_wave(o0, o1, had_block, quat, quat_full, lane);
   const int64_t base = row * kHeadDim;
-  store_elem(out, base + lane, out_dtype, o0 * scale);
-  store_elem(out, base + lane + 64, out_dtype, o1 * scale);
+  store_elem(out, base + lane, out_dtype, o0);
+  store_elem(out, base + lane + 64, out_dtype, o1);
 }
 
 }  // namespace attn

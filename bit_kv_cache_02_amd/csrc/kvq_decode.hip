@@ -87,7 +87,8 @@ __device__ __forceinline__ void patch_appended(PageData<FMT>& pg, const uint32_t
 
 // Rotate one head's normalised o' (element lane in o0, lane + 64 in o1) back and store it.
 __device__ __forceinline__ void store_head(const DecodeParams& a, float o0, float o1, int b, int h, int lane) {
-  store_row(a.out, (int64_t)b * a.hq + h, a.out_dtype, a.out_rotated, a.had_block, o0, o1, lane);
+  store_row(a.out, (int64_t)b * a.hq + h, a.out_dtype, a.out_rotated, a.had_block, a.quat, a.quat_full, o0, o1,
+            lane);
 }
 
 }  // namespace
@@ -111,7 +112,6 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   const int kvh = unit % a.hkv;
   const int b = unit / a.hkv;
   const int G = a.group;
-  const float isb = inv_sqrt_block(a.had_block);
   const int n = lane & 15;   // token (QK, softmax) / output column (p.V)
   const int jg = lane >> 4;  // row group: heads 2jg, 2jg+1
 
@@ -206,9 +206,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
     const int g = wave + k * W;
     if (g < G) {
       float v0 = qv[k][0], v1 = qv[k][1];
-      fwht_wave(v0, v1, a.had_block, lane);
-      v0 *= isb;
-      v1 *= isb;
+      rotate_wave(v0, v1, a.had_block, a.quat, a.quat_full, lane);
       if constexpr (FMT == 2) {
         mxfp8_limbs(v0, v1, g, lane, sm.q8, sm.q8s);
         continue;
@@ -252,9 +250,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   uint32_t app_word = 0, app_byte = 0, app_param = 0;
   if (app_wave) {
     float x0 = raw_to_f32(nword[0] >> nshift[0], a.kv_dtype), x1 = raw_to_f32(nword[1] >> nshift[1], a.kv_dtype);
-    fwht_wave(x0, x1, a.had_block, lane);
-    x0 *= isb;
-    x1 *= isb;
+    rotate_wave(x0, x1, a.had_block, a.quat, a.quat_full, lane);
     uint32_t c0, c1;
     if constexpr (FMT == 0) {
       const float lo = -wave_max(-fminf(x0, x1)), hi = wave_max(fmaxf(x0, x1));

@@ -3,8 +3,9 @@
 //   INT4   y^ = fma(scale, code, zero): a single rounding of the exact value (token-wise INT4 with an
 //          fp16 scale and zero, SAW-INT4 summary, "Summary"/"Method").
 //   MXFP4  y^ = e2m1(code) * 2^(E-127), exact (FP4 with UE8M0 group scales, UltraQuant article).
-// With KVQ_UNROTATE the rotation is undone: x^ = R_b y^ (R_b symmetric orthogonal), by an fp32
-// Walsh-Hadamard butterfly in LDS.
+// With KVQ_UNROTATE the rotation is undone, x^ = R^T y^: for R_b (symmetric) by an fp32
+// Walsh-Hadamard butterfly in LDS, for the quaternion block rotation by the transposed 4 x 4
+// block matrices (IsoQuant abstract), staged in LDS.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -25,6 +26,7 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
 // each thread owns channels a + 32q + 16e (q = 0..3, e = 0..1) of slot s, i.e. row bytes 4a..4a+3.
 __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   __shared__ float buf[2][kPage][kHeadDim];
+  __shared__ float qm[kHeadDim / 4][4][4];  // quaternion block matrices
   const int tid = thread_id();
   const int s = tid >> 4, col = tid & 15;
   const int i = block_id_x() / p.hkv, h = block_id_x() % p.hkv;
@@ -53,9 +55,31 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
       }
     }
   }
+  if (p.unrotate && p.had_block == kQuatBlock && tid < kHeadDim / 4) {
+    float c[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      quat_coeffs(p.quat, p.quat_full, tid, r, false, c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qm[tid][r][j] = c[j];
+    }
+  }
   __syncthreads();
   float scale = 1.0f;
-  if (p.unrotate && p.had_block > 1) {
+  if (p.unrotate && p.had_block == kQuatBlock) {
+    // x_c = sum_j M[j][c mod 4] y_(4 (c/4) + j) of block c/4; results go to registers first
+    float x[2][kPage * kHeadDim / 256];
+    for (int which = 0; which < 2; ++which)
+      for (int k = tid, n = 0; k < kPage * kHeadDim; k += 256, ++n) {
+        const int row = k >> 7, ch = k & 127, blk = ch >> 2, r = ch & 3;
+        const float* y = &buf[which][row][4 * blk];
+        x[which][n] = fmaf(qm[blk][3][r], y[3], fmaf(qm[blk][2][r], y[2], fmaf(qm[blk][1][r], y[1], qm[blk][0][r] * y[0])));
+      }
+    __syncthreads();
+    for (int which = 0; which < 2; ++which)
+      for (int k = tid, n = 0; k < kPage * kHeadDim; k += 256, ++n) (&buf[which][0][0])[k] = x[which][n];
+    __syncthreads();
+  } else if (p.unrotate && p.had_block > 1) {
     for (int len = 1; len < p.had_block; len <<= 1) {
       for (int k = tid; k < 2 * kPage * 64; k += 256) {
         const int row = k >> 6, kk = k & 63;

@@ -78,6 +78,66 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
+// ---- quaternion block rotation (IsoQuant abstract: a 4-channel block v -> qL v conj(qR)) ----
+// Rotation codes carried in the kernels' had_block argument besides the Hadamard widths.
+constexpr int kQuatBlock = 4;
+
+// M = L(a) R(conj(b)), where L(a) v = a v and R(c) v = v c are the Hamilton products of
+// quaternions (w, x, y, z); b = 1 (IsoQuant-Fast) leaves M = L(a).
+__device__ __forceinline__ void quat_matrix(const float (&a)[4], const float (&b)[4], float (&m)[4][4]) {
+  const float l[4][4] = {{a[0], -a[1], -a[2], -a[3]},
+                         {a[1], a[0], -a[3], a[2]},
+                         {a[2], a[3], a[0], -a[1]},
+                         {a[3], -a[2], a[1], a[0]}};
+  const float c0 = b[0], c1 = -b[1], c2 = -b[2], c3 = -b[3];
+  const float r[4][4] = {{c0, -c1, -c2, -c3}, {c1, c0, c3, -c2}, {c2, -c3, c0, c1}, {c3, c2, -c1, c0}};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      m[i][j] = fmaf(l[i][3], r[3][j], fmaf(l[i][2], r[2][j], fmaf(l[i][1], r[1][j], l[i][0] * r[0][j])));
+}
+
+// The coefficients with which channel r of 4-channel block `block` is formed from the block's
+// four inputs: row r of M (forward, y = M x) or column r (inverse, x = M^T y).  `quat` holds
+// q_L per block ([32][4], IsoQuant-Fast) or q_L then q_R ([32][8], IsoQuant-Full).
+__device__ __forceinline__ void quat_coeffs(const float* quat, int full, int block, int r, bool inverse,
+                                            float (&c)[4]) {
+  const float* q = quat + block * (full ? 8 : 4);
+  const float a[4] = {q[0], q[1], q[2], q[3]};
+  float b[4] = {1.0f, 0.0f, 0.0f, 0.0f};
+  if (full) {
+    b[0] = q[4];
+    b[1] = q[5];
+    b[2] = q[6];
+    b[3] = q[7];
+  }
+  float m[4][4];
+  quat_matrix(a, b, m);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c[j] = m[0][j];
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (i == r) c[j] = m[i][j];
+  if (inverse) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = m[j][0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) c[j] = i == r ? m[j][i] : c[j];
+    }
+  }
+}
+
+// One 4-channel block held by the four lanes of a DPP quad (lane 4m + r holds channel r):
+// channel r of the result = sum_j c[j] * (channel j of the input).
+__device__ __forceinline__ float quat_apply_quad(float x, const float (&c)[4]) {
+  const float g0 = dpp_f<0x00>(x), g1 = dpp_f<0x55>(x), g2 = dpp_f<0xAA>(x), g3 = dpp_f<0xFF>(x);
+  return fmaf(c[3], g3, fmaf(c[2], g2, fmaf(c[1], g1, c[0] * g0)));
+}
+
 // ---- scalar conversions ----
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h16) {

@@ -36,15 +36,23 @@ int check_cache(const kvq_cache* c) {
   // the kernels address a page's 16 token rows through one 32-bit buffer range
   if (c->num_kv_heads > 1024) return fail(KVQ_ERR_UNSUPPORTED, "num_kv_heads %d above 1024", c->num_kv_heads);
   if (c->num_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "num_pages must be >= 1");
-  if (c->reserved != 0) return fail(KVQ_ERR_INVALID_ARG, "cache->reserved must be 0");
+
   if (c->head_dim != KVQ_HEAD_DIM) return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", c->head_dim);
   if (c->page_size != KVQ_PAGE_SIZE) return fail(KVQ_ERR_UNSUPPORTED, "page_size %d unsupported (only 16)", c->page_size);
   if (c->format != KVQ_FMT_INT4_TOKEN && c->format != KVQ_FMT_MXFP4_G32)
     return fail(KVQ_ERR_UNSUPPORTED, "format %d unknown", c->format);
-  if (c->had_block != 1 && c->had_block != 64 && c->had_block != 128)
-    return fail(KVQ_ERR_UNSUPPORTED, "had_block %d unsupported (1, 64 or 128)", c->had_block);
+  if (c->had_block != 1 && c->had_block != KVQ_ROT_QUAT4 && c->had_block != 64 && c->had_block != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "had_block %d unsupported (1, 4, 64 or 128)", c->had_block);
   if (c->format == KVQ_FMT_MXFP4_G32 && c->had_block == 64)
-    return fail(KVQ_ERR_UNSUPPORTED, "MXFP4 uses the full 128-wide rotation (had_block 128, or 1 for tests)");
+    return fail(KVQ_ERR_UNSUPPORTED, "MXFP4 takes had_block 128 or 4 (or 1, for tests)");
+  if (c->had_block == KVQ_ROT_QUAT4) {
+    if (!c->quat) return fail(KVQ_ERR_INVALID_ARG, "had_block 4 needs cache->quat");
+    if (((uintptr_t)c->quat) & 15) return fail(KVQ_ERR_INVALID_ARG, "cache->quat must be 16-byte aligned");
+    if (c->quat_full != 0 && c->quat_full != 1) return fail(KVQ_ERR_INVALID_ARG, "cache->quat_full must be 0 or 1");
+  } else {
+    if (c->quat_full != 0) return fail(KVQ_ERR_INVALID_ARG, "cache->quat_full must be 0 unless had_block is 4");
+    if (c->quat) return fail(KVQ_ERR_INVALID_ARG, "cache->quat must be NULL unless had_block is 4");
+  }
   if (((uintptr_t)c->pool) & 15) return fail(KVQ_ERR_INVALID_ARG, "pool must be 16-byte aligned");
   return KVQ_OK;
 }
@@ -101,6 +109,8 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t kv_
   p.num_seqs = num_seqs;
   p.max_pages = max_pages;
   p.max_new = max_new_tokens;
+  p.quat = cache->quat;
+  p.quat_full = cache->quat_full;
   return hip_status(kvq::launch_append(p, kv_dtype == KVQ_BF16, cache->had_block, cache->format, (hipStream_t)stream),
                     "kvq_append launch");
 }
@@ -177,6 +187,8 @@ static int decode_common(const kvq_cache* cache, const void* knew, const void* v
   p.num_seqs = num_seqs;
   p.max_pages = max_pages;
   p.had_block = cache->had_block;
+  p.quat = cache->quat;
+  p.quat_full = cache->quat_full;
   p.q_dtype = q_dtype;
   p.out_dtype = out_dtype;
   p.out_rotated = (flags & KVQ_OUT_ROTATED) ? 1 : 0;
@@ -259,6 +271,8 @@ int kvq_prefill_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, flo
   p.num_tokens = num_tokens;
   p.max_pages = max_pages;
   p.had_block = cache->had_block;
+  p.quat = cache->quat;
+  p.quat_full = cache->quat_full;
   p.q_dtype = q_dtype;
   p.out_dtype = out_dtype;
   p.out_rotated = (flags & KVQ_OUT_ROTATED) ? 1 : 0;
@@ -286,6 +300,8 @@ int kvq_dequant_page(const kvq_cache* cache, const int32_t* page_ids, int32_t n,
   p.n = n;
   p.hkv = cache->num_kv_heads;
   p.had_block = cache->had_block;
+  p.quat = cache->quat;
+  p.quat_full = cache->quat_full;
   p.unrotate = (flags & KVQ_UNROTATE) ? 1 : 0;
   p.fmt = cache->format;
   return hip_status(kvq::launch_dequant(p, (hipStream_t)stream), "kvq_dequant_page launch");

@@ -20,6 +20,8 @@ struct AppendParams {
   int32_t num_seqs;
   int32_t max_pages;
   int32_t max_new;
+  const float* quat;   // had_block 4: unit quaternions [32][4] or [32][8] (quat_full)
+  int32_t quat_full;
 };
 
 struct DecodePlan {
@@ -42,7 +44,9 @@ struct DecodeParams {
   int32_t hq;
   int32_t num_seqs;
   int32_t max_pages;
-  int32_t had_block;
+  int32_t had_block;  // 1, 64, 128: Hadamard block width; 4: quaternion block rotation
+  const float* quat;
+  int32_t quat_full;
   int32_t q_dtype;
   int32_t out_dtype;
   int32_t out_rotated;
@@ -70,7 +74,9 @@ struct PrefillParams {
   int32_t num_seqs;
   int32_t num_tokens;
   int32_t max_pages;
-  int32_t had_block;
+  int32_t had_block;  // 1, 64, 128: Hadamard block width; 4: quaternion block rotation
+  const float* quat;
+  int32_t quat_full;
   int32_t q_dtype;
   int32_t out_dtype;
   int32_t out_rotated;
@@ -86,7 +92,9 @@ struct DequantParams {
   float* out_v;
   int32_t n;
   int32_t hkv;
-  int32_t had_block;
+  int32_t had_block;  // 1, 64, 128: Hadamard block width; 4: quaternion block rotation
+  const float* quat;
+  int32_t quat_full;
   int32_t unrotate;
   int32_t fmt;
 };

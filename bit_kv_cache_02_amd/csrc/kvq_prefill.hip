@@ -53,7 +53,6 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
   const int units = a.num_seqs * a.hkv;
   const int tile = block_id_x() / units, unit = block_id_x() % units;  // tile-major order
   const int kvh = unit % a.hkv, b = unit / a.hkv;
-  const float isb = inv_sqrt_block(a.had_block);
 
   const int qbeg = a.cu_q[b], nq = a.cu_q[b + 1] - qbeg;
   const int L = a.seq_lens[b];
@@ -102,11 +101,9 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
       v0[r] = raw_to_f32(qword[r][0] >> qshift[r][0], a.q_dtype) * a.q_scale;
       v1[r] = raw_to_f32(qword[r][1] >> qshift[r][1], a.q_dtype) * a.q_scale;
     }
-    fwht_rows<kRows>(v0, v1, a.had_block, lane);
+    rotate_rows<kRows>(v0, v1, a.had_block, a.quat, a.quat_full, lane, false);
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-      v0[r] *= isb;
-      v1[r] *= isb;
       if constexpr (FMT == 1) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -225,18 +222,14 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
     o0[r] = sm.wo[wave][r][lane];
     o1[r] = sm.wo[wave][r][lane + 64];
   }
-  float scale = 1.0f;
-  if (!a.out_rotated) {
-    fwht_rows<kRows>(o0, o1, a.had_block, lane);
-    scale = isb;
-  }
+  if (!a.out_rotated) rotate_rows<kRows>(o0, o1, a.had_block, a.quat, a.quat_full, lane, true);
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
     const int t = tw0 + r / G;
     if (t < nq) {
       const int64_t base = ((int64_t)(qbeg + t) * a.hq + kvh * G + r % G) * kHeadDim;
-      store_elem(a.out, base + lane, a.out_dtype, o0[r] * scale);
-      store_elem(a.out, base + lane + 64, a.out_dtype, o1[r] * scale);
+      store_elem(a.out, base + lane, a.out_dtype, o0[r]);
+      store_elem(a.out, base + lane + 64, a.out_dtype, o1[r]);
     }
   }
 }

@@ -20,6 +20,7 @@ KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP
 FMT_INT4, FMT_MXFP4 = 0, 1
 F16, BF16, F32, FP8_E4M3 = 0, 1, 2, 3
 OUT_ROTATED = 1
+ROT_QUAT4 = 4
 MX_SCALED_MFMA = 2
 UNROTATE = 1
 HEAD_DIM = 128
@@ -34,8 +35,8 @@ _FMT_CODE = {"int4": FMT_INT4, "mxfp4": FMT_MXFP4}
 class KvqCacheDesc(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("had_block", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("num_pages", ctypes.c_int64), ("pool", ctypes.c_void_p)]
+                ("had_block", ctypes.c_int32), ("quat_full", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64), ("pool", ctypes.c_void_p), ("quat", ctypes.c_void_p)]
 
 
 class KvqError(RuntimeError):
@@ -118,7 +119,17 @@ class Cache:
     """One layer's paged 4-bit cache: a caller-owned uint8 pool [num_pages][Hkv][2176]."""
 
     def __init__(self, num_pages: int, num_kv_heads: int, had_block: int, fmt: str = "int4",
-                 device="cuda", pool: Optional[torch.Tensor] = None, fill: Optional[int] = None):
+                 device="cuda", pool: Optional[torch.Tensor] = None, fill: Optional[int] = None,
+                 quat: Optional[torch.Tensor] = None):
+        """had_block: Hadamard block width (1, 64, 128) or ROT_QUAT4 with ``quat``, the unit
+        quaternions of the block-4 rotation: float32 [32][4] (IsoQuant-Fast) or [32][8]
+        (IsoQuant-Full), on the pool's device."""
+        if (had_block == ROT_QUAT4) != (quat is not None):
+            raise ValueError("quat is given exactly when had_block is 4")
+        if quat is not None and (quat.dtype != torch.float32 or tuple(quat.shape) not in ((32, 4), (32, 8))
+                                 or not quat.is_contiguous()):
+            raise ValueError("quat must be a contiguous float32 [32][4] or [32][8] tensor")
+        self.quat = quat
         self.fmt = fmt
         self.num_kv_heads = num_kv_heads
         self.had_block = had_block
@@ -133,8 +144,10 @@ class Cache:
         self.pool = pool
 
     def desc(self) -> KvqCacheDesc:
+        full = 1 if self.quat is not None and self.quat.shape[1] == 8 else 0
         return KvqCacheDesc(_FMT_CODE[self.fmt], self.num_kv_heads, HEAD_DIM, PAGE_SIZE,
-                            self.had_block, 0, self.num_pages, self.pool.data_ptr())
+                            self.had_block, full, self.num_pages, self.pool.data_ptr(),
+                            None if self.quat is None else self.quat.data_ptr())
 
 
 def abi_version() -> int:

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 #define KVQ_HEAD_DIM 128
 #define KVQ_PAGE_SIZE 16
 #define KVQ_PAGE_HEAD_BYTES 2176
@@ -76,12 +76,22 @@ typedef struct {
   int32_t num_kv_heads; /* >= 1                                                           */
   int32_t head_dim;     /* must be 128                                                    */
   int32_t page_size;    /* must be 16                                                     */
-  int32_t had_block;    /* Hadamard block width b: 1 (no rotation, "plain INT4"), 64, 128 */
-                        /* MXFP4 requires 128 (or 1, for tests)                            */
-  int32_t reserved;     /* must be 0                                                      */
+  int32_t had_block;    /* rotation before quantizing: Walsh-Hadamard block width b = 1   */
+                        /* (no rotation, "plain INT4"), 64 or 128; or KVQ_ROT_QUAT4 (4):  */
+                        /* the quaternion block-4 rotation below.  MXFP4 takes 128, 4, or */
+                        /* 1 (for tests).                                                 */
+  int32_t quat_full;    /* had_block 4: 0 = IsoQuant-Fast, 1 = IsoQuant-Full; else 0       */
   int64_t num_pages;    /* pages in the pool                                              */
   void* pool;           /* device uint8[num_pages][num_kv_heads][2176], 16-byte aligned   */
+  const float* quat;    /* had_block 4: device fp32 unit quaternions (w, x, y, z), 16-byte */
+                        /* aligned: [32][4] q_L (Fast) or [32][8] q_L, q_R (Full); else   */
+                        /* NULL.  Channels 4k..4k+3 of a vector, as the quaternion v, are */
+                        /* rotated to q_L v conj(q_R) (IsoQuant abstract: the isoclinic   */
+                        /* decomposition of SO(4); Fast keeps the left factor, q_R = 1);  */
+                        /* the way back is the transpose.  The caller draws them.         */
 } kvq_cache;
+
+#define KVQ_ROT_QUAT4 4
 
 /* Version of this ABI (KVQ_ABI_VERSION). */
 int kvq_abi_version(void);

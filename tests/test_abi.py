@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from bit_kv_cache_02_amd import kvq
 
@@ -32,8 +33,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_sizes():
-    assert kvq.abi_version() == 1
-    d = kvq.KvqCacheDesc(0, 8, 128, 16, 128, 0, 10, 4096)
+    assert kvq.abi_version() == 2
+    d = kvq.KvqCacheDesc(0, 8, 128, 16, 128, 0, 10, 4096, None)
     assert kvq.lib().kvq_page_bytes(ctypes.byref(d)) == 8 * 2176
     assert kvq.lib().kvq_page_bytes(None) == 0
     for s in (0, -1, -2, -3, -4, 7):
@@ -41,8 +42,8 @@ def test_version_and_sizes():
 
 
 def _desc(**kw):
-    base = dict(format=0, num_kv_heads=2, head_dim=128, page_size=16, had_block=64, reserved=0,
-                num_pages=8, pool=4096)
+    base = dict(format=0, num_kv_heads=2, head_dim=128, page_size=16, had_block=64, quat_full=0,
+                num_pages=8, pool=4096, quat=None)
     base.update(kw)
     return kvq.KvqCacheDesc(*[base[f] for f, _ in kvq.KvqCacheDesc._fields_])
 
@@ -64,11 +65,38 @@ def _append(desc, **kw):
     ("num_pages", 0, kvq.KVQ_ERR_INVALID_ARG),
     ("pool", None, kvq.KVQ_ERR_INVALID_ARG),
     ("pool", 4097, kvq.KVQ_ERR_INVALID_ARG),
-    ("reserved", 1, kvq.KVQ_ERR_INVALID_ARG),
+    ("quat_full", 1, kvq.KVQ_ERR_INVALID_ARG),       # only with the quaternion rotation
+    ("quat", 4096, kvq.KVQ_ERR_INVALID_ARG),         # likewise
+    ("had_block", 2, kvq.KVQ_ERR_UNSUPPORTED),
 ])
 def test_append_rejects_bad_cache(field, value, status):
     assert _append(_desc(**{field: value})) == status
     assert kvq.lib().kvq_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(quat=None), kvq.KVQ_ERR_INVALID_ARG),      # had_block 4 needs the quaternions
+    (dict(quat=4100), kvq.KVQ_ERR_INVALID_ARG),      # 16-byte aligned
+    (dict(quat_full=2), kvq.KVQ_ERR_INVALID_ARG),
+])
+def test_quaternion_rotation_rejects_bad_cache(kw, status):
+    base = dict(had_block=kvq.ROT_QUAT4, quat=8192)
+    base.update(kw)
+    assert _append(_desc(**base)) == status
+    assert _decode(_desc(**base)) == status
+    # a valid quaternion cache passes the cache checks (then fails on a NULL argument)
+    assert _append(_desc(had_block=kvq.ROT_QUAT4, quat=8192, quat_full=1), k=None) == kvq.KVQ_ERR_INVALID_ARG
+    assert _append(_desc(format=1, had_block=kvq.ROT_QUAT4, quat=8192), k=None) == kvq.KVQ_ERR_INVALID_ARG
+
+
+def test_cache_object_checks_quaternions():
+    with pytest.raises(ValueError):
+        kvq.Cache(4, 1, kvq.ROT_QUAT4, pool=torch.zeros((4, 1, 2176), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        kvq.Cache(4, 1, kvq.ROT_QUAT4, pool=torch.zeros((4, 1, 2176), dtype=torch.uint8),
+                  quat=torch.zeros((32, 5)))
+    with pytest.raises(ValueError):
+        kvq.Cache(4, 1, 64, pool=torch.zeros((4, 1, 2176), dtype=torch.uint8), quat=torch.zeros((32, 4)))
 
 
 def test_mxfp4_needs_full_rotation():

@@ -24,7 +24,9 @@ def run_append(label, k, v, lens_new, start, table, num_pages, hkv, hb, fmt, dty
         pool_o = np.full((num_pages, hkv, 2176), SENT, np.uint8)
     infos = oracle.append(pool_o, k, v, cu, start, table, hb, fmt)
     if cache is None:
-        cache = kvq.Cache(num_pages, hkv, hb, "int4" if fmt == oracle.FMT_INT4 else "mxfp4", fill=SENT)
+        khb, quat = parity.kernel_rotation(hb)
+        cache = kvq.Cache(num_pages, hkv, khb, "int4" if fmt == oracle.FMT_INT4 else "mxfp4", fill=SENT,
+                          quat=quat)
     kt = torch.from_numpy(np.ascontiguousarray(k, np.float32)).to(TDT[dtype]).cuda()
     vt = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(TDT[dtype]).cuda()
     kvq.append(cache, kt, vt, torch.from_numpy(cu).cuda(), torch.from_numpy(start).cuda(),

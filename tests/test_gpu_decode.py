@@ -51,8 +51,9 @@ def run_decode(label, pool, table, lens, hq, hb, fmt=oracle.FMT_INT4, q=None, q_
     q = torch.from_numpy(q).to(QDT[q_dtype])
     qnp = q.float().numpy()
     hkv = pool.shape[1]
-    cache = kvq.Cache(pool.shape[0], hkv, hb, "int4" if fmt == oracle.FMT_INT4 else "mxfp4",
-                      pool=torch.from_numpy(pool).cuda())
+    khb, quat = parity.kernel_rotation(hb)
+    cache = kvq.Cache(pool.shape[0], hkv, khb, "int4" if fmt == oracle.FMT_INT4 else "mxfp4",
+                      pool=torch.from_numpy(pool).cuda(), quat=quat)
     max_len = int(max(lens))
     out = kvq.decode_attn(cache, q.cuda(), torch.tensor(lens, dtype=torch.int32).cuda(),
                           torch.from_numpy(table).cuda(), max_len, q_scale=q_scale,

@@ -25,7 +25,8 @@ def run_prefill(label, lens, chunks, hkv, group, hb, fmt=oracle.FMT_INT4, q_dtyp
     q = rng.standard_normal((int(cu_q[-1]), hkv * group, 128)).astype(np.float32)
     q_t = torch.from_numpy(q).to(QDT[q_dtype])
     dev = torch.device("cuda")
-    cache = kvq.Cache(pool.shape[0], hkv, hb, "int4" if fmt == oracle.FMT_INT4 else "mxfp4",
+    khb, quat = parity.kernel_rotation(hb)
+    cache = kvq.Cache(pool.shape[0], hkv, khb, "int4" if fmt == oracle.FMT_INT4 else "mxfp4", quat=quat,
                       pool=torch.from_numpy(pool).to(dev))
     out = kvq.prefill_attn(cache, q_t.to(dev), torch.from_numpy(cu_q).to(dev),
                            torch.tensor(lens, dtype=torch.int32, device=dev), torch.from_numpy(table).to(dev),

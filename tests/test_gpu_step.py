@@ -69,7 +69,8 @@ def run_step(label, lens, hkv, group, hb, fmt="int4", kv_dtype="bf16", q_dtype="
     args = dict(seq_lens=torch.from_numpy(lens.astype(np.int32)).to(dev),
                 block_table=torch.from_numpy(table).to(dev), max_seq_len=int(lens.max()))
 
-    cache = kvq.Cache(total, hkv, hb, fmt, pool=torch.from_numpy(pool0).to(dev))
+    khb, quat = parity.kernel_rotation(hb)
+    cache = kvq.Cache(total, hkv, khb, fmt, pool=torch.from_numpy(pool0).to(dev), quat=quat)
     out = kvq.decode_step(cache, torch.from_numpy(knew).to(TDT[kv_dtype]).to(dev),
                           torch.from_numpy(vnew).to(TDT[kv_dtype]).to(dev), q_t.to(dev), **args,
                           scaled_mfma=scaled_mfma)
@@ -95,7 +96,7 @@ def run_step(label, lens, hkv, group, hb, fmt="int4", kv_dtype="bf16", q_dtype="
     assert err.max() <= parity.ATTN_TOL, f"{label}: row error {err.max():.3e}"
 
     # the two-call path on the same inputs
-    cache2 = kvq.Cache(total, hkv, hb, fmt, pool=torch.from_numpy(pool0).to(dev))
+    cache2 = kvq.Cache(total, hkv, khb, fmt, pool=torch.from_numpy(pool0).to(dev), quat=quat)
     kvq.append(cache2, torch.from_numpy(knew).to(TDT[kv_dtype]).to(dev),
                torch.from_numpy(vnew).to(TDT[kv_dtype]).to(dev), torch.from_numpy(cu1.astype(np.int32)).to(dev),
                torch.from_numpy(pre.astype(np.int32)).to(dev), args["block_table"], 1)
