@@ -240,8 +240,14 @@ def time_prefill_append(dev, repeats=10):
     start = torch.zeros(w.batch, dtype=torch.int32, device=dev)
     bt = torch.from_numpy(table).to(dev)
     res = {}
-    for hb in (128, 64, 1):
-        pools = [kvq.Cache(num_pages, w.num_kv_heads, hb, device=dev) for _ in range(2)]
+    quats = {"quat_fast": torch.from_numpy(wl.unit_quaternions(w.seed, False)).to(dev),
+             "quat_full": torch.from_numpy(wl.unit_quaternions(w.seed, True)).to(dev)}
+    for hb in (128, 64, 1, "quat_fast", "quat_full"):
+        if isinstance(hb, str):
+            pools = [kvq.Cache(num_pages, w.num_kv_heads, kvq.ROT_QUAT4, device=dev, quat=quats[hb])
+                     for _ in range(2)]
+        else:
+            pools = [kvq.Cache(num_pages, w.num_kv_heads, hb, device=dev) for _ in range(2)]
         for c in pools:
             kvq.append(c, k, v, cu, start, bt, int(lens.max()))
         torch.cuda.synchronize()
@@ -261,6 +267,8 @@ def time_prefill_append(dev, repeats=10):
         "us_rotated_b128": round(res[128], 2),
         "us_rotated_b64": round(res[64], 2),
         "us_plain_int4": round(res[1], 2),
+        "us_isoquant_fast": round(res["quat_fast"], 2),
+        "us_isoquant_full": round(res["quat_full"], 2),
         "rotation_overhead_pct": round(100.0 * (res[128] / res[1] - 1.0), 2),
         "GBps": round(nbytes / res[128] / 1e3, 1),
         "tokens_per_s": round(n_tok / res[128] * 1e6, 1),
