@@ -35,7 +35,7 @@ no independent pin checks say "parity unpinned" in their docstring; at present
 there are none.
 """
 
-from .hadamard import sylvester, rotation, rotation_matrix
+from .hadamard import sylvester, rotation, rotation_matrix, rotate
 from .quaternion import hamilton, conj, left_matrix, right_matrix, block_matrix, QuatRotation
 from .int4 import quantize_int4, dequantize_int4
 from .mxfp4 import quantize_mxfp4, dequantize_mxfp4, E2M1_GRID
@@ -45,7 +45,7 @@ from .paged import (append, dequant_pages, read_token, FMT_INT4, FMT_MXFP4)
 from .attention import decode_attention, decode_attention_one, prefill_attention
 
 __all__ = [
-    "prefill_attention", "rotation_matrix", "hamilton", "conj", "left_matrix", "right_matrix",
+    "prefill_attention", "rotation_matrix", "rotate", "hamilton", "conj", "left_matrix", "right_matrix",
     "block_matrix", "QuatRotation",
     "sylvester", "rotation", "quantize_int4", "dequantize_int4", "quantize_mxfp4",
     "dequantize_mxfp4", "E2M1_GRID", "PAGE_SIZE", "HEAD_DIM", "PAGE_HEAD_BYTES",

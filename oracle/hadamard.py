@@ -54,3 +54,25 @@ def rotation_matrix(rot, dim: int = 128) -> np.ndarray:
         return rotation(int(rot), dim)
     return rot.matrix()
 
+
+def rotate(x, rot, dim: int = 128) -> np.ndarray:
+    """y = R x for the rows of x[..., dim] (fp64).
+
+    For the Hadamard rotation the +-1 product H_b x is formed first and divided by sqrt(b)
+    once: the sums of the (fp16/bf16-exact) inputs are exact in fp64, so y carries one
+    rounding, and a component whose exact value is zero (a constant vector's, say) comes out
+    as exactly zero -- the quantizers' zero cases (an INT4 range of 0, an MXFP4 group amax of
+    0) then see what the definition gives.  Other rotations multiply by their matrix.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if isinstance(rot, (int, np.integer)):
+        b = int(rot)
+        if b < 1 or dim % b != 0:
+            raise ValueError(f"had_block {b} does not tile dim {dim}")
+        h = np.zeros((dim, dim))
+        blk = sylvester(b).astype(np.float64)
+        for start in range(0, dim, b):
+            h[start:start + b, start:start + b] = blk
+        return (x @ h.T) / np.sqrt(np.float64(b))
+    return x @ rot.matrix().T
+

@@ -16,7 +16,7 @@ Only the bytes of the appended slots are written.
 
 import numpy as np
 
-from .hadamard import rotation_matrix
+from .hadamard import rotation_matrix, rotate
 from .int4 import quantize_int4, dequantize_int4
 from .mxfp4 import quantize_mxfp4, dequantize_mxfp4
 from .layout import (PAGE_SIZE, HEAD_DIM, K_PARAMS_OFF, V_PARAMS_OFF, pack_row,
@@ -32,8 +32,7 @@ def encode(x: np.ndarray, had_block: int, fmt: int):
     Returns (row_bytes uint8[..., 64], param_bytes uint8[..., 4], info) where
     ``info`` holds the intermediate values the parity rules need.
     """
-    r = rotation_matrix(had_block, HEAD_DIM)
-    y = np.asarray(x, dtype=np.float64) @ r.T
+    y = rotate(x, had_block, HEAD_DIM)
     if fmt == FMT_INT4:
         codes, s16, z16, delta = quantize_int4(y)
         params = np.concatenate(

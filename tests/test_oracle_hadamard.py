@@ -71,3 +71,26 @@ def test_rotation_spreads_outliers():
     x[5] = 16.0
     y = rotation(64) @ x
     assert np.allclose(np.abs(y[:64]), 2.0) and not y[64:].any()
+
+
+def test_rotate_constant_vector_closed_form():
+    # H_b (c 1) = (c b, 0, ..., 0) per block: the normalised transform of a constant vector is
+    # c sqrt(b) in the first channel of each block and exactly zero elsewhere (what the
+    # quantizers' zero cases must see)
+    from oracle import rotate
+    for b in (64, 128):
+        y = rotate(np.full((1, 128), 0.75), b)[0]
+        first = np.zeros(128, bool)
+        first[::b] = True
+        assert np.all(y[~first] == 0.0)
+        assert np.allclose(y[first], 0.75 * np.sqrt(b), rtol=2.3e-16, atol=0)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((20, 128))
+    for b in (1, 64, 128):
+        assert np.allclose(rotate(x, b), x @ rotation(b).T, rtol=0, atol=1e-14)
+
+
+def test_mxfp4_constant_vector_has_zero_groups():
+    from oracle.paged import encode, FMT_MXFP4
+    _, params, info = encode(np.full((1, 128), 0.75), 128, FMT_MXFP4)
+    assert params[0, 1:].tolist() == [0, 0, 0] and params[0, 0] == 127 + 3 - 2
