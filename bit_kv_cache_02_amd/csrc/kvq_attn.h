@@ -395,8 +395,11 @@ __device__ __forceinline__ f32x4 scores_mx_scaled(const PageData<1>& pg, const i
 }
 
 // Online softmax and p.V of an MXFP4 page, from its q.K scores (C layout: column n = token n,
-// rows 4jg..4jg+3 = A rows 2g+part of heads 2jg, 2jg+1).
-__device__ __forceinline__ void softmax_pv_mx(const PageData<1>& pg, f32x4 sc, int valid0, int valid1,
+// rows 4jg..4jg+3 = A rows 2g+part of heads 2jg, 2jg+1).  vlimit (wave-uniform): tokens of the
+// page that exist in the sequence; the slots past it hold whatever the pool held, and their V
+// scale is taken as 0: dequantized with a stray scale byte they could overflow fp16, and 0 * inf
+// in the p.V contraction would poison every row even though their p is 0.
+__device__ __forceinline__ void softmax_pv_mx(const PageData<1>& pg, f32x4 sc, int valid0, int valid1, int vlimit,
                                               WaveState& s, float c2, bool has0, bool has1, int n, int jg,
                                               bool a_row_used, _Float16 (*ptile)[kPage]) {
   const bool tv0 = n < valid0, tv1 = n < valid1;
@@ -449,7 +452,7 @@ __device__ __forceinline__ void softmax_pv_mx(const PageData<1>& pg, f32x4 sc, i
     f16x4 blo, bhi;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const f16x2 h2 = cvt_fp4(Y, ue8m0_scale(pg.vp4[r], 8 * q), r);
+      const f16x2 h2 = cvt_fp4(Y, 4 * jg + r < vlimit ? ue8m0_scale(pg.vp4[r], 8 * q) : 0.0f, r);
       blo[r] = h2[0];
       bhi[r] = h2[1];
     }
@@ -458,18 +461,18 @@ __device__ __forceinline__ void softmax_pv_mx(const PageData<1>& pg, f32x4 sc, i
   }
 }
 
-__device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid0, int valid1, WaveState& s,
-                                                const f16x8 (&qh)[4], float c2, bool has0, bool has1,
+__device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid0, int valid1, int vlimit,
+                                                WaveState& s, const f16x8 (&qh)[4], float c2, bool has0, bool has1,
                                                 int n, int jg, bool a_row_used, _Float16 (*ptile)[kPage]) {
-  softmax_pv_mx(pg, scores_mx(pg, qh), valid0, valid1, s, c2, has0, has1, n, jg, a_row_used, ptile);
+  softmax_pv_mx(pg, scores_mx(pg, qh), valid0, valid1, vlimit, s, c2, has0, has1, n, jg, a_row_used, ptile);
 }
 
-__device__ __forceinline__ void process_page_mx_scaled(const PageData<1>& pg, int valid0, int valid1, WaveState& s,
-                                                       const i32x8 (&qa8)[2], const int (&qsa)[2], float c2,
-                                                       bool has0, bool has1, int n, int jg, bool a_row_used,
-                                                       _Float16 (*ptile)[kPage]) {
-  softmax_pv_mx(pg, scores_mx_scaled(pg, qa8, qsa, jg), valid0, valid1, s, c2, has0, has1, n, jg, a_row_used,
-                ptile);
+__device__ __forceinline__ void process_page_mx_scaled(const PageData<1>& pg, int valid0, int valid1, int vlimit,
+                                                       WaveState& s, const i32x8 (&qa8)[2], const int (&qsa)[2],
+                                                       float c2, bool has0, bool has1, int n, int jg,
+                                                       bool a_row_used, _Float16 (*ptile)[kPage]) {
+  softmax_pv_mx(pg, scores_mx_scaled(pg, qa8, qsa, jg), valid0, valid1, vlimit, s, c2, has0, has1, n, jg,
+                a_row_used, ptile);
 }
 
 // Rotate one row's normalised o' (element lane in o0, lane + 64 in o1) back and store it at

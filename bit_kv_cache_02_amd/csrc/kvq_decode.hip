@@ -357,11 +357,11 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
           process_page(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, s, qa, alpha0, beta0, alpha1, beta1,
                        has0, has1, n, jg, a_row_used, sm.ptile[wave]);
         else if constexpr (FMT == 1)
-          process_page_mx(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, s, qh, c2, has0, has1, n, jg,
-                          a_row_used, sm.ptile[wave]);
+          process_page_mx(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, valid0 - i * W * kPage, s, qh, c2,
+                          has0, has1, n, jg, a_row_used, sm.ptile[wave]);
         else
-          process_page_mx_scaled(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, s, qa8, qsa, c2, has0,
-                                 has1, n, jg, a_row_used, sm.ptile[wave]);
+          process_page_mx_scaled(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, valid0 - i * W * kPage, s,
+                                 qa8, qsa, c2, has0, has1, n, jg, a_row_used, sm.ptile[wave]);
       }
     }
   }

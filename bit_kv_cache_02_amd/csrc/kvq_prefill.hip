@@ -192,8 +192,8 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
           process_page(st[d], lim0 - i * kPage, lim1 - i * kPage, s, qa, alpha0, beta0, alpha1, beta1, has0, has1,
                        n, jg, a_row_used, sm.ptile[wave]);
         else
-          process_page_mx(st[d], lim0 - i * kPage, lim1 - i * kPage, s, qh, c2, has0, has1, n, jg, a_row_used,
-                          sm.ptile[wave]);
+          process_page_mx(st[d], lim0 - i * kPage, lim1 - i * kPage, L - i * kPage, s, qh, c2, has0, has1, n, jg,
+                          a_row_used, sm.ptile[wave]);
       }
     }
   }

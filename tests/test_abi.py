@@ -195,6 +195,7 @@ def _prefill(desc, **kw):
     (dict(q=None), kvq.KVQ_ERR_INVALID_ARG),
     (dict(msl=129), kvq.KVQ_ERR_INVALID_ARG),       # > max_pages * 16
     (dict(msl=140000, mp=9000), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(msl=131073, mp=8193), kvq.KVQ_ERR_UNSUPPORTED),  # one position past the prefill limit
     (dict(mq=101), kvq.KVQ_ERR_INVALID_ARG),        # chunk longer than the sequence bound
     (dict(T=-1), kvq.KVQ_ERR_INVALID_ARG),
     (dict(odt=kvq.FP8_E4M3), kvq.KVQ_ERR_UNSUPPORTED),

@@ -18,7 +18,9 @@ pytestmark = pytest.mark.gpu
 QDT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.float8_e4m3fn}
 
 
-def oracle_cache(rng, lens, hkv, hb, fmt=oracle.FMT_INT4, permute=True, dist="llama", extra=2):
+def oracle_cache(rng, lens, hkv, hb, fmt=oracle.FMT_INT4, permute=True, dist="llama", extra=2, fill=0x5A):
+    """A pool written by the oracle; bytes outside the appended slots are ``fill`` (an int) or,
+    for fill="random", random bytes."""
     n_pages = [-(-int(n) // 16) for n in lens]
     total = sum(n_pages) + extra
     ids = rng.permutation(total) if permute else np.arange(total)
@@ -34,7 +36,10 @@ def oracle_cache(rng, lens, hkv, hb, fmt=oracle.FMT_INT4, permute=True, dist="ll
         k[:, :, [5, 60, 111]] *= 15
     k = torch.from_numpy(k).bfloat16().float().numpy()
     v = torch.from_numpy(v).bfloat16().float().numpy()
-    pool = np.full((total, hkv, 2176), 0x5A, np.uint8)
+    if isinstance(fill, str):
+        pool = np.random.default_rng(12345).integers(0, 256, (total, hkv, 2176), dtype=np.uint8)
+    else:
+        pool = np.full((total, hkv, 2176), fill, np.uint8)
     cu = np.concatenate([[0], np.cumsum(lens)])
     oracle.append(pool, k, v, cu, np.zeros(len(lens), np.int64), table, hb, fmt)
     return pool, table

@@ -17,10 +17,10 @@ pytestmark = pytest.mark.gpu
 
 
 def run_prefill(label, lens, chunks, hkv, group, hb, fmt=oracle.FMT_INT4, q_dtype="bf16", q_scale=1.0,
-                sm_scale=None, out_dtype=torch.float32, rotated=False, seed=0, check=True):
+                sm_scale=None, out_dtype=torch.float32, rotated=False, seed=0, check=True, fill=0x5A):
     print(f"[prefill] {label}", flush=True)
     rng = np.random.default_rng(seed)
-    pool, table = oracle_cache(rng, lens, hkv, hb, fmt)
+    pool, table = oracle_cache(rng, lens, hkv, hb, fmt, fill=fill)
     cu_q = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
     q = rng.standard_normal((int(cu_q[-1]), hkv * group, 128)).astype(np.float32)
     q_t = torch.from_numpy(q).to(QDT[q_dtype])

@@ -36,7 +36,7 @@ def _vectors(rng, t, hkv, kv_dtype):
 
 
 def run_step(label, lens, hkv, group, hb, fmt="int4", kv_dtype="bf16", q_dtype="bf16", seed=0,
-             scaled_mfma=False):
+             scaled_mfma=False, fill=SENT):
     print(f"[step] {label}", flush=True)
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens, np.int64)
@@ -55,7 +55,7 @@ def run_step(label, lens, hkv, group, hb, fmt="int4", kv_dtype="bf16", q_dtype="
         k_all.append(k)
         v_all.append(v)
     # cache before the step: tokens 0 .. L-2
-    pool0 = np.full((total, hkv, 2176), SENT, np.uint8)
+    pool0 = np.full((total, hkv, 2176), fill, np.uint8)
     pre = lens - 1
     cu_pre = np.concatenate([[0], np.cumsum(pre)])
     if pre.sum() > 0:
@@ -84,7 +84,7 @@ def run_step(label, lens, hkv, group, hb, fmt="int4", kv_dtype="bf16", q_dtype="
     new = parity.touched_mask(pool0.shape, cu1, pre, table)
     pool_ref = pool0.copy()
     infos = oracle.append(pool_ref, knew, vnew, cu1, pre, table, hb, FMT[fmt])
-    flips = parity.check_append(gpu_pool, pool_ref, infos, cu1, pre, table, FMT[fmt], SENT, label,
+    flips = parity.check_append(gpu_pool, pool_ref, infos, cu1, pre, table, FMT[fmt], fill, label,
                                 prior_mask=prior)
     keep = prior & ~new
     assert np.array_equal(gpu_pool[keep], pool0[keep]), f"{label}: earlier tokens' bytes changed"
