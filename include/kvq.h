@@ -11,6 +11,9 @@
  *               (kvq_decode_attn).  An orthogonal R_b preserves q.k (IsoQuant abstract).
  * Two 4-bit formats: token-wise asymmetric INT4 with an fp16 scale and zero per vector,
  * and MXFP4 (e2m1 codes, one UE8M0 power-of-two scale per 32 channels, UltraQuant).
+ * Alternative rotation stage: IsoQuant's quaternion block-4 rotation (had_block 4, below).
+ * Also: chunked-prefill attention over the cache (kvq_prefill_attn), the write and read of a
+ * decode step in one launch (kvq_decode_step), page dequantization (kvq_dequant_page).
  *
  * Conventions for every entry point
  *   - Pointers named as device pointers must point to device memory (hipMalloc / a torch
@@ -24,11 +27,11 @@
  *   - A failed kernel launch returns KVQ_ERR_HIP with the HIP error text in kvq_last_error().
  *   - No C++ exception crosses this boundary.
  *
- * Cache geometry (ABI v1): head_dim 128, page 16 tokens.  One page-head block (one page, one
+ * Cache geometry: head_dim 128, page 16 tokens.  One page-head block (one page, one
  * kv head) is 2176 bytes; the pool is uint8[num_pages][num_kv_heads][2176]:
  *   [0,1024)     K code rows: slot s at 64*s; row byte 4a+q (a=0..15, q=0..3) holds channel
  *                a+32q in its low nibble and channel a+32q+16 in its high nibble (channels
- *                of the rotated vector).
+ *                of the rotated vector; row word a carries channel a+16i in nibble i).
  *   [1024,2048)  V code rows, same row bytes, interleaved by slot quads: byte j of slot s at
  *                1024 + 256*(s/4) + 4*j + (s%4).
  *   [2048,2112)  K parameters, slot s at 2048+4s;  [2112,2176) V parameters, same.
@@ -147,7 +150,8 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_q_heads,
  *   max_seq_len  host hint used to size the grid; must be <= max_pages*16.
  *   sm_scale     softmax scale (1/sqrt(128) is the usual value).
  *   out          device [num_seqs][num_q_heads][128], dtype out_dtype (F32, F16, BF16):
- *                o = R_b * sum_t softmax_t(sm_scale * q'.k^'_t) v^'_t, or the rotated-basis
+ *                o = R^T sum_t softmax_t(sm_scale * q'.k^'_t) v^'_t (q' = R q; R^T = R_b for
+ *                the Hadamard rotation), or the rotated-basis
  *                result with KVQ_OUT_ROTATED.
  *   flags        KVQ_OUT_ROTATED (above) and, for MXFP4 caches only, KVQ_MX_SCALED_MFMA: the
  *                q.K contraction then runs on v_mfma_scale_f32_16x16x128_f8f6f4 straight on the
@@ -224,7 +228,8 @@ int kvq_prefill_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, flo
  *   page_ids     device int32[n], each < num_pages.
  *   out_k, out_v device float[n][num_kv_heads][16][128]; channel order is natural.
  *   flags        0: values in the rotated basis (y^ = scale*code + zero, one fp32 rounding,
- *                or e2m1*2^(E-127) exactly); KVQ_UNROTATE: R_b * y^.
+ *                or e2m1*2^(E-127) exactly); KVQ_UNROTATE: R^T y^, the original basis (R_b^T =
+ *                R_b; for the quaternion rotation the transposed block matrices).
  * Slots never written hold whatever bytes the pool had.
  */
 int kvq_dequant_page(const kvq_cache* cache, const int32_t* page_ids, int32_t n,
