@@ -183,30 +183,63 @@ struct WaveState {
   f32x4 acc[8];
 };
 
-// valid0 / valid1: tokens of the page that rows x0 / x1 attend (decode: the same count).
-__device__ __forceinline__ void process_page(const PageData<0>& pg, int valid0, int valid1, WaveState& s,
-                                             const i32x4 (&qa)[2],
-                                             float alpha0, float beta0, float alpha1, float beta1,
-                                             bool has0, bool has1, int n, int jg, bool a_row_used,
-                                             _Float16 (*ptile)[kPage]) {
+// The row-independent operands of an INT4 page: the K codes as int8 B tiles (low and high
+// nibbles), the V codes as centred fp16 subnormal B tiles, and the token's parameters.
+struct PageI4 {
+  i32x4 kb0, kb1;
+  f16x4 blo[4], bhi[4];
+  float sk, zk, sv, zv;
+};
+
+__device__ __forceinline__ PageI4 unpack_i4(const PageData<0>& pg) {
   const uint32_t M4 = 0x0F0F0F0Fu, M16 = 0x000F000Fu;
+  PageI4 u;
+  u.kb0 = i32x4{(int)(pg.k[0] & M4), (int)(pg.k[1] & M4), (int)(pg.k[2] & M4), (int)(pg.k[3] & M4)};
+  u.kb1 = i32x4{(int)((pg.k[0] >> 4) & M4), (int)((pg.k[1] >> 4) & M4), (int)((pg.k[2] >> 4) & M4),
+                (int)((pg.k[3] >> 4) & M4)};
+  u.sk = f16_bits_to_f32(pg.kp & 0xFFFFu);
+  u.zk = f16_bits_to_f32(pg.kp >> 16);
+  u.sv = f16_bits_to_f32(pg.vp & 0xFFFFu);
+  u.zv = f16_bits_to_f32(pg.vp >> 16);
+  // V codes as fp16 subnormals: word q of the lane holds row byte 4n+q of 4 tokens.  Low nibbles
+  // (channel n+32q) are masked to c*2^-24, high nibbles (channel n+32q+16) are masked in place to
+  // 16c*2^-24 (their accumulators carry that factor 16 until the end).  One exact packed fp16
+  // subtraction centres the codes, c -> c - 8: all products p~*c would otherwise share one sign,
+  // and the MFMA accumulation error would not average out (the centre 8*sv moves into the zero
+  // point, zv + 8*sv).
+  typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+  const h2 c8lo = __builtin_bit_cast(h2, 0x00080008u), c8hi = __builtin_bit_cast(h2, 0x00800080u);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t Y = pg.v[q], Y8 = Y >> 8;
+    const h2 l0 = __builtin_bit_cast(h2, Y & M16) - c8lo, l1 = __builtin_bit_cast(h2, Y8 & M16) - c8lo;
+    const h2 u0 = __builtin_bit_cast(h2, Y & (M16 << 4)) - c8hi;
+    const h2 u1 = __builtin_bit_cast(h2, Y8 & (M16 << 4)) - c8hi;
+    u.blo[q] = f16x4{l0[0], l0[1], l1[0], l1[1]};  // tokens 0,2 | 1,3
+    u.bhi[q] = f16x4{u0[0], u0[1], u1[0], u1[1]};
+  }
+  return u;
+}
+
+// One set of 8 rows (A-tile rows 2g+limb) against an unpacked INT4 page.
+// valid0 / valid1: tokens of the page that rows x0 / x1 attend (decode: the same count).
+__device__ __forceinline__ void rows_i4(const PageI4& u, int valid0, int valid1, WaveState& s,
+                                        const i32x4 (&qa)[2], float alpha0, float beta0, float alpha1,
+                                        float beta1, bool has0, bool has1, int n, int jg, bool a_row_used,
+                                        _Float16 (*ptile)[kPage]) {
   const bool tv0 = n < valid0, tv1 = n < valid1;
 
   // q'.c_t on the integer matrix cores
-  const i32x4 kb0 = i32x4{(int)(pg.k[0] & M4), (int)(pg.k[1] & M4), (int)(pg.k[2] & M4), (int)(pg.k[3] & M4)};
-  const i32x4 kb1 = i32x4{(int)((pg.k[0] >> 4) & M4), (int)((pg.k[1] >> 4) & M4), (int)((pg.k[2] >> 4) & M4),
-                          (int)((pg.k[3] >> 4) & M4)};
-  i32x4 sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], kb0, i32x4{0, 0, 0, 0}, 0, 0, 0);
-  sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], kb1, sc, 0, 0, 0);
+  i32x4 sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], u.kb0, i32x4{0, 0, 0, 0}, 0, 0, 0);
+  sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], u.kb1, sc, 0, 0, 0);
 
-  const float sk = f16_bits_to_f32(pg.kp & 0xFFFFu), zk = f16_bits_to_f32(pg.kp >> 16);
-  float x0 = fmaf((float)(sc[0] * 256 + sc[1]) * alpha0, sk, zk * beta0);
-  float x1 = fmaf((float)(sc[2] * 256 + sc[3]) * alpha1, sk, zk * beta1);
+  float x0 = fmaf((float)(sc[0] * 256 + sc[1]) * alpha0, u.sk, u.zk * beta0);
+  float x1 = fmaf((float)(sc[2] * 256 + sc[3]) * alpha1, u.sk, u.zk * beta1);
   x0 = tv0 ? x0 : -INFINITY;
   x1 = tv1 ? x1 : -INFINITY;
 
   const float pm0 = row_max16(x0), pm1 = row_max16(x1);
-  const float sv = f16_bits_to_f32(pg.vp & 0xFFFFu), zv = f16_bits_to_f32(pg.vp >> 16);
+  const float sv = u.sv, zv = u.zv;
   // The reference max m only moves when a score exceeds it by more than 2^8 (or when p~ = p * sv
   // could leave the fp16 range): any m gives the same softmax, and p <= 2^8 keeps the fp16 and
   // fp32 partial sums in range.  exp2 of very negative arguments may flush to zero: harmless here.
@@ -254,25 +287,20 @@ __device__ __forceinline__ void process_page(const PageData<0>& pg, int valid0, 
   const f16x4 pa = a_row_used ? *(const f16x4*)&ptile[n][4 * jg] : f16x4{0, 0, 0, 0};
   __builtin_amdgcn_wave_barrier();
 
-  // V codes as fp16 subnormals: word q of the lane holds row byte 4n+q of 4 tokens.  Low nibbles
-  // (channel n+32q) are masked to c*2^-24, high nibbles (channel n+32q+16) are masked in place to
-  // 16c*2^-24 (their accumulators carry that factor 16 until the end).  One exact packed fp16
-  // subtraction centres the codes, c -> c - 8: all products p~*c would otherwise share one sign,
-  // and the MFMA accumulation error would not average out (the centre 8*sv moves into the zero
-  // point, zv + 8*sv).
-  typedef __attribute__((ext_vector_type(2))) _Float16 h2;
-  const h2 c8lo = __builtin_bit_cast(h2, 0x00080008u), c8hi = __builtin_bit_cast(h2, 0x00800080u);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t Y = pg.v[q], Y8 = Y >> 8;
-    const h2 l0 = __builtin_bit_cast(h2, Y & M16) - c8lo, l1 = __builtin_bit_cast(h2, Y8 & M16) - c8lo;
-    const h2 u0 = __builtin_bit_cast(h2, Y & (M16 << 4)) - c8hi;
-    const h2 u1 = __builtin_bit_cast(h2, Y8 & (M16 << 4)) - c8hi;
-    const f16x4 blo = f16x4{l0[0], l0[1], l1[0], l1[1]};  // tokens 0,2 | 1,3
-    const f16x4 bhi = f16x4{u0[0], u0[1], u1[0], u1[1]};
-    s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, blo, s.acc[2 * q], 0, 0, 0);
-    s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bhi, s.acc[2 * q + 1], 0, 0, 0);
+    s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, u.blo[q], s.acc[2 * q], 0, 0, 0);
+    s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, u.bhi[q], s.acc[2 * q + 1], 0, 0, 0);
   }
+}
+
+__device__ __forceinline__ void process_page(const PageData<0>& pg, int valid0, int valid1, WaveState& s,
+                                             const i32x4 (&qa)[2],
+                                             float alpha0, float beta0, float alpha1, float beta1,
+                                             bool has0, bool has1, int n, int jg, bool a_row_used,
+                                             _Float16 (*ptile)[kPage]) {
+  rows_i4(unpack_i4(pg), valid0, valid1, s, qa, alpha0, beta0, alpha1, beta1, has0, has1, n, jg, a_row_used,
+          ptile);
 }
 
 // MXFP4 page: K and V are dequantized to fp16 tiles with their UE8M0 group scales by the gfx950
@@ -282,21 +310,53 @@ __device__ __forceinline__ void process_page(const PageData<0>& pg, int valid0, 
 //        all in channel group q (one scale).
 //   p.V: v_mfma_f32_16x16x16_f16, A = p split high/low, B = V tile: byte r of V word q is token
 //        4jg+r, channels n+32q and n+32q+16 (group q), repacked so one register holds two tokens.
-__device__ __forceinline__ f32x4 scores_mx(const PageData<1>& pg, const f16x8 (&qh)[4]) {
-  f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+struct KTileMx {
+  f16x8 kb[4];
+};
+
+__device__ __forceinline__ KTileMx unpack_k_mx(const PageData<1>& pg) {
+  KTileMx t;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const uint32_t w = pg.k[kk];
-    f16x8 kb;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f16x2 h2 = cvt_fp4(w, ue8m0_scale(pg.kp, 8 * q), q);
-      kb[2 * q] = h2[0];
-      kb[2 * q + 1] = h2[1];
+      t.kb[kk][2 * q] = h2[0];
+      t.kb[kk][2 * q + 1] = h2[1];
     }
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[kk], kb, sc, 0, 0, 0);
   }
+  return t;
+}
+
+__device__ __forceinline__ f32x4 scores_mx(const KTileMx& t, const f16x8 (&qh)[4]) {
+  f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[kk], t.kb[kk], sc, 0, 0, 0);
   return sc;
+}
+
+// The V tile of an MXFP4 page as fp16 B operands.  vlimit (wave-uniform): tokens of the page
+// that exist in the sequence; the slots past it hold whatever the pool held, and their V scale
+// is taken as 0: dequantized with a stray scale byte they could overflow fp16, and 0 * inf in
+// the p.V contraction would poison every row even though their p is 0.
+struct VTileMx {
+  f16x4 blo[4], bhi[4];
+};
+
+__device__ __forceinline__ VTileMx unpack_v_mx(const PageData<1>& pg, int vlimit, int jg) {
+  VTileMx t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t Y = pg.v[q];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f16x2 h2 = cvt_fp4(Y, 4 * jg + r < vlimit ? ue8m0_scale(pg.vp4[r], 8 * q) : 0.0f, r);
+      t.blo[q][r] = h2[0];
+      t.bhi[q][r] = h2[1];
+    }
+  }
+  return t;
 }
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
@@ -395,13 +455,10 @@ __device__ __forceinline__ f32x4 scores_mx_scaled(const PageData<1>& pg, const i
 }
 
 // Online softmax and p.V of an MXFP4 page, from its q.K scores (C layout: column n = token n,
-// rows 4jg..4jg+3 = A rows 2g+part of heads 2jg, 2jg+1).  vlimit (wave-uniform): tokens of the
-// page that exist in the sequence; the slots past it hold whatever the pool held, and their V
-// scale is taken as 0: dequantized with a stray scale byte they could overflow fp16, and 0 * inf
-// in the p.V contraction would poison every row even though their p is 0.
-__device__ __forceinline__ void softmax_pv_mx(const PageData<1>& pg, f32x4 sc, int valid0, int valid1, int vlimit,
-                                              WaveState& s, float c2, bool has0, bool has1, int n, int jg,
-                                              bool a_row_used, _Float16 (*ptile)[kPage]) {
+// rows 4jg..4jg+3 = A rows 2g+part of heads 2jg, 2jg+1) and its V tile.
+__device__ __forceinline__ void softmax_pv_mx(const VTileMx& vt, f32x4 sc, int valid0, int valid1, WaveState& s,
+                                              float c2, bool has0, bool has1, int n, int jg, bool a_row_used,
+                                              _Float16 (*ptile)[kPage]) {
   const bool tv0 = n < valid0, tv1 = n < valid1;
   float x0 = (sc[0] + sc[1]) * c2, x1 = (sc[2] + sc[3]) * c2;
   x0 = tv0 ? x0 : -INFINITY;
@@ -448,31 +505,24 @@ __device__ __forceinline__ void softmax_pv_mx(const PageData<1>& pg, f32x4 sc, i
 
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t Y = pg.v[q];
-    f16x4 blo, bhi;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const f16x2 h2 = cvt_fp4(Y, 4 * jg + r < vlimit ? ue8m0_scale(pg.vp4[r], 8 * q) : 0.0f, r);
-      blo[r] = h2[0];
-      bhi[r] = h2[1];
-    }
-    s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, blo, s.acc[2 * q], 0, 0, 0);
-    s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bhi, s.acc[2 * q + 1], 0, 0, 0);
+    s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vt.blo[q], s.acc[2 * q], 0, 0, 0);
+    s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vt.bhi[q], s.acc[2 * q + 1], 0, 0, 0);
   }
 }
 
 __device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid0, int valid1, int vlimit,
                                                 WaveState& s, const f16x8 (&qh)[4], float c2, bool has0, bool has1,
                                                 int n, int jg, bool a_row_used, _Float16 (*ptile)[kPage]) {
-  softmax_pv_mx(pg, scores_mx(pg, qh), valid0, valid1, vlimit, s, c2, has0, has1, n, jg, a_row_used, ptile);
+  softmax_pv_mx(unpack_v_mx(pg, vlimit, jg), scores_mx(unpack_k_mx(pg), qh), valid0, valid1, s, c2, has0, has1, n,
+                jg, a_row_used, ptile);
 }
 
 __device__ __forceinline__ void process_page_mx_scaled(const PageData<1>& pg, int valid0, int valid1, int vlimit,
                                                        WaveState& s, const i32x8 (&qa8)[2], const int (&qsa)[2],
                                                        float c2, bool has0, bool has1, int n, int jg,
                                                        bool a_row_used, _Float16 (*ptile)[kPage]) {
-  softmax_pv_mx(pg, scores_mx_scaled(pg, qa8, qsa, jg), valid0, valid1, vlimit, s, c2, has0, has1, n, jg,
-                a_row_used, ptile);
+  softmax_pv_mx(unpack_v_mx(pg, vlimit, jg), scores_mx_scaled(pg, qa8, qsa, jg), valid0, valid1, s, c2, has0, has1,
+                n, jg, a_row_used, ptile);
 }
 
 // Rotate one row's normalised o' (element lane in o0, lane + 64 in o1) back and store it at

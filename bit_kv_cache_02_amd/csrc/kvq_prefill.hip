@@ -6,10 +6,12 @@
 // The chunk of sequence b is its last n_b positions, already appended (kvq_append); chunk token
 // j sits at position p_j = seq_lens[b] - n_b + j and attends positions 0 .. p_j.
 //
-// A workgroup (W waves) owns (sequence, kv head, tile of W * 8/G chunk tokens).  Wave w takes 8
-// rows: its 8/G chunk tokens times the G query heads of the kv head.  Each wave streams every page
-// its rows attend through the per-page step that decode uses (kvq_attn.h): the 8 rows fill the 8
-// row pairs of the matrix-core tiles, and each row pair carries its own causal limit.  The waves
+// A workgroup (W waves) owns (sequence, kv head, tile of W * 8 RS/G chunk tokens).  Wave w takes
+// RS sets of 8 rows: its 8 RS/G chunk tokens times the G query heads of the kv head.  Each wave
+// streams every page its rows attend; per page it unpacks the K and V codes once (the
+// row-independent half of the per-page step that decode uses, kvq_attn.h) and runs the scores,
+// online softmax and p.V of each row set against them: a set's 8 rows fill the 8 row pairs of the
+// matrix-core tiles, and each row pair carries its own causal limit.  The waves
 // of a workgroup read the same pages close together in time, so the caches serve all but the
 // first read of each page; the sequence's block-table entries are staged in LDS once per
 // workgroup.  Query rotation and the final rotation back run for the 8 rows of a wave at once.
@@ -23,30 +25,43 @@ namespace {
 
 using namespace attn;
 
-constexpr int kRows = 8;              // rows (chunk token x query head) per wave
+constexpr int kSetRows = 8;           // rows (chunk token x query head) per row set
 constexpr int kMaxTablePages = 8192;  // staged block-table entries: positions < 131072
 
-template <int W>
-struct PrefillSmem {
+// Per wave: the query operands (prologue) and the output rows (epilogue) share one slice; a wave
+// only overwrites its own operands, which it has read into registers before its page loop.
+template <int RS>
+struct PrefillWaveSmem {
   union {
-    uint8_t qlimb[W][2][kRows][2][4][16];  // INT4: q' limbs per wave, as in decode
-    _Float16 qh[W][2][kRows][4][4][8];     // MXFP4: q' fp16 high/low parts per wave
+    struct {
+      union {
+        uint8_t qlimb[2][kSetRows * RS][2][4][16];  // INT4: q' limbs, as in decode
+        _Float16 qh[2][kSetRows * RS][4][4][8];     // MXFP4: q' fp16 high/low parts
+      };
+      float qdelta[kSetRows * RS];
+      float qsum[kSetRows * RS];
+    } q;
+    float wo[kSetRows * RS][kHeadDim];
   };
-  float qdelta[W][kRows];
-  float qsum[W][kRows];
-  _Float16 ptile[W][2 * kRows][kPage];
-  float wo[W][kRows][kHeadDim];
+  _Float16 ptile[RS][2 * kSetRows][kPage];
+};
+
+template <int W, int RS>
+struct PrefillSmem {
+  PrefillWaveSmem<RS> w[W];
   int32_t table[kMaxTablePages];
 };
 
 }  // namespace
 
-template <int FMT, int W, int D>
+template <int FMT, int W, int D, int RS>
 __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
-  __shared__ PrefillSmem<W> sm;
+  constexpr int kRows = kSetRows * RS;  // rows per wave
+  __shared__ PrefillSmem<W, RS> sm;
   const int tid = thread_id();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  PrefillWaveSmem<RS>& ws = sm.w[wave];
   const int n = lane & 15, jg = lane >> 4;
   const int G = a.group;
   const int tpw = kRows / G;  // chunk tokens per wave
@@ -93,7 +108,7 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
 #pragma unroll
   for (int k = 0; k < kTableLoads; ++k) sm.table[k * W * 64 + tid] = (int32_t)tw[k];
 
-  // ---- 1. q' = R_b (q_scale q) for the 8 rows, then the decode's operand encodings ----
+  // ---- 1. q' = R (q_scale q) for the wave's rows, then the decode's operand encodings ----
   {
     float v0[kRows], v1[kRows];
 #pragma unroll
@@ -111,8 +126,8 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
           const float v = e ? v1[r] : v0[r];
           const _Float16 hi = (_Float16)v;
           const _Float16 lo = (_Float16)(v - (float)hi);
-          sm.qh[wave][0][r][ch & 3][(ch >> 2) & 3][ch >> 4] = hi;
-          sm.qh[wave][1][r][ch & 3][(ch >> 2) & 3][ch >> 4] = lo;
+          ws.q.qh[0][r][ch & 3][(ch >> 2) & 3][ch >> 4] = hi;
+          ws.q.qh[1][r][ch & 3][(ch >> 2) & 3][ch >> 4] = lo;
         }
       } else {
         const float amax = wave_max(fmaxf(fabsf(v0[r]), fabsf(v1[r])));
@@ -124,40 +139,51 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
           const int ch = lane + 64 * e, Q = e ? q1 : q0;
           const int hi = (Q + 128) >> 8, lo = Q - 256 * hi;
           const int c16 = ch & 15, c_hi = ch >> 4;
-          uint8_t* dst = &sm.qlimb[wave][0][r][c_hi & 1][c16 >> 2][4 * (c16 & 3) + (c_hi >> 1)];
+          uint8_t* dst = &ws.q.qlimb[0][r][c_hi & 1][c16 >> 2][4 * (c16 & 3) + (c_hi >> 1)];
           dst[0] = (uint8_t)(hi & 255);
-          dst[sizeof(sm.qlimb[0][0])] = (uint8_t)(lo & 255);
+          dst[sizeof(ws.q.qlimb[0])] = (uint8_t)(lo & 255);
         }
         if (lane == 0) {
-          sm.qdelta[wave][r] = delta;
-          sm.qsum[wave][r] = delta * (float)qs;
+          ws.q.qdelta[r] = delta;
+          ws.q.qsum[r] = delta * (float)qs;
         }
       }
     }
   }
   __syncthreads();  // block-table entries and query operands staged
 
-  const int ga = n >> 1, limb = n & 1;  // A-tile row 2g+limb of this lane
-  const int t_a = tw0 + ga / G;         // chunk token of the lane's A row
-  const bool a_row_used = t_a < nq;
-  const int t_row0 = tw0 + (2 * jg) / G, t_row1 = tw0 + (2 * jg + 1) / G;  // tokens of rows x0, x1
-  const bool has0 = t_row0 < nq, has1 = t_row1 < nq;
+  // Row set k holds rows 8k .. 8k+7; A-tile row 2g+limb of set k is row 8k + g.
+  const int ga = n >> 1, limb = n & 1;
   const float c2 = a.sm_scale_log2;
-  i32x4 qa[2];
-  f16x8 qh[4];
-  float alpha0 = 0.f, beta0 = 0.f, alpha1 = 0.f, beta1 = 0.f;
-  if constexpr (FMT == 0) {
+  i32x4 qa[RS][2];
+  f16x8 qh[RS][4];
+  float alpha0[RS], beta0[RS], alpha1[RS], beta1[RS];
+  bool a_row_used[RS], has0[RS], has1[RS];
+  int lim0[RS], lim1[RS];  // tokens of page i that rows x0 / x1 attend: lim - 16 i
 #pragma unroll
-    for (int a2 = 0; a2 < 2; ++a2)
-      qa[a2] = a_row_used ? *(const i32x4*)&sm.qlimb[wave][limb][ga][a2][jg][0] : i32x4{0, 0, 0, 0};
-    alpha0 = has0 ? sm.qdelta[wave][2 * jg] * c2 : 0.0f;
-    beta0 = has0 ? sm.qsum[wave][2 * jg] * c2 : 0.0f;
-    alpha1 = has1 ? sm.qdelta[wave][2 * jg + 1] * c2 : 0.0f;
-    beta1 = has1 ? sm.qsum[wave][2 * jg + 1] * c2 : 0.0f;
-  } else {
+  for (int k = 0; k < RS; ++k) {
+    const int rbase = kSetRows * k;
+    a_row_used[k] = tw0 + (rbase + ga) / G < nq;
+    const int t_row0 = tw0 + (rbase + 2 * jg) / G, t_row1 = tw0 + (rbase + 2 * jg + 1) / G;
+    has0[k] = t_row0 < nq;
+    has1[k] = t_row1 < nq;
+    lim0[k] = pos0 + t_row0 + 1;
+    lim1[k] = pos0 + t_row1 + 1;
+    alpha0[k] = beta0[k] = alpha1[k] = beta1[k] = 0.0f;
+    if constexpr (FMT == 0) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qh[kk] = a_row_used ? *(const f16x8*)&sm.qh[wave][limb][ga][kk][jg][0] : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int a2 = 0; a2 < 2; ++a2)
+        qa[k][a2] = a_row_used[k] ? *(const i32x4*)&ws.q.qlimb[limb][rbase + ga][a2][jg][0] : i32x4{0, 0, 0, 0};
+      alpha0[k] = has0[k] ? ws.q.qdelta[rbase + 2 * jg] * c2 : 0.0f;
+      beta0[k] = has0[k] ? ws.q.qsum[rbase + 2 * jg] * c2 : 0.0f;
+      alpha1[k] = has1[k] ? ws.q.qdelta[rbase + 2 * jg + 1] * c2 : 0.0f;
+      beta1[k] = has1[k] ? ws.q.qsum[rbase + 2 * jg + 1] * c2 : 0.0f;
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qh[k][kk] = a_row_used[k] ? *(const f16x8*)&ws.q.qh[limb][rbase + ga][kk][jg][0]
+                                  : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
   }
 
   // ---- 2. stream pages 0 .. npw-1 (the positions this wave's rows attend) ----
@@ -175,42 +201,55 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
   PageData<FMT> st[NB];
 #pragma unroll
   for (int d = 0; d < D; ++d) st[d] = load_page<FMT>(page_base(d), d < npw, koff, voff, poff, qoff);
-  WaveState s;
-  s.m0 = s.m1 = kNegBig;
-  s.l0 = s.l1 = s.pz0 = s.pz1 = 0.0f;
+  WaveState s[RS];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // tokens of page i that row x attends: (p_x + 1) - 16 i
-  const int lim0 = pos0 + t_row0 + 1, lim1 = pos0 + t_row1 + 1;
+  for (int k = 0; k < RS; ++k) {
+    s[k].m0 = s[k].m1 = kNegBig;
+    s[k].l0 = s[k].l1 = s[k].pz0 = s[k].pz1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[k].acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   for (int i0 = 0; i0 < npw; i0 += NB) {
 #pragma unroll
     for (int d = 0; d < NB; ++d) {
       const int i = i0 + d;
       st[(d + D) % NB] = load_page<FMT>(page_base(i + D), i + D < npw, koff, voff, poff, qoff);
       if (i < npw) {
-        if constexpr (FMT == 0)
-          process_page(st[d], lim0 - i * kPage, lim1 - i * kPage, s, qa, alpha0, beta0, alpha1, beta1, has0, has1,
-                       n, jg, a_row_used, sm.ptile[wave]);
-        else
-          process_page_mx(st[d], lim0 - i * kPage, lim1 - i * kPage, L - i * kPage, s, qh, c2, has0, has1, n, jg,
-                          a_row_used, sm.ptile[wave]);
+        if constexpr (FMT == 0) {
+          const PageI4 u = unpack_i4(st[d]);
+#pragma unroll
+          for (int k = 0; k < RS; ++k)
+            rows_i4(u, lim0[k] - i * kPage, lim1[k] - i * kPage, s[k], qa[k], alpha0[k], beta0[k], alpha1[k],
+                    beta1[k], has0[k], has1[k], n, jg, a_row_used[k], ws.ptile[k]);
+        } else {
+          const KTileMx kt = unpack_k_mx(st[d]);
+          const VTileMx vt = unpack_v_mx(st[d], L - i * kPage, jg);
+#pragma unroll
+          for (int k = 0; k < RS; ++k)
+            softmax_pv_mx(vt, scores_mx(kt, qh[k]), lim0[k] - i * kPage, lim1[k] - i * kPage, s[k], c2, has0[k],
+                          has1[k], n, jg, a_row_used[k], ws.ptile[k]);
+        }
       }
     }
   }
 
-  // ---- 3. normalise the 8 rows, rotate them back, store ----
-  const float l0 = row_sum16(s.l0), l1 = row_sum16(s.l1);
-  const float pz0 = row_sum16(s.pz0), pz1 = row_sum16(s.pz1);
-  const float il0 = has0 ? 1.0f / l0 : 0.0f, il1 = has1 ? 1.0f / l1 : 0.0f;
+  // ---- 3. normalise the rows, rotate them back, store ----
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int k = 0; k < RS; ++k) {
+    const float l0 = row_sum16(s[k].l0), l1 = row_sum16(s[k].l1);
+    const float pz0 = row_sum16(s[k].pz0), pz1 = row_sum16(s[k].pz1);
+    const float il0 = has0[k] ? 1.0f / l0 : 0.0f, il1 = has1[k] ? 1.0f / l1 : 0.0f;
+    const int rbase = kSetRows * k;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int ch = n + 32 * q + 16 * e;
-      const f32x4 v = s.acc[2 * q + e];
-      const float sc = FMT == 1 ? 1.0f : (e ? 1048576.0f : 16777216.0f);
-      sm.wo[wave][2 * jg][ch] = (sc * (v[0] + v[1]) + pz0) * il0;
-      sm.wo[wave][2 * jg + 1][ch] = (sc * (v[2] + v[3]) + pz1) * il1;
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int ch = n + 32 * q + 16 * e;
+        const f32x4 v = s[k].acc[2 * q + e];
+        const float sc = FMT == 1 ? 1.0f : (e ? 1048576.0f : 16777216.0f);
+        ws.wo[rbase + 2 * jg][ch] = (sc * (v[0] + v[1]) + pz0) * il0;
+        ws.wo[rbase + 2 * jg + 1][ch] = (sc * (v[2] + v[3]) + pz1) * il1;
+      }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -219,8 +258,8 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
   float o0[kRows], o1[kRows];
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
-    o0[r] = sm.wo[wave][r][lane];
-    o1[r] = sm.wo[wave][r][lane + 64];
+    o0[r] = ws.wo[r][lane];
+    o1[r] = ws.wo[r][lane + 64];
   }
   if (!a.out_rotated) rotate_rows<kRows>(o0, o1, a.had_block, a.quat, a.quat_full, lane, true);
 #pragma unroll
@@ -237,16 +276,19 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
 namespace {
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillDepth = 3;
+constexpr int kPrefillSets = 2;  // row sets per wave: 16 rows share each page's unpack
 }  // namespace
 
-int prefill_tokens_per_tile(int group) { return kPrefillWaves * (kRows / group); }
+int prefill_tokens_per_tile(int group) { return kPrefillWaves * (kSetRows * kPrefillSets / group); }
 
 hipError_t launch_prefill(const PrefillParams& p, int fmt, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.num_seqs * p.hkv * p.tiles));
   if (fmt == 0)
-    hipLaunchKernelGGL((prefill_kernel<0, kPrefillWaves, kPrefillDepth>), grid, dim3(kPrefillWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<0, kPrefillWaves, kPrefillDepth, kPrefillSets>), grid, dim3(kPrefillWaves * 64),
+                       0, stream, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<1, kPrefillWaves, kPrefillDepth>), grid, dim3(kPrefillWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<1, kPrefillWaves, kPrefillDepth, kPrefillSets>), grid, dim3(kPrefillWaves * 64),
+                       0, stream, p);
   return hipGetLastError();
 }
 
