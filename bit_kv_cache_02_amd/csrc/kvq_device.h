@@ -155,7 +155,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   uint32_t s = (b >> 7) & 1u, e = (b >> 3) & 15u, m = b & 7u;
   float v;
-  if (e == 15u && m == 7u) v = __builtin_nanf("");
+  if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);  // NaN (bit pattern: the build assumes no NaN math)
   else if (e == 0u) v = (float)m * 0x1p-9f;
   else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
   return s ? -v : v;
