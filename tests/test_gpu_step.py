@@ -172,11 +172,16 @@ def test_step_repeated_calls_grow_the_cache():
         ref_pool = gpu_pool.copy()  # the next step builds on the GPU's bytes
 
 
-def test_step_graph_replays_match_eager():
+@pytest.mark.parametrize("fmt,rot,scaled", [("int4", "hadamard", False), ("mxfp4", "hadamard", True),
+                                            ("int4", "quat", False)])
+def test_step_graph_replays_match_eager(fmt, rot, scaled):
     # the step captured in a HIP graph and replayed several times, with eager work and
-    # synchronisations in between: every replay gives the eager result bit for bit
+    # synchronisations in between: every replay gives the eager result bit for bit (INT4; MXFP4
+    # on the scaled-MFMA path; the quaternion rotation)
+    from bit_kv_cache_02_amd import workloads as wl
     rng = np.random.default_rng(8)
-    hkv, group, hb = 2, 4, 128
+    hkv, group = 2, 4
+    hb = 128 if rot == "hadamard" else oracle.QuatRotation(wl.unit_quaternions(9, True))
     lens = np.array([700, 33, 5000], np.int64)
     n_pages = [-(-int(n) // 16) for n in lens]
     total = sum(n_pages)
@@ -190,7 +195,7 @@ def test_step_graph_replays_match_eager():
     pool = np.full((total, hkv, 2176), SENT, np.uint8)
     cu = np.concatenate([[0], np.cumsum(lens - 1)])
     sel = np.concatenate([np.arange(s, s + n - 1) for s, n in zip(np.concatenate([[0], np.cumsum(lens)])[:-1], lens)])
-    oracle.append(pool, k[sel], v[sel], cu, np.zeros(3, np.int64), table, hb)
+    oracle.append(pool, k[sel], v[sel], cu, np.zeros(3, np.int64), table, hb, FMT[fmt])
     last = np.cumsum(lens) - 1
     dev = torch.device("cuda")
     kn = torch.from_numpy(k[last]).bfloat16().to(dev)
@@ -198,22 +203,25 @@ def test_step_graph_replays_match_eager():
     q = torch.from_numpy(rng.standard_normal((3, hkv * group, 128)).astype(np.float32)).bfloat16().to(dev)
     sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
     bt = torch.from_numpy(table).to(dev)
-    cache = kvq.Cache(total, hkv, hb, pool=torch.from_numpy(pool).to(dev))
+    khb, quat = parity.kernel_rotation(hb)
+    cache = kvq.Cache(total, hkv, khb, fmt, pool=torch.from_numpy(pool).to(dev), quat=quat)
     ws = kvq.make_workspace(cache, hkv * group, 3, int(lens.max()), dev)
     out = torch.empty((3, hkv * group, 128), dtype=torch.float32, device=dev)
-    kvq.decode_step(cache, kn, vn, q, sl, bt, int(lens.max()), out=out, workspace=ws)
+    step = lambda: kvq.decode_step(cache, kn, vn, q, sl, bt, int(lens.max()), out=out, workspace=ws,
+                                   scaled_mfma=scaled)
+    step()
     torch.cuda.synchronize()
     eager = out.clone()
     eager_pool = cache.pool.clone()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        kvq.decode_step(cache, kn, vn, q, sl, bt, int(lens.max()), out=out, workspace=ws)
+        step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        kvq.decode_step(cache, kn, vn, q, sl, bt, int(lens.max()), out=out, workspace=ws)
+        step()
     for r in range(4):
         out.zero_()
         scratch = torch.randn(1 << 20, device=dev).sum()  # unrelated eager work
