@@ -17,7 +17,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_host.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_prefill.hip", "kvq_dequant.hip"]
+SOURCES = ["kvq_host.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_prefill.hip", "kvq_dequant.hip",
+           "kvq_check.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

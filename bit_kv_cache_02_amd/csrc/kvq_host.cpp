@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "kvq_internal.h"
@@ -55,6 +56,31 @@ int check_cache(const kvq_cache* c) {
   }
   if (((uintptr_t)c->pool) & 15) return fail(KVQ_ERR_INVALID_ARG, "pool must be 16-byte aligned");
   return KVQ_OK;
+}
+
+// KVQ_DEBUG_CHECKS (environment, read on every call; unset, empty or "0": off): validate the
+// call's device-side tables on its stream, wait for the verdict, and refuse the call before its
+// kernels run.  The check synchronizes the stream, so it is for debugging, not graph capture.
+bool debug_checks() {
+  const char* e = getenv("KVQ_DEBUG_CHECKS");
+  return e && e[0] && strcmp(e, "0") != 0;
+}
+
+int device_check(const kvq::CheckParams& c, void* stream, const char* what) {
+  int code = 0, index = 0;
+  const hipError_t e = kvq::run_check(c, (hipStream_t)stream, &code, &index);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: KVQ_DEBUG_CHECKS: %s", what, hipGetErrorString(e));
+  const char* msg = nullptr;
+  switch (code) {
+    case kvq::kCheckOk: return KVQ_OK;
+    case kvq::kBadSeqLen: msg = "seq_lens out of [1, max_seq_len]"; break;
+    case kvq::kBadPageId: msg = "a block-table entry / page id outside [0, num_pages)"; break;
+    case kvq::kBadCumulative: msg = "cumulative counts not non-decreasing within [0, num_tokens]"; break;
+    case kvq::kBadStartPos: msg = "start_pos negative or the appended positions beyond max_pages*16"; break;
+    case kvq::kBadChunk: msg = "chunk longer than its sequence or than max_q_len"; break;
+    default: msg = "unknown violation"; break;
+  }
+  return fail(KVQ_ERR_INVALID_ARG, "%s: KVQ_DEBUG_CHECKS: %s (index %d)", what, msg, index);
 }
 
 }  // namespace
@@ -111,6 +137,20 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t kv_
   p.max_new = max_new_tokens;
   p.quat = cache->quat;
   p.quat_full = cache->quat_full;
+  if (debug_checks()) {
+    kvq::CheckParams c;
+    memset(&c, 0, sizeof(c));
+    c.kind = kvq::kCheckAppend;
+    c.cu = cu_new;
+    c.start_pos = start_pos;
+    c.block_table = block_table;
+    c.num_seqs = num_seqs;
+    c.num_tokens = num_tokens;
+    c.max_pages = max_pages;
+    c.max_len = max_new_tokens;
+    c.num_pages = cache->num_pages;
+    if (int st = device_check(c, stream, "kvq_append")) return st;
+  }
   return hip_status(kvq::launch_append(p, kv_dtype == KVQ_BF16, cache->had_block, cache->format, (hipStream_t)stream),
                     "kvq_append launch");
 }
@@ -199,6 +239,18 @@ static int decode_common(const kvq_cache* cache, const void* knew, const void* v
   p.kv_dtype = append ? kv_dtype : KVQ_BF16;
   p.append = append ? 1 : 0;
   p.plan = plan;
+  if (debug_checks()) {
+    kvq::CheckParams c;
+    memset(&c, 0, sizeof(c));
+    c.kind = kvq::kCheckDecode;
+    c.seq_lens = seq_lens;
+    c.block_table = block_table;
+    c.num_seqs = num_seqs;
+    c.max_pages = max_pages;
+    c.max_len = max_seq_len;
+    c.num_pages = cache->num_pages;
+    if (int st = device_check(c, stream, what)) return st;
+  }
   // kernel variant 2: MXFP4 with q.K on the scaled matrix cores
   const int variant = (flags & KVQ_MX_SCALED_MFMA) ? 2 : cache->format;
   return hip_status(kvq::launch_decode(p, variant, (hipStream_t)stream), what);
@@ -279,6 +331,21 @@ int kvq_prefill_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, flo
   p.tiles = (int32_t)tiles;
   p.q_scale = q_scale;
   p.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  if (debug_checks()) {
+    kvq::CheckParams c;
+    memset(&c, 0, sizeof(c));
+    c.kind = kvq::kCheckPrefill;
+    c.cu = cu_q;
+    c.seq_lens = seq_lens;
+    c.block_table = block_table;
+    c.num_seqs = num_seqs;
+    c.num_tokens = num_tokens;
+    c.max_pages = max_pages;
+    c.max_len = max_seq_len;
+    c.max_q_len = max_q_len;
+    c.num_pages = cache->num_pages;
+    if (int st = device_check(c, stream, "kvq_prefill_attn")) return st;
+  }
   return hip_status(kvq::launch_prefill(p, cache->format, (hipStream_t)stream), "kvq_prefill_attn launch");
 }
 
@@ -304,6 +371,15 @@ int kvq_dequant_page(const kvq_cache* cache, const int32_t* page_ids, int32_t n,
   p.quat_full = cache->quat_full;
   p.unrotate = (flags & KVQ_UNROTATE) ? 1 : 0;
   p.fmt = cache->format;
+  if (debug_checks()) {
+    kvq::CheckParams c;
+    memset(&c, 0, sizeof(c));
+    c.kind = kvq::kCheckDequant;
+    c.page_ids = page_ids;
+    c.n = n;
+    c.num_pages = cache->num_pages;
+    if (int st = device_check(c, stream, "kvq_dequant_page")) return st;
+  }
   return hip_status(kvq::launch_dequant(p, (hipStream_t)stream), "kvq_dequant_page launch");
 }
 

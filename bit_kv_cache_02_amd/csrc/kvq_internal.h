@@ -99,6 +99,28 @@ struct DequantParams {
   int32_t fmt;
 };
 
+// KVQ_DEBUG_CHECKS: validation of a call's device-side tables (kvq_check.hip)
+enum CheckKind { kCheckAppend = 0, kCheckDecode = 1, kCheckPrefill = 2, kCheckDequant = 3 };
+enum CheckCode { kCheckOk = 0, kBadSeqLen = 1, kBadPageId = 2, kBadCumulative = 3, kBadStartPos = 4, kBadChunk = 5 };
+struct CheckParams {
+  int32_t kind;
+  const int32_t* cu;           // append: cu_new; prefill: cu_q
+  const int32_t* start_pos;    // append
+  const int32_t* seq_lens;     // decode, prefill
+  const int32_t* block_table;  // append, decode, prefill
+  const int32_t* page_ids;     // dequant
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t max_pages;
+  int32_t max_len;             // decode / prefill: max_seq_len; append: max_new_tokens
+  int32_t max_q_len;           // prefill
+  int32_t n;                   // dequant: page ids
+  int64_t num_pages;
+};
+// Runs the check on `stream` and waits for it: *code is a CheckCode, *index the sequence or page
+// index of the first violation found.
+hipError_t run_check(const CheckParams& c, hipStream_t stream, int* code, int* index);
+
 hipError_t launch_append(const AppendParams& p, bool bf16, int had_block, int fmt, hipStream_t stream);
 DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len);
 size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int hkv, int group);

@@ -23,7 +23,15 @@
  *     global state, so calls are thread-safe; calls on one stream run in order.
  *   - Host-side argument checks run before any HIP call and return a negative kvq_status;
  *     kvq_last_error() then names the argument.  Device-side data (token counts, sequence
- *     lengths, page ids) is trusted: out-of-range values are undefined behaviour.
+ *     lengths, page ids) is trusted: out-of-range values are undefined behaviour -- except when
+ *     the environment variable KVQ_DEBUG_CHECKS is set (not "0"; read on every call): each
+ *     entry point then first validates its device tables on its stream (cu_new / cu_q
+ *     non-decreasing within [0, num_tokens]; 1 <= seq_lens <= max_seq_len; chunks no longer
+ *     than their sequence or max_q_len; start_pos >= 0 with the appended positions inside
+ *     max_pages*16; every block-table entry or page id the call reads inside [0, num_pages)),
+ *     waits for the verdict, and returns KVQ_ERR_INVALID_ARG naming the violation and its index
+ *     instead of launching.  That wait synchronizes the stream: a debugging aid, not for graph
+ *     capture.
  *   - A failed kernel launch returns KVQ_ERR_HIP with the HIP error text in kvq_last_error().
  *   - No C++ exception crosses this boundary.
  *
