@@ -31,7 +31,8 @@
  *     max_pages*16; every block-table entry or page id the call reads inside [0, num_pages)),
  *     waits for the verdict, and returns KVQ_ERR_INVALID_ARG naming the violation and its index
  *     instead of launching.  That wait synchronizes the stream: a debugging aid, not for graph
- *     capture.
+ *     capture.  The verdict lives in one slot per device, so checked calls on one device must
+ *     not overlap in time (on other streams or threads).
  *   - A failed kernel launch returns KVQ_ERR_HIP with the HIP error text in kvq_last_error().
  *   - No C++ exception crosses this boundary.
  *
