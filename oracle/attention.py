@@ -44,11 +44,14 @@ def gather_sequence(pool, block_table_row, seq_len: int, had_block: int, fmt: in
     n_pages = -(-seq_len // PAGE_SIZE)
     ks = np.empty((hkv, n_pages * PAGE_SIZE, HEAD_DIM))
     vs = np.empty_like(ks)
-    for j in range(n_pages):
-        page = int(block_table_row[j])
-        for g in range(hkv):
-            ks[g, j * PAGE_SIZE:(j + 1) * PAGE_SIZE] = dequant_block(pool[page, g], "k", fmt)
-            vs[g, j * PAGE_SIZE:(j + 1) * PAGE_SIZE] = dequant_block(pool[page, g], "v", fmt)
+    # whole pages are dequantized, then cut to seq_len: the slots past the sequence end hold
+    # whatever the pool held (possibly inf / NaN parameters), and are never attended
+    with np.errstate(invalid="ignore", over="ignore"):
+        for j in range(n_pages):
+            page = int(block_table_row[j])
+            for g in range(hkv):
+                ks[g, j * PAGE_SIZE:(j + 1) * PAGE_SIZE] = dequant_block(pool[page, g], "k", fmt)
+                vs[g, j * PAGE_SIZE:(j + 1) * PAGE_SIZE] = dequant_block(pool[page, g], "v", fmt)
     return ks[:, :seq_len], vs[:, :seq_len]
 
 
