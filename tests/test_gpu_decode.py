@@ -244,3 +244,16 @@ def test_dequant_pages_mxfp4():
     # e2m1 * 2^(E-127) is exact in fp32
     assert np.array_equal(k.cpu().numpy(), kr.astype(np.float32))
     assert np.array_equal(v.cpu().numpy(), vr.astype(np.float32))
+
+
+@pytest.mark.parametrize("group", [2, 3, 5, 6, 7])
+def test_decode_every_group_size(group):
+    # G need not be a power of two: heads past G in the 8 row pairs of the tiles stay unused
+    rng = np.random.default_rng(70 + group)
+    lens = [1, 33, 700]
+    pool, table = oracle_cache(rng, lens, 3, 64)
+    run_decode(f"int4/G{group}", pool, table, lens, 3 * group, 64, seed=group)
+    poolm, tablem = oracle_cache(rng, lens, 2, 128, fmt=oracle.FMT_MXFP4)
+    for scaled in (False, True):
+        run_decode(f"mxfp4/G{group}/scaled={scaled}", poolm, tablem, lens, 2 * group, 128, fmt=oracle.FMT_MXFP4,
+                   q_dtype="e4m3", seed=group, scaled_mfma=scaled)

@@ -230,3 +230,8 @@ def test_step_graph_replays_match_eager(fmt, rot, scaled):
         assert torch.equal(out, eager), f"replay {r} differs from the eager step"
         assert torch.equal(cache.pool, eager_pool), f"replay {r} wrote different bytes"
         del scratch
+
+
+@pytest.mark.parametrize("group", [3, 6])
+def test_step_odd_group_sizes(group):
+    run_step(f"int4/G{group}", [1, 16, 17, 300], hkv=2, group=group, hb=128, seed=90 + group)
