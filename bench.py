@@ -169,6 +169,51 @@ def time_graph_steps(every, single, steps, warmup):
     return wall, e0.elapsed_time(e1) * 1e3 / steps
 
 
+def time_long_decode(dev, replays=25):
+    """Long/ragged decode: 8 sequences with contexts ~ U{1024..32768}, 32 q / 8 kv heads,
+    Hadamard block 64, over a permuted shared page pool; kvq_decode_attn (decode kernel plus the
+    merge of split runs) on each of 8 layer caches in turn, captured in one HIP graph and replayed,
+    so host launch gaps are not timed."""
+    w = wl.WORKLOADS["long"]
+    caches, step, lens, _ = build_layers(w, 8, dev)
+    max_len = int(lens.max())
+    dbytes = decode_step_bytes(w, lens)
+    ws = kvq.make_workspace(caches[0], w.num_q_heads, w.batch, max_len, dev)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+
+    def all_layers():
+        for c in caches:
+            kvq.decode_attn(c, step["q"], step["lens"], step["bt"], max_len, out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        all_layers()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        all_layers()
+    for _ in range(max(2, replays // 5)):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (replays * len(caches))
+    gbps = dbytes / us / 1e3
+    res = {"workload": "batch 8, contexts U{1024..32768} (seeded), 32 q / 8 kv heads, INT4, Hadamard block 64, "
+                       "permuted shared pool, 8 layer caches in one HIP graph",
+           "sum_context": int(lens.sum()), "max_context": max_len, "us_per_decode": round(us, 3),
+           "algorithmic_bytes": dbytes, "GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    del g, caches, step
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_mxfp4_decode(dev, repeats=40):
     """MXFP4 decode, 64 x 16K contexts, 64 q / 8 kv heads, fp8 e4m3 queries, over 2 alternating
     pools (2.3 GB, beyond the Infinity Cache): q.K on f16 tiles vs the scaled FP8 x FP4 MFMA."""
@@ -509,6 +554,8 @@ def main():
         res["prefill_append"]["traffic"] = traffic_entry(res["prefill_append"]["algorithmic_bytes"],
                                                          APPEND_TRAFFIC_FILE, APPEND_SRC, "append_source_sha256")
         torch.cuda.empty_cache()
+    log("[bench] long/ragged decode")
+    res["long_ragged_decode"] = time_long_decode(dev, replays=5 if args.profile_run else 25)
     if not args.no_mxfp4 and not args.profile_run:
         log("[bench] MXFP4 decode (f16-tile and scaled-MFMA q.K)")
         res["mxfp4_decode"] = time_mxfp4_decode(dev)

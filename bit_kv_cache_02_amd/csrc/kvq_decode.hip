@@ -60,7 +60,63 @@ struct DecodeSmem {
   uint8_t acode[2][kHeadDim];
   uint32_t arow[2][16];
   uint32_t aparam[2];
+  // balanced cut: wave totals of the block scans, and the piece this workgroup takes
+  int red[16];
+  int cut[4];
 };
+
+// Exclusive prefix sum of v over the workgroup's threads (in thread order); *total gets the sum.
+// Every thread of the workgroup (nw waves) must call it; red holds one int per wave.
+__device__ __forceinline__ int block_scan_excl(int v, int nw, int* red, int* total) {
+  const int lane = lane_id(), wave = thread_id() >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(x, d);
+    if (lane >= d) x += t;
+  }
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  int before = 0, sum = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int r = red[w];
+    before += w < wave ? r : 0;
+    sum += r;
+  }
+  __syncthreads();  // red is free again for the next scan
+  *total = sum;
+  return before + x - v;
+}
+
+// The balanced cut, computed alike by every workgroup of the decode kernel and of the merge
+// kernel from seq_lens: sequence b has np_b pages; with T = hkv * sum(np_b) and
+// C = max(ceil(T / slots), min_piece), each of its kv heads is cut into n_b = ceil(np_b / C)
+// pieces, piece j holding pages [j np_b / n_b, (j+1) np_b / n_b).  Pieces are numbered in
+// (sequence, kv head, piece) order; sequence b's first is hkv * sum_{b' < b} n_b'.
+// by_seq: find sequence `key`; otherwise the sequence whose pieces hold piece number `key`.
+// cut[] receives {sequence or -1, its first piece, n_b, np_b}.  One thread per sequence: the
+// workgroup's nw waves cover num_seqs.
+__device__ __forceinline__ void balanced_cut(const DecodeParams& a, int key, bool by_seq, int nw, int* red,
+                                             int* cut) {
+  const int t = thread_id();
+  const int L = t < a.num_seqs ? a.seq_lens[t] : 0;
+  const int np = (max(L, 0) + kPage - 1) / kPage;
+  if (t == 0) cut[0] = -1;
+  int total;
+  block_scan_excl(np, nw, red, &total);
+  const int64_t T = (int64_t)total * a.hkv;
+  const int C = max((int)((T + a.plan.slots - 1) / a.plan.slots), a.plan.min_piece);
+  const int n = (np + C - 1) / C;
+  int ntotal;
+  const int first = block_scan_excl(n, nw, red, &ntotal) * a.hkv;
+  if (t < a.num_seqs && (by_seq ? t == key : (n > 0 && key >= first && key < first + a.hkv * n))) {
+    cut[0] = t;
+    cut[1] = first;
+    cut[2] = n;
+    cut[3] = np;
+  }
+  __syncthreads();
+}
 
 // Fused step: put the appended token's bytes (staged in LDS) into the registers of the page that
 // holds it, whatever the page load returned for that slot.
@@ -101,16 +157,36 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   const int tid = thread_id();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nsplit = a.plan.nsplit;
-  const int P = a.plan.pages_per_split;
-  // split-major order: every unit's first split is dispatched before any second split, so the
-  // workgroups that have pages spread over the CUs and the empty ones (splits past a short
-  // sequence's end) come last and exit at once
-  const int units = a.num_seqs * a.hkv;
-  const int split = block_id_x() / units;
-  const int unit = block_id_x() % units;
-  const int kvh = unit % a.hkv;
-  const int b = unit / a.hkv;
+  // This workgroup's run: pages [p_begin, p_begin + span) of (sequence b, kv head kvh), one of
+  // the unit's runs; its partial goes to workspace slot `slot`.
+  int b, kvh, p_begin, span, pieces_cut = 0;
+  int64_t slot;
+  if (a.plan.balanced) {
+    balanced_cut(a, block_id_x(), false, W, sm.red, sm.cut);
+    if (sm.cut[0] < 0) return;  // past the last piece (uniform: read from LDS after a barrier)
+    b = __builtin_amdgcn_readfirstlane(sm.cut[0]);
+    const int r = block_id_x() - __builtin_amdgcn_readfirstlane(sm.cut[1]);
+    const int nb = __builtin_amdgcn_readfirstlane(sm.cut[2]), np = __builtin_amdgcn_readfirstlane(sm.cut[3]);
+    kvh = r / nb;
+    const int j = r - kvh * nb;
+    p_begin = (int)((int64_t)j * np / nb);
+    // at most 64 W pages by the plan; the clamp keeps lengths beyond the host hint in bounds
+    span = min((int)((int64_t)(j + 1) * np / nb) - p_begin, 64 * W);
+    pieces_cut = nb;
+    slot = block_id_x();
+  } else {
+    // split-major order: every unit's first split is dispatched before any second split, so the
+    // workgroups that have pages spread over the CUs and the empty ones (splits past a short
+    // sequence's end) come last and exit at once
+    const int units = a.num_seqs * a.hkv;
+    const int split = block_id_x() / units;
+    const int unit = block_id_x() % units;
+    kvh = unit % a.hkv;
+    b = unit / a.hkv;
+    p_begin = split * a.plan.pages_per_split;
+    span = a.plan.pages_per_split;
+    slot = (int64_t)unit * a.plan.nsplit + split;
+  }
   const int G = a.group;
   const int n = lane & 15;   // token (QK, softmax) / output column (p.V)
   const int jg = lane >> 4;  // row group: heads 2jg, 2jg+1
@@ -137,12 +213,11 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       qshift[k][e] = 8 * (byte & 3);
     }
   }
-  const int p_begin = split * P;
   const int pw0 = p_begin + wave;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const int bt_idx = pw0 + W * lane;
   const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(bt, a.max_pages * 4);
-  const int pid_vec = (int)__builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, lane * W < P ? 4 * bt_idx : kOutOfRange, 0, 0);
+  const int pid_vec = (int)__builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, lane * W < span ? 4 * bt_idx : kOutOfRange, 0, 0);
 
   // Fused step: the workgroup that holds the sequence's last page appends the new token there,
   // wave W-1 the K vector and wave W-2 the V vector (their words load here; every wave issues
@@ -150,7 +225,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   const int n_pages = (L + kPage - 1) / kPage;
   const int last_pg = n_pages - 1;
   const int app_slot = (L - 1) & (kPage - 1);
-  const bool app_wg = a.append && last_pg >= p_begin && last_pg < p_begin + P;
+  const bool app_wg = a.append && last_pg >= p_begin && last_pg < p_begin + span;
   const int app_which = wave == W - 1 ? 0 : 1;  // 0: K, 1: V
   const bool app_wave = app_wg && wave >= W - 2;
   uint32_t nword[2];
@@ -178,11 +253,11 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   __builtin_amdgcn_sched_barrier(0);
 
   if (p_begin >= n_pages) return;  // uniform over the workgroup
-  const int p_end = min(p_begin + P, n_pages);
-  const int nsplit_b = (n_pages + P - 1) / P;
+  const int p_end = min(p_begin + span, n_pages);
+  const int pieces = a.plan.balanced ? pieces_cut : (n_pages + span - 1) / span;  // runs of this unit
 
   // ---- 1. this wave's pages; start the first loads before the query math ----
-  const int npw = max(0, (p_end - pw0 + W - 1) / W);  // <= 64 (planned: P <= 64 W)
+  const int npw = max(0, (p_end - pw0 + W - 1) / W);  // <= 64 (span <= 64 W)
   const uint8_t* pool_h = a.pool + (int64_t)kvh * kPageHeadBytes;
   const int64_t page_stride = (int64_t)a.hkv * kPageHeadBytes;
   auto page_base = [&](int i) {
@@ -388,7 +463,6 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   __syncthreads();
 
   // ---- 5. merge the waves (wave w handles heads w, w+W, ...); finish, or write the split partial ----
-  const int64_t slot = (int64_t)unit * nsplit + split;
   for (int g = wave; g < G; g += W) {
     float M = sm.wm[0][g];
 #pragma unroll
@@ -401,7 +475,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       O1 = fmaf(f, sm.wo[w][g][lane + 64], O1);
       Ls = fmaf(f, sm.wl[w][g], Ls);
     }
-    if (nsplit_b == 1) {
+    if (pieces == 1) {
       store_head(a, O0 / Ls, O1 / Ls, b, kvh * G + g, lane);
     } else {
       float* po = a.part_o + (slot * G + g) * kHeadDim;
@@ -416,54 +490,63 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
 }
 
 // Merge the split partials of every (sequence, kv head) that was split, rotate back, store.
-// One workgroup per (sequence, kv head); wave w handles heads w, w+4, ...  Lane s takes split s
-// for the running maxima and weights (64 splits per pass); the partial outputs are then summed
-// with lanes over channels, four splits' loads in flight at a time.
+// One workgroup per (sequence, kv head); wave w handles heads w, w+4, ...  The partials are taken
+// 16 at a time: lane j < 16 loads partial j's running maximum and weight while every lane loads
+// its two channels of all 16 partial outputs, all in one round of loads; the passes merge
+// online (rescaled by the change of maximum), so a unit of at most 16 runs costs one round trip.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams a) {
+  constexpr int kBatch = 16;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(thread_id() >> 6);
   const int unit = block_id_x();
   const int kvh = unit % a.hkv, b = unit / a.hkv;
   const int G = a.group;
-  const int P = a.plan.pages_per_split;
-  const int n_pages = (a.seq_lens[b] + kPage - 1) / kPage;
-  const int nsplit_b = (n_pages + P - 1) / P;
+  int nsplit_b;  // runs of this unit, in slots s0 .. s0 + nsplit_b - 1
+  int64_t s0;
+  if (a.plan.balanced) {
+    __shared__ int red[4], cut[4];
+    balanced_cut(a, b, true, 4, red, cut);
+    nsplit_b = __builtin_amdgcn_readfirstlane(cut[2]);
+    s0 = __builtin_amdgcn_readfirstlane(cut[1]) + (int64_t)kvh * nsplit_b;
+  } else {
+    const int P = a.plan.pages_per_split;
+    const int n_pages = (a.seq_lens[b] + kPage - 1) / kPage;
+    nsplit_b = (n_pages + P - 1) / P;
+    s0 = (int64_t)unit * a.plan.nsplit;
+  }
   if (nsplit_b <= 1) return;
-  const int64_t s0 = (int64_t)unit * a.plan.nsplit;
   for (int g = wave; g < G; g += 4) {
-    const float* ml = a.part_ml + (s0 * G + g) * 2;  // split s at ml[2 G s]
-    float M = kNegBig;
-    for (int s = lane; s < nsplit_b; s += 64) M = fmaxf(M, ml[2 * G * s]);
-    M = wave_max(M);
-    float O0 = 0.f, O1 = 0.f, Lp = 0.f;
-    for (int c = 0; c < nsplit_b; c += 64) {
-      const int s = c + lane;
-      const float f = s < nsplit_b ? exp2f(ml[2 * G * s] - M) : 0.0f;
-      if (s < nsplit_b) Lp = fmaf(f, ml[2 * G * s + 1], Lp);
-      const int cnt = min(64, nsplit_b - c);
+    float M = kNegBig, Ls = 0.f, O0 = 0.f, O1 = 0.f;
+    for (int c = 0; c < nsplit_b; c += kBatch) {
+      const int cnt = min(kBatch, nsplit_b - c);
+      // partial j of this pass at slot s0 + c + j; indexes past the unit's last run re-read it
+      // and get weight 0
+      const int jl = min(lane, cnt - 1);
+      const float* ml = a.part_ml + ((s0 + c + jl) * G + g) * 2;
+      const float mj = ml[0], lj = ml[1];
       const float* po = a.part_o + ((s0 + c) * G + g) * kHeadDim;
-      int j = 0;
-      for (; j + 4 <= cnt; j += 4) {
-        float x[4][2];
+      float x[kBatch][2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          x[u][0] = po[(j + u) * G * kHeadDim + lane];
-          x[u][1] = po[(j + u) * G * kHeadDim + lane + 64];
-        }
+      for (int u = 0; u < kBatch; ++u) {
+        const int ju = min(u, cnt - 1);
+        x[u][0] = po[(int64_t)ju * G * kHeadDim + lane];
+        x[u][1] = po[(int64_t)ju * G * kHeadDim + lane + 64];
+      }
+      const float mv = lane < cnt ? mj : kNegBig;
+      const float Mn = fmaxf(M, wave_max(mv));
+      const float r = exp2f(M - Mn);
+      const float f = lane < cnt ? exp2f(mj - Mn) : 0.0f;
+      Ls = fmaf(Ls, r, wave_sum_f(f * lj));
+      O0 *= r;
+      O1 *= r;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j + u));
-          O0 = fmaf(fj, x[u][0], O0);
-          O1 = fmaf(fj, x[u][1], O1);
-        }
+      for (int u = 0; u < kBatch; ++u) {
+        const float fu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u));
+        O0 = fmaf(fu, x[u][0], O0);
+        O1 = fmaf(fu, x[u][1], O1);
       }
-      for (; j < cnt; ++j) {
-        const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
-        O0 = fmaf(fj, po[j * G * kHeadDim + lane], O0);
-        O1 = fmaf(fj, po[j * G * kHeadDim + lane + 64], O1);
-      }
+      M = Mn;
     }
-    const float Ls = wave_sum_f(Lp);
     store_head(a, O0 / Ls, O1 / Ls, b, kvh * G + g, lane);
   }
 }
@@ -475,9 +558,15 @@ DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len) {
   // One (sequence, kv head) per CU (at most 256 units of at most 512 pages): 8-wave workgroups,
   // no split.  More units or longer sequences than that: 4-wave workgroups over 256-page splits,
   // three of which share a CU, so that one workgroup's start and end latency overlap another's
-  // streaming.  Narrow batches of long sequences: 4-wave workgroups over 128-page splits (halved
-  // until the grid has 512 workgroups).  Measured on the decode workloads of the benchmark.
+  // streaming.  Narrow batches (fewer than 256 units) with enough pages to fill the chip (at
+  // least 64 per CU at the longest length): the balanced cut, 4-wave workgroups, two per CU, two
+  // pages in flight per wave; slots = 512 minus one per unit (the most the cut can add by rounding
+  // up per unit), so that the pieces fit two workgroups per CU.  Smaller narrow batches: fixed
+  // 128-page splits, halved until the grid has 512 workgroups (the cut would cost one more
+  // dependent load, of seq_lens, before a workgroup knows its pages).  Measured on the decode
+  // workloads of the benchmark.
   int W, P;
+  bool balanced = false;
   if (units >= 256 && units * ((max_pg + 511) / 512) <= 256) {
     W = 8;
     P = 512;
@@ -488,23 +577,48 @@ DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len) {
     W = 4;
     P = 128;
     while (P > 16 && units * ((max_pg + P - 1) / P) < 512) P /= 2;
+    balanced = units * max_pg >= 256 * 64;
   }
-  int D = 3;
   // tuning overrides (read on every call, so a sweep can change them between calls)
   const char* ew = getenv("KVQ_DECODE_WAVES");
   const char* ep = getenv("KVQ_DECODE_PAGES_PER_SPLIT");
   const char* ed = getenv("KVQ_DECODE_DEPTH");
+  const char* eb = getenv("KVQ_DECODE_BALANCED");
+  const char* es = getenv("KVQ_DECODE_SLOTS");
+  const char* em = getenv("KVQ_DECODE_MIN_PIECE");
   const int env_w = ew ? atoi(ew) : 0, env_p = ep ? atoi(ep) : 0, env_d = ed ? atoi(ed) : 0;
   if (env_w) W = env_w;
   if (env_p) P = env_p;
-  if (env_d) D = env_d;
+  if (eb) balanced = atoi(eb) != 0;
   if (W != 4 && W != 8 && W != 16) W = 8;
+  // the cut runs one thread per sequence
+  if (balanced && (max_pg <= 0 || num_seqs > 64 * W || num_seqs > 256)) balanced = false;
+  int D = env_d ? env_d : (balanced ? 2 : 3);
   if (D != 2 && D != 3 && D != 4) D = 3;
   if (W == 16) D = 2;  // register budget of 1024-thread workgroups
   if (P > 64 * W) P = 64 * W;
   if (P < 1) P = 1;
   plan.waves = W;
   plan.depth = D;
+  plan.balanced = balanced ? 1 : 0;
+  plan.slots = 0;
+  plan.min_piece = 0;
+  if (balanced) {
+    int64_t S = es ? atoll(es) : 512 - units;
+    int mp = em ? atoi(em) : 16;
+    mp = mp < 1 ? 1 : (mp > 64 * W ? 64 * W : mp);
+    // a piece holds at most 64 W pages (one block-table entry per lane of each wave): enough slots
+    // that ceil(total / slots) stays within that for any lengths up to max_seq_len (the grid then
+    // rounded up to whole rounds of 256 workgroups)
+    const int64_t need = (units * max_pg + 64 * W - 1) / (64 * W);
+    if (S < need) S = (need + units + 255) / 256 * 256 - units;
+    if (S < 1) S = 1;
+    plan.slots = (int32_t)S;
+    plan.min_piece = mp;
+    plan.pages_per_split = 64 * W;
+    plan.nsplit = (int32_t)((S + units + units - 1) / units);
+    return plan;
+  }
   plan.pages_per_split = P;
   plan.nsplit = max_pg > 0 ? (max_pg + P - 1) / P : 1;
   return plan;

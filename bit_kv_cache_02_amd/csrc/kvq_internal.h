@@ -25,10 +25,16 @@ struct AppendParams {
 };
 
 struct DecodePlan {
-  int32_t pages_per_split;  // pages one workgroup handles
-  int32_t nsplit;           // workgroups per (sequence, kv head)
+  int32_t pages_per_split;  // pages one workgroup handles (fixed splits)
+  int32_t nsplit;           // workgroups per (sequence, kv head); the grid is units * nsplit
   int32_t waves;            // waves per workgroup
   int32_t depth;            // pages in flight per wave (register prefetch pipeline)
+  // Balanced cut (narrow batches): the units are cut on the device, from seq_lens, into
+  // near-equal pieces of at most C = max(ceil(total pages / slots), min_piece) pages; workgroup
+  // k takes piece k.  units * nsplit >= slots + units covers every cut.
+  int32_t balanced;
+  int32_t slots;
+  int32_t min_piece;
 };
 
 struct DecodeParams {
