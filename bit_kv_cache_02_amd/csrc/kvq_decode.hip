@@ -24,9 +24,10 @@
 // is the B-operand shape of the p.V MFMA, so one 16-byte load per lane feeds it directly.
 // Each wave streams its pages through a register prefetch pipeline (the query loads and the
 // first page loads are issued before anything waits).  The waves' partials merge in LDS; when a
-// (sequence, kv head) is split over several workgroups, a second small kernel merges the split
-// partials.  The query rotation and the final rotation back run in fp32 in registers, one head per
-// wave, with lane shuffles for the cross-lane butterfly stages.
+// (sequence, kv head) is split over several workgroups, each writes its partial and the last to
+// finish merges them all (a counter per unit in the workspace).  The query rotation and the final
+// rotation back run in fp32 in registers, one head per wave, with lane shuffles for the
+// cross-lane butterfly stages.
 #include "kvq_attn.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -63,7 +64,20 @@ struct DecodeSmem {
   // balanced cut: wave totals of the block scans, and the piece this workgroup takes
   int red[16];
   int cut[4];
+  int last;  // this workgroup finished its unit's last run: it merges the unit
 };
+
+// Split partials cross workgroups, possibly on other XCDs (each with its own L2), within one
+// launch.  They are written and read as relaxed agent-scope atomics: the stores write through
+// to the device-coherent level and the loads read from it, so no L2 write-back or invalidate
+// of the whole cache is needed.  A writer waits for its stores to complete before it counts
+// its run done; the merging workgroup loads only after its count came back as the last.
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Exclusive prefix sum of v over the workgroup's threads (in thread order); *total gets the sum.
 // Every thread of the workgroup (nw waves) must call it; red holds one int per wave.
@@ -88,16 +102,14 @@ __device__ __forceinline__ int block_scan_excl(int v, int nw, int* red, int* tot
   return before + x - v;
 }
 
-// The balanced cut, computed alike by every workgroup of the decode kernel and of the merge
-// kernel from seq_lens: sequence b has np_b pages; with T = hkv * sum(np_b) and
+// The balanced cut, computed alike by every workgroup from seq_lens: sequence b has np_b pages;
+// with T = hkv * sum(np_b) and
 // C = max(ceil(T / slots), min_piece), each of its kv heads is cut into n_b = ceil(np_b / C)
 // pieces, piece j holding pages [j np_b / n_b, (j+1) np_b / n_b).  Pieces are numbered in
 // (sequence, kv head, piece) order; sequence b's first is hkv * sum_{b' < b} n_b'.
-// by_seq: find sequence `key`; otherwise the sequence whose pieces hold piece number `key`.
-// cut[] receives {sequence or -1, its first piece, n_b, np_b}.  One thread per sequence: the
-// workgroup's nw waves cover num_seqs.
-__device__ __forceinline__ void balanced_cut(const DecodeParams& a, int key, bool by_seq, int nw, int* red,
-                                             int* cut) {
+// cut[] receives {sequence whose pieces hold piece number `key` (or -1), its first piece, n_b,
+// np_b}.  One thread per sequence: the workgroup's nw waves cover num_seqs.
+__device__ __forceinline__ void balanced_cut(const DecodeParams& a, int key, int nw, int* red, int* cut) {
   const int t = thread_id();
   const int L = t < a.num_seqs ? a.seq_lens[t] : 0;
   const int np = (max(L, 0) + kPage - 1) / kPage;
@@ -109,7 +121,7 @@ __device__ __forceinline__ void balanced_cut(const DecodeParams& a, int key, boo
   const int n = (np + C - 1) / C;
   int ntotal;
   const int first = block_scan_excl(n, nw, red, &ntotal) * a.hkv;
-  if (t < a.num_seqs && (by_seq ? t == key : (n > 0 && key >= first && key < first + a.hkv * n))) {
+  if (t < a.num_seqs && n > 0 && key >= first && key < first + a.hkv * n) {
     cut[0] = t;
     cut[1] = first;
     cut[2] = n;
@@ -147,7 +159,54 @@ __device__ __forceinline__ void store_head(const DecodeParams& a, float o0, floa
             lane);
 }
 
+// Merge the partials of one (sequence, kv head)'s runs, in slots s0 .. s0 + n - 1, for heads
+// wave, wave + nw, ...; rotate back and store.  The partials are taken 16 at a time: lane j < 16
+// loads partial j's running maximum and weight while every lane loads its two channels of all
+// 16 partial outputs, all in one round of loads; the passes merge online (rescaled by the
+// change of maximum), so a unit of at most 16 runs costs one round trip.
+__device__ __forceinline__ void merge_runs(const DecodeParams& a, int64_t s0, int n, int b, int kvh, int wave,
+                                           int nw) {
+  constexpr int kBatch = 16;
+  const int lane = lane_id();
+  const int G = a.group;
+  for (int g = wave; g < G; g += nw) {
+    float M = kNegBig, Ls = 0.f, O0 = 0.f, O1 = 0.f;
+    for (int c = 0; c < n; c += kBatch) {
+      const int cnt = min(kBatch, n - c);
+      // partial j of this pass at slot s0 + c + j; indexes past the unit's last run re-read it
+      // and get weight 0
+      const int jl = min(lane, cnt - 1);
+      const float* ml = a.part_ml + ((s0 + c + jl) * G + g) * 2;
+      const float mj = ld_coherent(ml), lj = ld_coherent(ml + 1);
+      const float* po = a.part_o + ((s0 + c) * G + g) * kHeadDim;
+      float x[kBatch][2];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int ju = min(u, cnt - 1);
+        x[u][0] = ld_coherent(po + (int64_t)ju * G * kHeadDim + lane);
+        x[u][1] = ld_coherent(po + (int64_t)ju * G * kHeadDim + lane + 64);
+      }
+      const float mv = lane < cnt ? mj : kNegBig;
+      const float Mn = fmaxf(M, wave_max(mv));
+      const float r = exp2f(M - Mn);
+      const float f = lane < cnt ? exp2f(mj - Mn) : 0.0f;
+      Ls = fmaf(Ls, r, wave_sum_f(f * lj));
+      O0 *= r;
+      O1 *= r;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float fu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u));
+        O0 = fmaf(fu, x[u][0], O0);
+        O1 = fmaf(fu, x[u][1], O1);
+      }
+      M = Mn;
+    }
+    store_head(a, O0 / Ls, O1 / Ls, b, kvh * G + g, lane);
+  }
+}
+
 }  // namespace
+
 
 // FMT: 0 INT4; 1 MXFP4 (f16 tiles); 2 MXFP4 with q.K on the scaled FP8 x FP4 matrix cores
 template <int FMT, int W, int D>
@@ -160,9 +219,9 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   // This workgroup's run: pages [p_begin, p_begin + span) of (sequence b, kv head kvh), one of
   // the unit's runs; its partial goes to workspace slot `slot`.
   int b, kvh, p_begin, span, pieces_cut = 0;
-  int64_t slot;
+  int64_t slot, unit_s0;  // this run's slot and the unit's first
   if (a.plan.balanced) {
-    balanced_cut(a, block_id_x(), false, W, sm.red, sm.cut);
+    balanced_cut(a, block_id_x(), W, sm.red, sm.cut);
     if (sm.cut[0] < 0) return;  // past the last piece (uniform: read from LDS after a barrier)
     b = __builtin_amdgcn_readfirstlane(sm.cut[0]);
     const int r = block_id_x() - __builtin_amdgcn_readfirstlane(sm.cut[1]);
@@ -174,6 +233,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
     span = min((int)((int64_t)(j + 1) * np / nb) - p_begin, 64 * W);
     pieces_cut = nb;
     slot = block_id_x();
+    unit_s0 = slot - j;
   } else {
     // split-major order: every unit's first split is dispatched before any second split, so the
     // workgroups that have pages spread over the CUs and the empty ones (splits past a short
@@ -186,6 +246,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
     p_begin = split * a.plan.pages_per_split;
     span = a.plan.pages_per_split;
     slot = (int64_t)unit * a.plan.nsplit + split;
+    unit_s0 = (int64_t)unit * a.plan.nsplit;
   }
   const int G = a.group;
   const int n = lane & 15;   // token (QK, softmax) / output column (p.V)
@@ -254,7 +315,9 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
 
   if (p_begin >= n_pages) return;  // uniform over the workgroup
   const int p_end = min(p_begin + span, n_pages);
-  const int pieces = a.plan.balanced ? pieces_cut : (n_pages + span - 1) / span;  // runs of this unit
+  // runs of this unit (fixed splits: lengths beyond the host hint are cut off at the grid, so
+  // that every counted run exists)
+  const int pieces = a.plan.balanced ? pieces_cut : min((n_pages + span - 1) / span, a.plan.nsplit);
 
   // ---- 1. this wave's pages; start the first loads before the query math ----
   const int npw = max(0, (p_end - pw0 + W - 1) / W);  // <= 64 (span <= 64 W)
@@ -479,76 +542,28 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       store_head(a, O0 / Ls, O1 / Ls, b, kvh * G + g, lane);
     } else {
       float* po = a.part_o + (slot * G + g) * kHeadDim;
-      po[lane] = O0;
-      po[lane + 64] = O1;
+      st_coherent(po + lane, O0);
+      st_coherent(po + lane + 64, O1);
       if (lane == 0) {
-        a.part_ml[(slot * G + g) * 2 + 0] = M;
-        a.part_ml[(slot * G + g) * 2 + 1] = Ls;
+        st_coherent(a.part_ml + (slot * G + g) * 2 + 0, M);
+        st_coherent(a.part_ml + (slot * G + g) * 2 + 1, Ls);
       }
     }
   }
-}
+  if (pieces == 1) return;
 
-// Merge the split partials of every (sequence, kv head) that was split, rotate back, store.
-// One workgroup per (sequence, kv head); wave w handles heads w, w+4, ...  The partials are taken
-// 16 at a time: lane j < 16 loads partial j's running maximum and weight while every lane loads
-// its two channels of all 16 partial outputs, all in one round of loads; the passes merge
-// online (rescaled by the change of maximum), so a unit of at most 16 runs costs one round trip.
-__global__ __launch_bounds__(256) void combine_kernel(DecodeParams a) {
-  constexpr int kBatch = 16;
-  const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(thread_id() >> 6);
-  const int unit = block_id_x();
-  const int kvh = unit % a.hkv, b = unit / a.hkv;
-  const int G = a.group;
-  int nsplit_b;  // runs of this unit, in slots s0 .. s0 + nsplit_b - 1
-  int64_t s0;
-  if (a.plan.balanced) {
-    __shared__ int red[4], cut[4];
-    balanced_cut(a, b, true, 4, red, cut);
-    nsplit_b = __builtin_amdgcn_readfirstlane(cut[2]);
-    s0 = __builtin_amdgcn_readfirstlane(cut[1]) + (int64_t)kvh * nsplit_b;
-  } else {
-    const int P = a.plan.pages_per_split;
-    const int n_pages = (a.seq_lens[b] + kPage - 1) / kPage;
-    nsplit_b = (n_pages + P - 1) / P;
-    s0 = (int64_t)unit * a.plan.nsplit;
+  // ---- 6. the unit's last run to finish merges all of its runs' partials ----
+  // Counting wraps at the unit's number of runs, so the counter is back at zero after the last.
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t done = __builtin_amdgcn_atomic_inc32(a.counters + (b * a.hkv + kvh), (uint32_t)(pieces - 1),
+                                                        __ATOMIC_RELAXED, "agent");
+    sm.last = done == (uint32_t)(pieces - 1);
   }
-  if (nsplit_b <= 1) return;
-  for (int g = wave; g < G; g += 4) {
-    float M = kNegBig, Ls = 0.f, O0 = 0.f, O1 = 0.f;
-    for (int c = 0; c < nsplit_b; c += kBatch) {
-      const int cnt = min(kBatch, nsplit_b - c);
-      // partial j of this pass at slot s0 + c + j; indexes past the unit's last run re-read it
-      // and get weight 0
-      const int jl = min(lane, cnt - 1);
-      const float* ml = a.part_ml + ((s0 + c + jl) * G + g) * 2;
-      const float mj = ml[0], lj = ml[1];
-      const float* po = a.part_o + ((s0 + c) * G + g) * kHeadDim;
-      float x[kBatch][2];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int ju = min(u, cnt - 1);
-        x[u][0] = po[(int64_t)ju * G * kHeadDim + lane];
-        x[u][1] = po[(int64_t)ju * G * kHeadDim + lane + 64];
-      }
-      const float mv = lane < cnt ? mj : kNegBig;
-      const float Mn = fmaxf(M, wave_max(mv));
-      const float r = exp2f(M - Mn);
-      const float f = lane < cnt ? exp2f(mj - Mn) : 0.0f;
-      Ls = fmaf(Ls, r, wave_sum_f(f * lj));
-      O0 *= r;
-      O1 *= r;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float fu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u));
-        O0 = fmaf(fu, x[u][0], O0);
-        O1 = fmaf(fu, x[u][1], O1);
-      }
-      M = Mn;
-    }
-    store_head(a, O0 / Ls, O1 / Ls, b, kvh * G + g, lane);
-  }
+  __syncthreads();
+  if (!sm.last) return;
+  merge_runs(a, unit_s0, pieces, b, kvh, wave, W);
 }
 
 DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len) {
@@ -626,16 +641,28 @@ DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace: [counters][part_ml][part_o], each part 256-byte aligned.  The counter region has
+// the same size (room for kCounterUnits units) for every call with at most that many units, so
+// such calls share one layout and a call never finds another call's partials where it expects
+// zeroed counters.
+constexpr size_t kCounterUnits = 16384;
+
+static size_t counter_bytes(size_t units) { return align256(4 * (units > kCounterUnits ? units : kCounterUnits)); }
+
 size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int hkv, int group) {
   if (plan.nsplit <= 1) return 0;
-  const size_t slots = (size_t)num_seqs * hkv * plan.nsplit;
-  return align256(slots * group * 2 * 4) + slots * group * kHeadDim * 4;
+  const size_t units = (size_t)num_seqs * hkv;
+  const size_t slots = units * plan.nsplit;
+  return counter_bytes(units) + align256(slots * group * 2 * 4) + slots * group * kHeadDim * 4;
 }
 
 void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, int group, float** part_ml,
-                     float** part_o) {
-  const size_t slots = (size_t)num_seqs * hkv * plan.nsplit;
+                     float** part_o, uint32_t** counters) {
+  const size_t units = (size_t)num_seqs * hkv;
+  const size_t slots = units * plan.nsplit;
   uint8_t* p = (uint8_t*)ws;
+  *counters = (uint32_t*)p;
+  p += counter_bytes(units);
   *part_ml = (float*)p;
   p += align256(slots * group * 2 * 4);
   *part_o = (float*)p;
@@ -659,9 +686,6 @@ hipError_t launch_decode(const DecodeParams& p, int variant, hipStream_t stream)
   KVQ_DECODE_CASE(2, 8, 2) KVQ_DECODE_CASE(2, 8, 3) KVQ_DECODE_CASE(2, 8, 4)
   KVQ_DECODE_CASE(2, 16, 2) { return hipErrorInvalidValue; }
 #undef KVQ_DECODE_CASE
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.plan.nsplit <= 1) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)units), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -214,7 +214,7 @@ static int decode_common(const kvq_cache* cache, const void* knew, const void* v
     if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (workspace_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes given, %zu required", workspace_bytes, need);
     if (((uintptr_t)workspace) & 255) return fail(KVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    kvq::carve_workspace(workspace, plan, num_seqs, hkv, group, &p.part_ml, &p.part_o);
+    kvq::carve_workspace(workspace, plan, num_seqs, hkv, group, &p.part_ml, &p.part_o, &p.counters);
   }
   p.pool = (uint8_t*)cache->pool;
   p.q = q;

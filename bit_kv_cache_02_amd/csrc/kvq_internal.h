@@ -45,6 +45,7 @@ struct DecodeParams {
   void* out;
   float* part_o;     // [units][nsplit][G][128] split partials (unnormalised o')
   float* part_ml;    // [units][nsplit][G][2]   running max (log2 domain) and sum
+  uint32_t* counters;  // [units] runs finished; zero between calls (each call wraps it back)
   int32_t hkv;
   int32_t group;     // q heads per kv head (1..8)
   int32_t hq;
@@ -131,7 +132,7 @@ hipError_t launch_append(const AppendParams& p, bool bf16, int had_block, int fm
 DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len);
 size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int hkv, int group);
 void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, int group, float** part_ml,
-                     float** part_o);
+                     float** part_o, uint32_t** counters);
 // variant: 0 INT4, 1 MXFP4, 2 MXFP4 with q.K on the scaled FP8 x FP4 matrix cores
 hipError_t launch_decode(const DecodeParams& p, int variant, hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);

@@ -179,11 +179,12 @@ def decode_workspace_bytes(cache: Cache, num_q_heads: int, num_seqs: int, max_se
 
 
 def make_workspace(cache: Cache, num_q_heads: int, num_seqs: int, max_seq_len: int, device="cuda"):
-    """Workspace for kvq_decode_attn / kvq_decode_step (None when none is needed)."""
+    """Workspace for kvq_decode_attn / kvq_decode_step (None when none is needed), zero-filled as
+    the library requires before its first use (the calls leave it zeroed)."""
     n = decode_workspace_bytes(cache, num_q_heads, num_seqs, max_seq_len)
     if n == 0:
         return None
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def _flags(rotated: bool, scaled_mfma: bool) -> int:

@@ -138,9 +138,15 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t kv_
 /*
  * Bytes of workspace kvq_decode_attn and kvq_decode_step need for these sizes (same
  * arguments as there).  The workspace holds the partial results of (sequence, kv head) pairs
- * split over several workgroups; it needs no initialisation and its contents between calls
- * are meaningless.  Returns 0 when no workspace is needed (then `workspace` may be NULL), or
- * (size_t)-1 on invalid arguments.
+ * split over several workgroups and one counter per pair, which the last of a pair's
+ * workgroups to finish uses to know that it merges the partials.  It must be zero-filled once
+ * before its first use (e.g. hipMemset when it is allocated).  Every call leaves its counters
+ * at zero again, and the counters have the same place for every call of at most 16384 (sequence,
+ * kv head) pairs, so a workspace serves any number of later such calls, of any sizes that fit
+ * it, without being cleared.  Clear it again before a call with more pairs than that if it
+ * served smaller calls, and after a call that did not run to completion (a launch error).
+ * Returns 0 when no workspace is needed (then `workspace` may be NULL), or (size_t)-1 on
+ * invalid arguments.
  */
 size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_q_heads,
                                   int32_t num_seqs, int32_t max_seq_len);

@@ -159,8 +159,10 @@ def test_decode_gqa_equal_queries_give_equal_rows():
     assert np.array_equal(out[0, 0], out[0, 3])
 
 
-def test_decode_workspace_reuse():
-    # split partials live in the workspace: repeated calls on one (uninitialised) workspace agree
+def test_decode_workspace_reuse(monkeypatch):
+    # Split runs merge through per-unit counters in the workspace (its first 64 KB): one
+    # zero-filled workspace serves repeated calls, and calls of other shapes and plans, and its
+    # counters are back at zero after each call.
     rng = np.random.default_rng(27)
     lens = [3000, 2000]
     pool, table = oracle_cache(rng, lens, 2, 64)
@@ -170,9 +172,25 @@ def test_decode_workspace_reuse():
     bt = torch.from_numpy(table).cuda()
     ws = kvq.make_workspace(cache, 8, 2, 3000)
     assert ws is not None
-    outs = [kvq.decode_attn(cache, q, sl, bt, 3000, workspace=ws).cpu() for _ in range(4)]
+    counters = ws[:65536]
+    outs = []
+    for _ in range(4):
+        outs.append(kvq.decode_attn(cache, q, sl, bt, 3000, workspace=ws).cpu())
+        assert int(counters.count_nonzero()) == 0
     for o in outs[1:]:
         assert torch.equal(outs[0], o)
+    ref = oracle.decode_attention(pool, q.float().cpu().numpy(), lens, table, 64)
+    assert parity.attn_row_error(outs[0].numpy(), ref).max() <= parity.ATTN_TOL
+    # another shape and plan on the same workspace: one sequence, the balanced cut, 13 slots
+    monkeypatch.setenv("KVQ_DECODE_BALANCED", "1")
+    monkeypatch.setenv("KVQ_DECODE_SLOTS", "13")
+    small = kvq.decode_attn(cache, q[:1], sl[:1], bt[:1], 3000, workspace=ws).cpu().numpy()
+    assert int(counters.count_nonzero()) == 0
+    assert parity.attn_row_error(small, ref[:1]).max() <= parity.ATTN_TOL
+    monkeypatch.delenv("KVQ_DECODE_BALANCED")
+    monkeypatch.delenv("KVQ_DECODE_SLOTS")
+    assert torch.equal(kvq.decode_attn(cache, q, sl, bt, 3000, workspace=ws).cpu(), outs[0])
+    assert int(counters.count_nonzero()) == 0
 
 
 @pytest.mark.parametrize("hb", [64, 128])
