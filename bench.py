@@ -51,6 +51,9 @@ def decode_step_bytes(w, lens, out_bytes=2):
     return kv + q + out + bt
 
 
+TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.float8_e4m3fn}
+
+
 def append_bytes(n_tokens, hkv, in_bytes=2):
     return n_tokens * hkv * (2 * 128 * in_bytes + 2 * 68) + n_tokens * 4
 
@@ -60,8 +63,9 @@ def build_layers(w, n_layers, dev):
     lens = wl.seq_lens(w)
     table, num_pages = wl.block_table(w, lens)
     data = wl.decode_step_inputs(w)
-    k = torch.from_numpy(np.concatenate(data["prefix_k"])).to(torch.bfloat16).to(dev)
-    v = torch.from_numpy(np.concatenate(data["prefix_v"])).to(torch.bfloat16).to(dev)
+    kdt, qdt = TORCH_DT[w.kv_dtype], TORCH_DT[w.q_dtype]
+    k = torch.from_numpy(np.concatenate(data["prefix_k"])).to(kdt).to(dev)
+    v = torch.from_numpy(np.concatenate(data["prefix_v"])).to(kdt).to(dev)
     pre = lens - 1
     cu = torch.tensor(np.concatenate([[0], np.cumsum(pre)]), dtype=torch.int32, device=dev)
     start0 = torch.zeros(w.batch, dtype=torch.int32, device=dev)
@@ -74,11 +78,11 @@ def build_layers(w, n_layers, dev):
     torch.cuda.synchronize()
     del k, v
     step = {
-        "k": torch.from_numpy(data["new_k"]).to(torch.bfloat16).to(dev),
-        "v": torch.from_numpy(data["new_v"]).to(torch.bfloat16).to(dev),
+        "k": torch.from_numpy(data["new_k"]).to(kdt).to(dev),
+        "v": torch.from_numpy(data["new_v"]).to(kdt).to(dev),
         "cu": torch.arange(w.batch + 1, dtype=torch.int32, device=dev),
         "start": torch.from_numpy(pre.astype(np.int32)).to(dev),
-        "q": torch.from_numpy(wl.queries(w)).to(torch.bfloat16).to(dev),
+        "q": torch.from_numpy(wl.queries(w)).to(qdt).to(dev),
         "lens": torch.from_numpy(lens.astype(np.int32)).to(dev),
         "bt": bt,
     }
@@ -169,6 +173,54 @@ def time_graph_steps(every, single, steps, warmup):
     return wall, e0.elapsed_time(e1) * 1e3 / steps
 
 
+def settle(fn, seconds=0.3):
+    """Run fn (GPU work) repeatedly for about `seconds`, so that clocks have settled after the
+    host-side input generation that precedes each workload before anything is timed."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
+
+
+def time_tiny_step(dev, replays=400):
+    """Tiny workload: 1 sequence, 4 q / 1 kv head, fp16, Hadamard block 64; a step appends the
+    256th token and attends all 256 (kvq_decode_step), captured in a HIP graph and replayed.
+    Latency-bound: the 35 KB cache is far below any bandwidth scale."""
+    w = wl.WORKLOADS["tiny"]
+    caches, step, lens, _ = build_layers(w, 1, dev)
+    max_len = int(lens.max())
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=dev)
+    ws = kvq.make_workspace(caches[0], w.num_q_heads, w.batch, max_len, dev)
+
+    def one():
+        kvq.decode_step(caches[0], step["k"], step["v"], step["q"], step["lens"], step["bt"], max_len, out=out,
+                        out_dtype=torch.float32, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(10):
+            one()
+    settle(g.replay)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays // 10):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (replays // 10 * 10)
+    nbytes = decode_step_bytes(w, lens, out_bytes=4) + append_bytes(w.batch, w.num_kv_heads)
+    del g, caches, step
+    return {"workload": "1 sequence, context 256 (255 cached + the appended token), 4 q / 1 kv head, fp16 "
+                        "K/V/q, Hadamard block 64, fp32 out; kvq_decode_step in a HIP graph (10 per replay)",
+            "us_per_step": round(us, 3), "algorithmic_bytes": nbytes}
+
+
 def time_long_decode(dev, replays=25):
     """Long/ragged decode: 8 sequences with contexts ~ U{1024..32768}, 32 q / 8 kv heads,
     Hadamard block 64, over a permuted shared page pool; kvq_decode_attn (decode kernel plus the
@@ -194,9 +246,7 @@ def time_long_decode(dev, replays=25):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         all_layers()
-    for _ in range(max(2, replays // 5)):
-        g.replay()
-    torch.cuda.synchronize()
+    settle(g.replay)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(replays):
@@ -240,9 +290,11 @@ def time_mxfp4_decode(dev, repeats=40):
     out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
     max_len = int(lens.max())
     ws = kvq.make_workspace(caches[0], w.num_q_heads, w.batch, max_len, dev)
-    for i in range(30):
-        kvq.decode_attn(caches[i % 2], q, sl, bt, max_len, out=out, workspace=ws)
-    torch.cuda.synchronize()
+    def warm_round():
+        for i in range(8):
+            kvq.decode_attn(caches[i % 2], q, sl, bt, max_len, out=out, workspace=ws)
+
+    settle(warm_round)
     times = {False: [], True: []}
     for scaled in (False, True, False, True):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -295,7 +347,7 @@ def time_prefill_append(dev, repeats=10):
             pools = [kvq.Cache(num_pages, w.num_kv_heads, hb, device=dev) for _ in range(2)]
         for c in pools:
             kvq.append(c, k, v, cu, start, bt, int(lens.max()))
-        torch.cuda.synchronize()
+        settle(lambda: kvq.append(pools[0], k, v, cu, start, bt, int(lens.max())), 0.1)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(repeats)]
         for i in range(repeats):
@@ -420,6 +472,55 @@ def cpu_baseline(w, budget_s=12.0, n_seqs=4):
     }
 
 
+def cpu_per_workload(budget_s=2.0):
+    """The oracle, as it stands, on one sequence of each other workload (the tiny one has only
+    one): a decode step (append of the step's token + decode attention) or, for the prefill
+    workload, the append of one sequence's new tokens; each repeated for about budget_s.
+    Context for the GPU figures, not a target."""
+    import oracle
+
+    def run(fn):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        return (time.perf_counter() - t0) / reps, reps
+
+    res = {}
+    for name in ("tiny", "long", "mxfp4"):
+        w = wl.WORKLOADS[name]
+        fmt = oracle.FMT_MXFP4 if w.fmt == "mxfp4" else oracle.FMT_INT4
+        data = wl.decode_step_inputs(w, seqs=[0])
+        L = int(data["lens"][0])
+        lens = np.array([L])
+        table, num_pages = wl.block_table(wl.small_variant(w, 1, L), lens)
+        pool = np.zeros((num_pages, w.num_kv_heads, PAGE_HEAD), np.uint8)
+        oracle.append(pool, data["prefix_k"][0], data["prefix_v"][0], np.array([0, L - 1]), np.zeros(1, np.int64),
+                      table, w.had_block, fmt)
+        q = wl.queries(w)[:1]
+        nk, nv = data["new_k"][:1], data["new_v"][:1]
+
+        def step():
+            oracle.append(pool, nk, nv, np.array([0, 1]), np.array([L - 1]), table, w.had_block, fmt)
+            oracle.decode_attention(pool, q, lens, table, w.had_block, fmt)
+
+        sec, reps = run(step)
+        res[name] = {"sample": f"sequence 0 of {w.batch} (context {L}): append of its step token + decode "
+                               f"attention, {reps}x", "s_per_sequence_step": round(sec, 5),
+                     "s_per_step_all_sequences_est": round(sec * w.batch, 4) if name != "tiny" else round(sec, 5)}
+    w = wl.WORKLOADS["prefill"]
+    n = int(wl.seq_lens(w)[0])
+    k, v = wl.sequence_kv(w, 0, n)
+    table, num_pages = wl.block_table(wl.small_variant(w, 1, n), np.array([n]))
+    pool = np.zeros((num_pages, w.num_kv_heads, PAGE_HEAD), np.uint8)
+    sec, reps = run(lambda: oracle.append(pool, k, v, np.array([0, n]), np.zeros(1, np.int64), table, w.had_block))
+    res["prefill"] = {"sample": f"sequence 0 of {w.batch}: append of its {n} new tokens, {reps}x",
+                      "tokens_per_s": round(n / sec, 1)}
+    return res
+
+
 def code_sha256(paths):
     """sha256 of the code of the given source files: comment-only edits leave it unchanged."""
     lines = []
@@ -457,7 +558,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--profile-run", action="store_true",
                     help="run for rocprofv3: the fused steps as timed by default, the copy probe, "
-                         "three prefill appends; no two-launch step and no CPU leg")
+                         "three prefill appends, short long/ragged, tiny and MXFP4 legs; no "
+                         "two-launch step and no CPU leg")
     args = ap.parse_args()
     if args.profile_run:
         args.no_cpu = True
@@ -556,12 +658,16 @@ def main():
         torch.cuda.empty_cache()
     log("[bench] long/ragged decode")
     res["long_ragged_decode"] = time_long_decode(dev, replays=5 if args.profile_run else 25)
-    if not args.no_mxfp4 and not args.profile_run:
+    log("[bench] tiny decode step")
+    res["tiny_step"] = time_tiny_step(dev, replays=100 if args.profile_run else 400)
+    if not args.no_mxfp4:
         log("[bench] MXFP4 decode (f16-tile and scaled-MFMA q.K)")
-        res["mxfp4_decode"] = time_mxfp4_decode(dev)
+        res["mxfp4_decode"] = time_mxfp4_decode(dev, repeats=3 if args.profile_run else 40)
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)
+        log("[bench] CPU oracle on the other workloads")
+        res["cpu_baseline"]["per_workload"] = cpu_per_workload()
     print(json.dumps(res), flush=True)
 
 
