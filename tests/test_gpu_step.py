@@ -172,13 +172,19 @@ def test_step_repeated_calls_grow_the_cache():
         ref_pool = gpu_pool.copy()  # the next step builds on the GPU's bytes
 
 
-@pytest.mark.parametrize("fmt,rot,scaled", [("int4", "hadamard", False), ("mxfp4", "hadamard", True),
-                                            ("int4", "quat", False)])
-def test_step_graph_replays_match_eager(fmt, rot, scaled):
+@pytest.mark.parametrize("fmt,rot,scaled,plan", [("int4", "hadamard", False, "fixed"),
+                                                 ("mxfp4", "hadamard", True, "fixed"),
+                                                 ("int4", "quat", False, "fixed"),
+                                                 ("int4", "hadamard", False, "balanced")])
+def test_step_graph_replays_match_eager(fmt, rot, scaled, plan, monkeypatch):
     # the step captured in a HIP graph and replayed several times, with eager work and
-    # synchronisations in between: every replay gives the eager result bit for bit (INT4; MXFP4
-    # on the scaled-MFMA path; the quaternion rotation)
+    # synchronisations in between: every replay gives the eager result bit for bit and leaves
+    # the workspace's merge counters at zero (INT4; MXFP4 on the scaled-MFMA path; the
+    # quaternion rotation; the balanced cut)
     from bit_kv_cache_02_amd import workloads as wl
+    if plan == "balanced":
+        monkeypatch.setenv("KVQ_DECODE_BALANCED", "1")
+        monkeypatch.setenv("KVQ_DECODE_SLOTS", "37")
     rng = np.random.default_rng(8)
     hkv, group = 2, 4
     hb = 128 if rot == "hadamard" else oracle.QuatRotation(wl.unit_quaternions(9, True))
@@ -229,6 +235,7 @@ def test_step_graph_replays_match_eager(fmt, rot, scaled):
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {r} differs from the eager step"
         assert torch.equal(cache.pool, eager_pool), f"replay {r} wrote different bytes"
+        assert int(ws[:65536].count_nonzero()) == 0, f"replay {r} left merge counters set"
         del scratch
 
 
