@@ -103,10 +103,10 @@ __device__ __forceinline__ int block_scan_excl(int v, int nw, int* red, int* tot
 }
 
 // The balanced cut, computed alike by every workgroup from seq_lens: sequence b has np_b pages;
-// with T = hkv * sum(np_b) and
-// C = max(ceil(T / slots), min_piece), each of its kv heads is cut into n_b = ceil(np_b / C)
-// pieces, piece j holding pages [j np_b / n_b, (j+1) np_b / n_b).  Pieces are numbered in
-// (sequence, kv head, piece) order; sequence b's first is hkv * sum_{b' < b} n_b'.
+// with T = hkv * sum(np_b) and C = max(ceil(T / slots), min_piece), each of its kv heads is cut
+// into n_b = ceil(np_b / C) pieces, piece j holding pages [j np_b / n_b, (j+1) np_b / n_b).
+// Pieces are numbered in (sequence, kv head, piece) order; sequence b's first is
+// hkv * sum_{b' < b} n_b'.  At most slots + units pieces: rounding up adds less than one per unit.
 // cut[] receives {sequence whose pieces hold piece number `key` (or -1), its first piece, n_b,
 // np_b}.  One thread per sequence: the workgroup's nw waves cover num_seqs.
 __device__ __forceinline__ void balanced_cut(const DecodeParams& a, int key, int nw, int* red, int* cut) {
