@@ -191,16 +191,20 @@ struct PageI4 {
   float sk, zk, sv, zv;
 };
 
-__device__ __forceinline__ PageI4 unpack_i4(const PageData<0>& pg) {
+// vlimit (wave-uniform): slots of the page that exist in the sequence.  Past it the V parameters
+// are taken as 0, so whatever bytes the pool held there stay finite in the p.V terms (their p is
+// 0: an inf or NaN scale would still poison the sums).
+__device__ __forceinline__ PageI4 unpack_i4(const PageData<0>& pg, int vlimit, int n) {
   const uint32_t M4 = 0x0F0F0F0Fu, M16 = 0x000F000Fu;
   PageI4 u;
+  const uint32_t vp = n < vlimit ? pg.vp : 0u;
   u.kb0 = i32x4{(int)(pg.k[0] & M4), (int)(pg.k[1] & M4), (int)(pg.k[2] & M4), (int)(pg.k[3] & M4)};
   u.kb1 = i32x4{(int)((pg.k[0] >> 4) & M4), (int)((pg.k[1] >> 4) & M4), (int)((pg.k[2] >> 4) & M4),
                 (int)((pg.k[3] >> 4) & M4)};
   u.sk = f16_bits_to_f32(pg.kp & 0xFFFFu);
   u.zk = f16_bits_to_f32(pg.kp >> 16);
-  u.sv = f16_bits_to_f32(pg.vp & 0xFFFFu);
-  u.zv = f16_bits_to_f32(pg.vp >> 16);
+  u.sv = f16_bits_to_f32(vp & 0xFFFFu);
+  u.zv = f16_bits_to_f32(vp >> 16);
   // V codes as fp16 subnormals: word q of the lane holds row byte 4n+q of 4 tokens.  Low nibbles
   // (channel n+32q) are masked to c*2^-24, high nibbles (channel n+32q+16) are masked in place to
   // 16c*2^-24 (their accumulators carry that factor 16 until the end).  One exact packed fp16
@@ -263,13 +267,15 @@ __device__ __forceinline__ void rows_i4(const PageI4& u, int valid0, int valid1,
   const float p0 = __builtin_amdgcn_exp2f(x0 - s.m0), p1 = __builtin_amdgcn_exp2f(x1 - s.m1);
   s.l0 += p0;
   s.l1 += p1;
+  // A masked score is -inf, so its p is exactly 0, and sv, zv are finite (zeroed past the
+  // sequence's end): masked tokens add nothing below without a select.
   const float zc = fmaf(8.0f, sv, zv);  // zero point of the centred codes (exact: fp16 inputs)
-  s.pz0 = tv0 ? fmaf(p0, zc, s.pz0) : s.pz0;
-  s.pz1 = tv1 ? fmaf(p1, zc, s.pz1) : s.pz1;
+  s.pz0 = fmaf(p0, zc, s.pz0);
+  s.pz1 = fmaf(p1, zc, s.pz1);
 
   // p~ = p * sv as fp16 high + low parts, stored at A-tile rows 2g+limb in the k order of the
   // V words (tokens 0, 2, 1, 3 of each quad: bits 0 and 1 of the token swapped)
-  const float pt0 = tv0 ? p0 * sv : 0.0f, pt1 = tv1 ? p1 * sv : 0.0f;
+  const float pt0 = p0 * sv, pt1 = p1 * sv;
   const _Float16 h0 = (_Float16)pt0, h1 = (_Float16)pt1;
   const _Float16 r0 = (_Float16)(pt0 - (float)h0), r1 = (_Float16)(pt1 - (float)h1);
   const int pos = (n & ~3) | ((n & 1) << 1) | ((n >> 1) & 1);
@@ -299,7 +305,8 @@ __device__ __forceinline__ void process_page(const PageData<0>& pg, int valid0, 
                                              float alpha0, float beta0, float alpha1, float beta1,
                                              bool has0, bool has1, int n, int jg, bool a_row_used,
                                              _Float16 (*ptile)[kPage]) {
-  rows_i4(unpack_i4(pg), valid0, valid1, s, qa, alpha0, beta0, alpha1, beta1, has0, has1, n, jg, a_row_used,
+  rows_i4(unpack_i4(pg, max(valid0, valid1), n), valid0, valid1, s, qa, alpha0, beta0, alpha1, beta1, has0, has1, n,
+          jg, a_row_used,
           ptile);
 }
 
@@ -346,12 +353,15 @@ struct VTileMx {
 
 __device__ __forceinline__ VTileMx unpack_v_mx(const PageData<1>& pg, int vlimit, int jg) {
   VTileMx t;
+  uint32_t vw[4];  // the scale words of tokens 4jg .. 4jg+3, zero past the sequence's end
+#pragma unroll
+  for (int r = 0; r < 4; ++r) vw[r] = 4 * jg + r < vlimit ? pg.vp4[r] : 0u;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t Y = pg.v[q];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const f16x2 h2 = cvt_fp4(Y, 4 * jg + r < vlimit ? ue8m0_scale(pg.vp4[r], 8 * q) : 0.0f, r);
+      const f16x2 h2 = cvt_fp4(Y, ue8m0_scale(vw[r], 8 * q), r);
       t.blo[q][r] = h2[0];
       t.bhi[q][r] = h2[1];
     }
@@ -485,8 +495,9 @@ __device__ __forceinline__ void softmax_pv_mx(const VTileMx& vt, f32x4 sc, int v
   s.l0 += p0;
   s.l1 += p1;
 
-  // p as fp16 high + low parts at A-tile rows 2g+limb, natural token order
-  const float pt0 = tv0 ? p0 : 0.0f, pt1 = tv1 ? p1 : 0.0f;
+  // p as fp16 high + low parts at A-tile rows 2g+limb, natural token order (a masked score is
+  // -inf: its p is exactly 0)
+  const float pt0 = p0, pt1 = p1;
   const _Float16 h0 = (_Float16)pt0, h1 = (_Float16)pt1;
   const _Float16 r0 = (_Float16)(pt0 - (float)h0), r1 = (_Float16)(pt1 - (float)h1);
   if (has0) {

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
       st[(d + D) % NB] = load_page<FMT>(page_base(i + D), i + D < npw, koff, voff, poff, qoff);
       if (i < npw) {
         if constexpr (FMT == 0) {
-          const PageI4 u = unpack_i4(st[d]);
+          const PageI4 u = unpack_i4(st[d], L - i * kPage, n);
 #pragma unroll
           for (int k = 0; k < RS; ++k)
             rows_i4(u, lim0[k] - i * kPage, lim1[k] - i * kPage, s[k], qa[k], alpha0[k], beta0[k], alpha1[k],
