@@ -197,3 +197,27 @@ def test_append_mxfp4_exact_grid():
     _, _, flips = run_append("mxfp4-grid", x, x[::-1].copy(), [t], [0], table, 3, hkv, 1,
                              oracle.FMT_MXFP4, "bf16")
     assert flips == 0
+
+
+@pytest.mark.parametrize("fmt", [oracle.FMT_INT4, oracle.FMT_MXFP4])
+@pytest.mark.parametrize("hb", [1, 128])
+def test_append_degenerate_vectors(fmt, hb):
+    # vectors whose scale is 0 (all zero; constant, a degenerate range without rotation; a range
+    # below the smallest fp16 step), MXFP4 groups that are zero or below 2^-125, interleaved with
+    # ordinary vectors: byte parity with the oracle
+    rng = np.random.default_rng(40 + hb + fmt)
+    hkv, t = 2, 40
+    k, v = rand_kv(rng, t, hkv, "bf16")
+    k[0] = 0.0
+    v[1] = 0.0
+    k[2] = 3.25
+    v[3] = -0.5
+    k[4] = rng.uniform(0.0, 1e-7, (hkv, 128))
+    v[5] = rng.uniform(-3e-8, 3e-8, (hkv, 128))
+    k[6, :, :32] = 0.0
+    v[7, :, 32:64] = rng.uniform(-1e-39, 1e-39, (hkv, 32))
+    k = torch.from_numpy(k).bfloat16().float().numpy()
+    v = torch.from_numpy(v).bfloat16().float().numpy()
+    lens_new = [17, 23]
+    table, total = ragged_table(rng, lens_new, [0, 5])
+    run_append(f"degenerate/fmt{fmt}/b{hb}", k, v, lens_new, [0, 5], table, total, hkv, hb, fmt, "bf16")
