@@ -65,6 +65,7 @@ struct DecodeSmem {
   int red[16];
   int cut[4];
   int last;  // this workgroup finished its unit's last run: it merges the unit
+  int prog[W];  // page groups each wave has streamed (8-wave pacing)
 };
 
 // Split partials cross workgroups, possibly on other XCDs (each with its own L2), within one
@@ -439,6 +440,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)app_byte, r, vb, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b32(app_param, r, pw, 0, 0);
   }
+  if (lane == 0) sm.prog[wave] = 0;
   __syncthreads();
 
   const int ga = n >> 1;   // A-tile row 2g+limb -> head of this lane's A row
@@ -477,13 +479,22 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   for (int i0 = 0; i0 < npw; i0 += NB) {
     // The waves of a workgroup hold equal shares of the pages, but the issue arbiter favours
     // older waves, which would finish first and leave the last pages to fewer waves (fewer loads
-    // in flight).  A wave's priority falls as it progresses, so the waves that are behind get
-    // the issue slots.
-    const int progress = 4 * i0;  // compared with 3 npw, 2 npw, npw
-    if (progress < npw) __builtin_amdgcn_s_setprio(3);
-    else if (progress < 2 * npw) __builtin_amdgcn_s_setprio(2);
-    else if (progress < 3 * npw) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
+    // in flight).  8 waves: waves w and w ^ 4 share a SIMD (a workgroup's waves go to the CU's
+    // four SIMDs in turn); each publishes its progress in LDS and the one ahead of its SIMD-mate
+    // yields the issue slots, so the pair keep pace page group by page group.  Otherwise a
+    // wave's priority falls as it progresses, so the waves that are behind get the issue slots.
+    if constexpr (W == 8) {
+      if (lane == 0) *(volatile int*)&sm.prog[wave] = i0;
+      const int mate = __builtin_amdgcn_readfirstlane(*(volatile const int*)&sm.prog[wave ^ 4]);
+      if (i0 > mate) __builtin_amdgcn_s_setprio(0);
+      else __builtin_amdgcn_s_setprio(3);
+    } else {
+      const int progress = 4 * i0;  // compared with 3 npw, 2 npw, npw
+      if (progress < npw) __builtin_amdgcn_s_setprio(3);
+      else if (progress < 2 * npw) __builtin_amdgcn_s_setprio(2);
+      else if (progress < 3 * npw) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
 #pragma unroll
     for (int d = 0; d < NB; ++d) {
       const int i = i0 + d;
