@@ -16,16 +16,27 @@ __device__ __forceinline__ float inv_sqrt_block(int hb) {
   return hb == 128 ? 0.08838834764831845f : (hb == 64 ? 0.125f : 1.0f);
 }
 
+// One butterfly stage of the Walsh-Hadamard transform over lanes `lane` and `lane ^ M`.
+template <int M>
+__device__ __forceinline__ void fwht_stage(float& x0, float& x1, int lane) {
+  const float y0 = xor_lane<M>(x0, lane), y1 = xor_lane<M>(x1, lane);
+  const bool upper = (lane & M) != 0;
+  x0 = upper ? y0 - x0 : x0 + y0;
+  x1 = upper ? y1 - x1 : x1 + y1;
+}
+
 // Walsh-Hadamard transform of one 128-vector held by a wave, element `lane` in x0 and element
-// `lane + 64` in x1 (unnormalised, blocks of hb channels, natural Sylvester order).  Cross-lane
-// stages use lane shuffles, so no workgroup barrier is needed.
+// `lane + 64` in x1 (unnormalised, blocks of hb channels, natural Sylvester order; hb is 64 or
+// 128, and 1 leaves x as it is).  Cross-lane stages use lane exchanges, so no workgroup barrier
+// is needed; the stage across the two halves (hb 128) stays in registers.
 __device__ __forceinline__ void fwht_wave(float& x0, float& x1, int hb, int lane) {
-  for (int len = 1; len < hb && len < 64; len <<= 1) {
-    const float y0 = __shfl_xor(x0, len), y1 = __shfl_xor(x1, len);
-    const bool upper = (lane & len) != 0;
-    x0 = upper ? y0 - x0 : x0 + y0;
-    x1 = upper ? y1 - x1 : x1 + y1;
-  }
+  if (hb < 64) return;
+  fwht_stage<1>(x0, x1, lane);
+  fwht_stage<2>(x0, x1, lane);
+  fwht_stage<4>(x0, x1, lane);
+  fwht_stage<8>(x0, x1, lane);
+  fwht_stage<16>(x0, x1, lane);
+  fwht_stage<32>(x0, x1, lane);
   if (hb == 128) {
     const float t = x0;
     x0 = t + x1;
@@ -33,23 +44,18 @@ __device__ __forceinline__ void fwht_wave(float& x0, float& x1, int hb, int lane
   }
 }
 
-// The same transform of R vectors at once (row r in x0[r], x1[r]): each stage issues the
-// shuffles of all rows back to back, so their latencies overlap.
+// The same transform of R vectors at once (row r in x0[r], x1[r]).
 template <int R>
 __device__ __forceinline__ void fwht_rows(float (&x0)[R], float (&x1)[R], int hb, int lane) {
-  for (int len = 1; len < hb && len < 64; len <<= 1) {
-    float y0[R], y1[R];
+  if (hb < 64) return;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      y0[r] = __shfl_xor(x0[r], len);
-      y1[r] = __shfl_xor(x1[r], len);
-    }
-    const bool upper = (lane & len) != 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      x0[r] = upper ? y0[r] - x0[r] : x0[r] + y0[r];
-      x1[r] = upper ? y1[r] - x1[r] : x1[r] + y1[r];
-    }
+  for (int r = 0; r < R; ++r) {
+    fwht_stage<1>(x0[r], x1[r], lane);
+    fwht_stage<2>(x0[r], x1[r], lane);
+    fwht_stage<4>(x0[r], x1[r], lane);
+    fwht_stage<8>(x0[r], x1[r], lane);
+    fwht_stage<16>(x0[r], x1[r], lane);
+    fwht_stage<32>(x0[r], x1[r], lane);
   }
   if (hb == 128) {
 #pragma unroll

@@ -78,6 +78,32 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
+// ---- lane exchanges ----
+// x from lane (lane ^ M) of the wave, for M = 1 .. 32, without the LDS unit's permute where the
+// VALU can do it: quad permutes (1, 2), row shifts by 4 with complementary bank masks (lanes
+// with bit 2 clear read lane + 4, the others lane - 4), a row rotation by 8, a swizzle (16, LDS
+// unit but no address operand), and the gfx950 32-lane swap (32).  Every lane read lies in the
+// same 16-lane row (M <= 8), so no bound control is involved.
+template <int CTRL, int BANK>
+__device__ __forceinline__ int dpp_i(int old, int x) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, 0xF, BANK, false);
+}
+template <int M>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+  const int x = __float_as_int(v);
+  if constexpr (M == 1) return __int_as_float(dpp_i<0xB1, 0xF>(0, x));        // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return __int_as_float(dpp_i<0x4E, 0xF>(0, x));   // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) return __int_as_float(dpp_i<0x114, 0xA>(dpp_i<0x104, 0x5>(0, x), x));  // row_shl/shr:4
+  else if constexpr (M == 8) return __int_as_float(dpp_i<0x128, 0xF>(0, x));  // row_ror:8
+  else if constexpr (M == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x401F));  // xor 16 in 32
+  else {
+    static_assert(M == 32, "lane exchange distance");
+    // swap: lanes 32..63 of the first copy take lanes 0..31 of the second, and back
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return __int_as_float(lane < 32 ? (int)r[1] : (int)r[0]);
+  }
+}
+
 // ---- quaternion block rotation (IsoQuant abstract: a 4-channel block v -> qL v conj(qR)) ----
 // Rotation codes carried in the kernels' had_block argument besides the Hadamard widths.
 constexpr int kQuatBlock = 4;
