@@ -423,8 +423,8 @@ __device__ __forceinline__ void mxfp8_limbs(float v0, float v1, int g, int lane,
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
     float m0 = row_max16(fabsf(v0)), m1 = row_max16(fabsf(v1));
-    m0 = fmaxf(m0, __shfl_xor(m0, 16));
-    m1 = fmaxf(m1, __shfl_xor(m1, 16));
+    m0 = fmaxf(m0, xor_lane<16>(m0, lane_id()));
+    m1 = fmaxf(m1, xor_lane<16>(m1, lane_id()));
     const int e0 = min(max((int)((__float_as_uint(m0) >> 23) & 255u) - 8, 0), 254);
     const int e1 = min(max((int)((__float_as_uint(m1) >> 23) & 255u) - 8, 0), 254);
     const float y0 = fminf(fmaxf(ldexpf(v0, 127 - e0), -448.0f), 448.0f);

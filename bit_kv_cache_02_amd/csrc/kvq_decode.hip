@@ -403,8 +403,8 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
     } else {
       // UE8M0 exponent per 32 channels: lanes 0-31 / 32-63 hold groups 0 / 1 (x0) and 2 / 3 (x1)
       float m0 = row_max16(fabsf(x0)), m1 = row_max16(fabsf(x1));
-      m0 = fmaxf(m0, __shfl_xor(m0, 16));
-      m1 = fmaxf(m1, __shfl_xor(m1, 16));
+      m0 = fmaxf(m0, xor_lane<16>(m0, lane_id()));
+      m1 = fmaxf(m1, xor_lane<16>(m1, lane_id()));
       const int e0 = min(max((int)((__float_as_uint(m0) >> 23) & 255u) - 2, 0), 254);
       const int e1 = min(max((int)((__float_as_uint(m1) >> 23) & 255u) - 2, 0), 254);
       c0 = e2m1_code(ldexpf(x0, 127 - e0));

@@ -60,24 +60,6 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// Full-wave reductions (prologue/epilogue only).
-__device__ __forceinline__ float wave_max(float x) {
-  x = row_max16(x);
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-__device__ __forceinline__ float wave_sum_f(float x) {
-  x = row_sum16(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-__device__ __forceinline__ int wave_sum_i(int x) {
-  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
 // ---- lane exchanges ----
 // x from lane (lane ^ M) of the wave, for M = 1 .. 32, without the LDS unit's permute where the
 // VALU can do it: quad permutes (1, 2), row shifts by 4 with complementary bank masks (lanes
@@ -102,6 +84,29 @@ __device__ __forceinline__ float xor_lane(float v, int lane) {
     const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
     return __int_as_float(lane < 32 ? (int)r[1] : (int)r[0]);
   }
+}
+
+// Full-wave reductions (prologue/epilogue only): the row reduction, then rows 16 and 32 apart.
+__device__ __forceinline__ float wave_max(float x) {
+  x = row_max16(x);
+  x = fmaxf(x, xor_lane<16>(x, lane_id()));
+  x = fmaxf(x, xor_lane<32>(x, lane_id()));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+  x = row_sum16(x);
+  x += xor_lane<16>(x, lane_id());
+  x += xor_lane<32>(x, lane_id());
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x += dpp_i<kQuadSwap1, 0xF>(0, x);
+  x += dpp_i<kQuadSwap2, 0xF>(0, x);
+  x += dpp_i<kRowHalfMirror, 0xF>(0, x);
+  x += dpp_i<kRowMirror, 0xF>(0, x);
+  x += __float_as_int(xor_lane<16>(__int_as_float(x), lane_id()));
+  x += __float_as_int(xor_lane<32>(__int_as_float(x), lane_id()));
+  return x;
 }
 
 // ---- quaternion block rotation (IsoQuant abstract: a 4-channel block v -> qL v conj(qR)) ----
