@@ -108,9 +108,40 @@ __device__ __forceinline__ int block_scan_excl(int v, int nw, int* red, int* tot
 // into n_b = ceil(np_b / C) pieces, piece j holding pages [j np_b / n_b, (j+1) np_b / n_b).
 // Pieces are numbered in (sequence, kv head, piece) order; sequence b's first is
 // hkv * sum_{b' < b} n_b'.  At most slots + units pieces: rounding up adds less than one per unit.
-// cut[] receives {sequence whose pieces hold piece number `key` (or -1), its first piece, n_b,
-// np_b}.  One thread per sequence: the workgroup's nw waves cover num_seqs.
-__device__ __forceinline__ void balanced_cut(const DecodeParams& a, int key, int nw, int* red, int* cut) {
+struct Cut {
+  int b;      // the sequence whose pieces hold piece number `key`, or -1
+  int first;  // its first piece
+  int n;      // its pieces per kv head
+  int np;     // its pages
+};
+
+// Up to 64 sequences every wave computes the cut alone (lane = sequence; DPP scans, no LDS, no
+// barrier); more (at most the workgroup's threads) take one thread per sequence, block scans
+// through red and the answer broadcast through cut (4 ints).  The planner keeps sum(np_b) below
+// 2^30.
+__device__ __forceinline__ Cut balanced_cut(const DecodeParams& a, int key, int nw, int* red, int* cut) {
+  Cut c;
+  if (a.num_seqs <= 64) {
+    const int lane = lane_id();
+    const int L = lane < a.num_seqs ? a.seq_lens[lane] : 0;
+    const int np = (max(L, 0) + kPage - 1) / kPage;
+    const int total = __builtin_amdgcn_readlane(wave_scan_incl(np), 63);
+    const int64_t T = (int64_t)total * a.hkv;
+    const int C = max((int)((T + a.plan.slots - 1) / a.plan.slots), a.plan.min_piece);
+    const int n = (np + C - 1) / C;
+    const int first = (wave_scan_incl(n) - n) * a.hkv;
+    const uint64_t m = __ballot(lane < a.num_seqs && n > 0 && key >= first && key < first + a.hkv * n);
+    if (m == 0) {
+      c.b = -1;
+      return c;
+    }
+    const int src = __builtin_ctzll(m);
+    c.b = src;
+    c.first = __builtin_amdgcn_readlane(first, src);
+    c.n = __builtin_amdgcn_readlane(n, src);
+    c.np = __builtin_amdgcn_readlane(np, src);
+    return c;
+  }
   const int t = thread_id();
   const int L = t < a.num_seqs ? a.seq_lens[t] : 0;
   const int np = (max(L, 0) + kPage - 1) / kPage;
@@ -129,6 +160,11 @@ __device__ __forceinline__ void balanced_cut(const DecodeParams& a, int key, int
     cut[3] = np;
   }
   __syncthreads();
+  c.b = __builtin_amdgcn_readfirstlane(cut[0]);
+  c.first = __builtin_amdgcn_readfirstlane(cut[1]);
+  c.n = __builtin_amdgcn_readfirstlane(cut[2]);
+  c.np = __builtin_amdgcn_readfirstlane(cut[3]);
+  return c;
 }
 
 // Fused step: put the appended token's bytes (staged in LDS) into the registers of the page that
@@ -222,11 +258,11 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   int b, kvh, p_begin, span, pieces_cut = 0;
   int64_t slot, unit_s0;  // this run's slot and the unit's first
   if (a.plan.balanced) {
-    balanced_cut(a, block_id_x(), W, sm.red, sm.cut);
-    if (sm.cut[0] < 0) return;  // past the last piece (uniform: read from LDS after a barrier)
-    b = __builtin_amdgcn_readfirstlane(sm.cut[0]);
-    const int r = block_id_x() - __builtin_amdgcn_readfirstlane(sm.cut[1]);
-    const int nb = __builtin_amdgcn_readfirstlane(sm.cut[2]), np = __builtin_amdgcn_readfirstlane(sm.cut[3]);
+    const Cut c = balanced_cut(a, block_id_x(), W, sm.red, sm.cut);
+    if (c.b < 0) return;  // past the last piece (uniform)
+    b = c.b;
+    const int r = block_id_x() - c.first;
+    const int nb = c.n, np = c.np;
     kvh = r / nb;
     const int j = r - kvh * nb;
     p_begin = (int)((int64_t)j * np / nb);
@@ -617,8 +653,9 @@ DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len) {
   if (env_p) P = env_p;
   if (eb) balanced = atoi(eb) != 0;
   if (W != 4 && W != 8 && W != 16) W = 8;
-  // the cut runs one thread per sequence
-  if (balanced && (max_pg <= 0 || num_seqs > 64 * W || num_seqs > 256)) balanced = false;
+  // the cut runs one thread per sequence and counts pages in 32 bits
+  if (balanced && (max_pg <= 0 || num_seqs > 64 * W || num_seqs > 256 || (int64_t)num_seqs * max_pg >= (1 << 30)))
+    balanced = false;
   int D = env_d ? env_d : (balanced ? 2 : 3);
   if (D != 2 && D != 3 && D != 4) D = 3;
   if (W == 16) D = 2;  // register budget of 1024-thread workgroups

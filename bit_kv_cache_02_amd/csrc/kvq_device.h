@@ -86,6 +86,23 @@ __device__ __forceinline__ float xor_lane(float v, int lane) {
   }
 }
 
+// Inclusive prefix sum over the wave's 64 lanes: shifts by 1, 2, 4, 8 inside each 16-lane row
+// (lanes whose source lies before the row add 0), then the last lane of row 0 / rows 0-1 is
+// broadcast into rows 1, 3 / rows 2, 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_rows(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += dpp_rows<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_rows<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_rows<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_rows<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_rows<0x142, 0xA>(x);  // row_bcast:15
+  x += dpp_rows<0x143, 0xC>(x);  // row_bcast:31
+  return x;
+}
+
 // Full-wave reductions (prologue/epilogue only): the row reduction, then rows 16 and 32 apart.
 __device__ __forceinline__ float wave_max(float x) {
   x = row_max16(x);
