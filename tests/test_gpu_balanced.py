@@ -6,7 +6,8 @@ workgroup, and merge the runs' partial softmax states afterwards.  The planner p
 large work only; these tests force it on small cases through the tuning variables (read on
 every call): slot counts from 1 to more than the pages (runs of one page, units of more than 16
 runs, so the merge takes several passes), 4- and 8-wave workgroups, every prefetch depth, both
-cache formats and both MXFP4 q.K paths, and the fused append."""
+cache formats and both MXFP4 q.K paths, the fused append, and batches of more than 64
+sequences (where the cut takes one thread per sequence and block scans instead of one wave)."""
 import numpy as np
 import pytest
 
@@ -76,3 +77,15 @@ def test_balanced_is_the_default_for_large_narrow_batches(monkeypatch):
     lens = [12000, 1100, 7000, 3]
     pool, table = oracle_cache(rng, lens, 8, 64)
     run_decode("balanced/default", pool, table, lens, 32, 64, seed=440)
+
+
+@pytest.mark.parametrize("nseq,slots", [(80, 100), (200, 57)])
+def test_balanced_many_sequences(balanced, nseq, slots):
+    # more than 64 sequences: the cut runs one thread per sequence with block scans (up to 64,
+    # every wave computes it alone); short ragged sequences, some split into several runs
+    balanced(slots=slots, min_piece=2)
+    rng = np.random.default_rng(450 + nseq)
+    lens = [int(x) for x in rng.integers(1, 400, size=nseq)]
+    lens[3] = 1500
+    pool, table = oracle_cache(rng, lens, 1, 64)
+    run_decode(f"balanced/{nseq}-seqs/slots={slots}", pool, table, lens, 4, 64, seed=nseq)
