@@ -512,6 +512,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) s.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int valid0 = L - pw0 * kPage;
+  const int late_bias = (a.plan.balanced && 2 * block_id_x() >= a.num_seqs * a.hkv * a.plan.nsplit) ? 1 : 0;
   for (int i0 = 0; i0 < npw; i0 += NB) {
     // The waves of a workgroup hold equal shares of the pages, but the issue arbiter favours
     // older waves, which would finish first and leave the last pages to fewer waves (fewer loads
@@ -525,7 +526,10 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       if (i0 > mate) __builtin_amdgcn_s_setprio(0);
       else __builtin_amdgcn_s_setprio(3);
     } else {
-      const int progress = 4 * i0;  // compared with 3 npw, 2 npw, npw
+      // Balanced plan (two workgroups per CU): the second half of the grid shares the CUs' SIMDs
+      // with the first half, whose older waves win the ties; it takes one level more at equal
+      // progress.
+      const int progress = 4 * i0 - late_bias * npw;  // compared with 3 npw, 2 npw, npw
       if (progress < npw) __builtin_amdgcn_s_setprio(3);
       else if (progress < 2 * npw) __builtin_amdgcn_s_setprio(2);
       else if (progress < 3 * npw) __builtin_amdgcn_s_setprio(1);
