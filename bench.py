@@ -11,7 +11,7 @@ kvq_decode_step, replayed from a HIP graph; steps cycle over 8 independent layer
 Printed: one JSON line with the whole-step algorithmic throughput (GB/s), the step
 kernel's average launch duration from HIP events on its stream and its roofline
 fraction against 8 TB/s, the same step as two launches (kvq_append + kvq_decode_attn),
-the measured copy bandwidth, the prefill-append throughput (64 x 2048 tokens, with and
+the measured copy and read-only bandwidths, the prefill-append throughput (64 x 2048 tokens, with and
 without rotation) and the CPU oracle's rate on a bounded sample.
 """
 import argparse
@@ -417,8 +417,7 @@ def time_prefill_attention(w, caches, lens, dev, chunk=512, repeats=20):
 def hbm_copy_probe(dev, nbytes=1 << 30, repeats=10):
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
-    kvq.hbm_copy(src, dst)
-    torch.cuda.synchronize()
+    settle(lambda: kvq.hbm_copy(src, dst))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(repeats):
@@ -427,6 +426,34 @@ def hbm_copy_probe(dev, nbytes=1 << 30, repeats=10):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / repeats
     return 2 * nbytes / us / 1e3
+
+
+def hbm_read_probe(dev, window=1 << 30, buf_bytes=1 << 30, repeats=20):
+    """Read-only probe: GB/s of one launch over `window` bytes; launches cycle over the
+    windows of a 1 GiB buffer, so that windows smaller than the 256 MB MALL are not re-read
+    from it."""
+    window -= window % 16
+    src = torch.empty(buf_bytes, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.zeros(kvq.HBM_READ_SINK_WORDS, dtype=torch.int32, device=dev)
+    views = [src[k * window:(k + 1) * window] for k in range(buf_bytes // window)]
+    for v in views:
+        kvq.hbm_read(v, sink)
+    torch.cuda.synchronize()
+    # one HIP graph holds a launch per window (as the decode step is timed: graph replays)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for v in views:
+            kvq.hbm_read(v, sink)
+    replays = max(1, -(-repeats // len(views)))
+    settle(g.replay)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (replays * len(views))
+    return window / us / 1e3
 
 
 def cpu_baseline(w, budget_s=12.0, n_seqs=4):
@@ -648,6 +675,12 @@ def main():
     log("[bench] HBM copy probe")
     res["hbm_copy_GBps"] = round(hbm_copy_probe(dev), 1)
     res["step_frac_of_copy_bw"] = round(achieved / res["hbm_copy_GBps"], 4)
+    log("[bench] HBM read probe")
+    res["hbm_read_GBps"] = round(hbm_read_probe(dev), 1)
+    res["step_frac_of_read_bw"] = round(achieved / res["hbm_read_GBps"], 4)
+    # the same probe at one step's byte count per launch (its launch and drain included)
+    res["hbm_read_GBps_at_step_bytes"] = round(hbm_read_probe(dev, window=step_bytes, repeats=56), 1)
+    res["step_frac_of_read_bw_at_step_bytes"] = round(achieved / res["hbm_read_GBps_at_step_bytes"], 4)
     del caches
     torch.cuda.empty_cache()
     if not args.no_prefill:

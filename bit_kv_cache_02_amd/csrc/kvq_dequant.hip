@@ -100,19 +100,48 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   }
 }
 
+// Bandwidth probes.  Each workgroup streams one contiguous chunk of the buffer, 4 KiB per
+// wave-group step (256 lanes x 16 B), several steps' loads in flight before they are used:
+// whole DRAM rows are read while open, which a grid-stride walk (neighbouring kilobytes from
+// different workgroups at different times) does not get.
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                  int64_t n16, int64_t nthreads) {
-  // each thread moves 4 x 16 bytes per step, all four loads issued before the stores
-  const int64_t t = (int64_t)block_id_x() * 256 + thread_id();
-  int64_t i = t;
-  for (; i + 3 * nthreads < n16; i += 4 * nthreads) {
-    const u32x4 a0 = src[i], a1 = src[i + nthreads], a2 = src[i + 2 * nthreads], a3 = src[i + 3 * nthreads];
-    dst[i] = a0;
-    dst[i + nthreads] = a1;
-    dst[i + 2 * nthreads] = a2;
-    dst[i + 3 * nthreads] = a3;
+                                                  int64_t n16, int64_t per_block) {
+  const int64_t b0 = (int64_t)block_id_x() * per_block;
+  const int64_t b1 = b0 + per_block < n16 ? b0 + per_block : n16;
+  int64_t i = b0 + thread_id();
+  for (; i + 3 * 256 < b1; i += 4 * 256) {
+    u32x4 a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = src[i + j * 256];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(a[j], &dst[i + j * 256]);
   }
-  for (; i < n16; i += nthreads) dst[i] = src[i];
+  for (; i < b1; i += 256) __builtin_nontemporal_store(src[i], &dst[i]);
+}
+
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n16, int64_t per_block,
+                                                  uint32_t* __restrict__ sink) {
+  // non-temporal loads (streamed once); the workgroup's XOR of everything it read goes to
+  // sink[workgroup], so every load feeds a stored result
+  __shared__ uint32_t red[4];
+  const int64_t b0 = (int64_t)block_id_x() * per_block;
+  const int64_t b1 = b0 + per_block < n16 ? b0 + per_block : n16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  int64_t i = b0 + thread_id();
+  for (; i + 7 * 256 < b1; i += 8 * 256) {
+    u32x4 a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = __builtin_nontemporal_load(&src[i + j * 256]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= a[j];
+  }
+  for (; i < b1; i += 256) acc ^= __builtin_nontemporal_load(&src[i]);
+  uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x ^= (uint32_t)__shfl_xor((int)x, m, 64);
+  if ((thread_id() & 63) == 0) red[thread_id() >> 6] = x;
+  __syncthreads();
+  if (thread_id() == 0) sink[block_id_x()] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
@@ -121,12 +150,26 @@ hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  // 4096 workgroups (16 per CU) of 4 x 4 KiB steps, fewer for small copies
   const int64_t n16 = (int64_t)(bytes / 16);
-  int64_t blocks = (n16 + 255) / 256;
-  if (blocks > 256 * 16) blocks = 256 * 16;
+  int64_t blocks = (n16 + 256 * 4 - 1) / (256 * 4);
+  if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
+  const int64_t per_block = (n16 + blocks - 1) / blocks;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)src, (u32x4*)dst, n16,
-                     blocks * 256);
+                     per_block);
+  return hipGetLastError();
+}
+
+hipError_t launch_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  // 2048 workgroups (8 per CU) of 8 x 4 KiB steps, fewer for small reads
+  const int64_t n16 = (int64_t)(bytes / 16);
+  int64_t blocks = (n16 + 256 * 8 - 1) / (256 * 8);
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  const int64_t per_block = (n16 + blocks - 1) / blocks;
+  hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)src, n16, per_block,
+                     sink);
   return hipGetLastError();
 }
 

@@ -392,4 +392,13 @@ int kvq_hbm_copy(const void* src, void* dst, size_t bytes, void* stream) {
   return hip_status(kvq::launch_copy(src, dst, bytes, (hipStream_t)stream), "kvq_hbm_copy launch");
 }
 
+int kvq_hbm_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  g_last_error[0] = 0;
+  if (!src || !sink) return fail(KVQ_ERR_INVALID_ARG, "src and sink must not be NULL");
+  if (bytes % 16) return fail(KVQ_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  if (((uintptr_t)src & 15) || ((uintptr_t)sink & 3)) return fail(KVQ_ERR_INVALID_ARG, "src must be 16-byte and sink 4-byte aligned");
+  if (bytes == 0) return KVQ_OK;
+  return hip_status(kvq::launch_read(src, bytes, sink, (hipStream_t)stream), "kvq_hbm_read launch");
+}
+
 }  // extern "C"

@@ -139,5 +139,6 @@ hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
 int prefill_tokens_per_tile(int group);
 hipError_t launch_prefill(const PrefillParams& p, int fmt, hipStream_t stream);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace kvq

@@ -68,6 +68,7 @@ SIGNATURES = [
     ("kvq_strerror", ctypes.c_char_p, [ctypes.c_int]),
     ("kvq_last_error", ctypes.c_char_p, []),
     ("kvq_hbm_copy", ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+    ("kvq_hbm_read", ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
 ]
 
 
@@ -296,3 +297,15 @@ def hbm_copy(src: torch.Tensor, dst: torch.Tensor):
     """Plain copy kernel (bandwidth probe)."""
     st = lib().kvq_hbm_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(), _stream())
     _check(st, "kvq_hbm_copy")
+
+
+HBM_READ_SINK_WORDS = 4096
+
+
+def hbm_read(src: torch.Tensor, sink: torch.Tensor):
+    """Read-only streaming kernel (bandwidth probe).  sink: int32/uint32 [4096] on the device;
+    after a call on a zeroed sink, the XOR of its words is the XOR of src's 32-bit words."""
+    if sink.numel() * sink.element_size() < 4 * HBM_READ_SINK_WORDS or not sink.is_contiguous():
+        raise ValueError("hbm_read: sink must be a contiguous buffer of 4096 32-bit words")
+    st = lib().kvq_hbm_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream())
+    _check(st, "kvq_hbm_read")

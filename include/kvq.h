@@ -263,6 +263,17 @@ const char* kvq_last_error(void);
  */
 int kvq_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
 
+/*
+ * kvq_hbm_read -- read-only streaming kernel: every 16-byte vector of src is loaded once and
+ * XORed into its workgroup's 32-bit word.  Not part of the method: it measures the achievable
+ * HBM read bandwidth, the ceiling of decode attention (which only reads the cache).
+ * src: device, 16-byte aligned, bytes a multiple of 16.  sink: device uint32[4096], 4-byte
+ * aligned; the call writes words [0, w) with w <= 2048 and leaves the rest as they are, so that
+ * after a call on a zeroed sink the XOR of all 4096 words equals the XOR of all 32-bit words of
+ * src.  bytes == 0 writes nothing and returns KVQ_OK.
+ */
+int kvq_hbm_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -236,6 +236,11 @@ def test_dequant_and_copy_reject_bad_args():
     assert lib.kvq_hbm_copy(FAKE, FAKE, 17, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_hbm_copy(None, FAKE, 16, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_hbm_copy(FAKE, FAKE, 0, None) == kvq.KVQ_OK
+    assert lib.kvq_hbm_read(FAKE, 17, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_hbm_read(None, 16, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_hbm_read(FAKE, 16, None, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_hbm_read(ctypes.c_void_p(4096 + 8), 16, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_hbm_read(FAKE, 0, FAKE, None) == kvq.KVQ_OK
 
 
 def test_python_layer_raises_typed_errors():
