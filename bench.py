@@ -495,7 +495,8 @@ def cpu_baseline(w, budget_s=12.0, n_seqs=4):
         "kind": "oracle",
         "sample": f"{n_seqs} of {w.batch} sequences (all 32 q / 8 kv heads, context 4096), "
                   f"append of the step token + decode attention, repeated {reps}x in {el:.1f} s; "
-                  f"host os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}",
+                  f"host os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}, "
+                  f"BLAS threads={blas_threads}",
     }
 
 
