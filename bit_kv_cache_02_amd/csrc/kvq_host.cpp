@@ -287,7 +287,6 @@ int kvq_prefill_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, flo
   int st = decode_geometry(cache, num_q_heads, num_seqs, max_seq_len);
   if (st != KVQ_OK) return st;
   const int group = num_q_heads / cache->num_kv_heads;
-  if (8 % group) return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d unsupported by prefill (1, 2, 4 or 8)", group);
   if (!q || !cu_q || !seq_lens || !block_table || !out)
     return fail(KVQ_ERR_INVALID_ARG, "q, cu_q, seq_lens, block_table and out must not be NULL");
   if (q_dtype < KVQ_F16 || q_dtype > KVQ_FP8_E4M3) return fail(KVQ_ERR_UNSUPPORTED, "q_dtype %d unknown", q_dtype);

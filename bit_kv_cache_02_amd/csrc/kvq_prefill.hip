@@ -6,8 +6,9 @@
 // The chunk of sequence b is its last n_b positions, already appended (kvq_append); chunk token
 // j sits at position p_j = seq_lens[b] - n_b + j and attends positions 0 .. p_j.
 //
-// A workgroup (W waves) owns (sequence, kv head, tile of W * 8 RS/G chunk tokens).  Wave w takes
-// RS sets of 8 rows: its 8 RS/G chunk tokens times the G query heads of the kv head.  Each wave
+// A workgroup (W waves) owns (sequence, kv head, tile of W * floor(8 RS/G) chunk tokens).  Wave w
+// takes RS sets of 8 rows: its floor(8 RS/G) chunk tokens times the G query heads of the kv head
+// (where G does not divide 8 RS, the last rows of the sets belong to no token and stay idle).  Each wave
 // streams every page its rows attend; per page it unpacks the K and V codes once (the
 // row-independent half of the per-page step that decode uses, kvq_attn.h) and runs the scores,
 // online softmax and p.V of each row set against them: a set's 8 rows fill the 8 row pairs of the
@@ -65,6 +66,7 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
   const int n = lane & 15, jg = lane >> 4;
   const int G = a.group;
   const int tpw = kRows / G;  // chunk tokens per wave
+  const int rows_used = tpw * G;  // rows past it (G = 3, 5, 6, 7) belong to no token of this wave
   const int units = a.num_seqs * a.hkv;
   const int tile = block_id_x() / units, unit = block_id_x() % units;  // tile-major order
   const int kvh = unit % a.hkv, b = unit / a.hkv;
@@ -163,10 +165,10 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
 #pragma unroll
   for (int k = 0; k < RS; ++k) {
     const int rbase = kSetRows * k;
-    a_row_used[k] = tw0 + (rbase + ga) / G < nq;
+    a_row_used[k] = rbase + ga < rows_used && tw0 + (rbase + ga) / G < nq;
     const int t_row0 = tw0 + (rbase + 2 * jg) / G, t_row1 = tw0 + (rbase + 2 * jg + 1) / G;
-    has0[k] = t_row0 < nq;
-    has1[k] = t_row1 < nq;
+    has0[k] = rbase + 2 * jg < rows_used && t_row0 < nq;
+    has1[k] = rbase + 2 * jg + 1 < rows_used && t_row1 < nq;
     lim0[k] = pos0 + t_row0 + 1;
     lim1[k] = pos0 + t_row1 + 1;
     alpha0[k] = beta0[k] = alpha1[k] = beta1[k] = 0.0f;
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
     const int t = tw0 + r / G;
-    if (t < nq) {
+    if (r < rows_used && t < nq) {
       const int64_t base = ((int64_t)(qbeg + t) * a.hq + kvh * G + r % G) * kHeadDim;
       store_elem(a.out, base + lane, a.out_dtype, o0[r]);
       store_elem(a.out, base + lane + 64, a.out_dtype, o1[r]);

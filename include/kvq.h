@@ -219,7 +219,7 @@ int kvq_decode_step(const kvq_cache* cache, const void* k, const void* v, int32_
  *
  *   q            device [num_tokens][num_q_heads][128], dtype q_dtype (F16, BF16, F32,
  *                FP8_E4M3); the kernel uses q_scale * q.
- *   num_q_heads  as for kvq_decode_attn, with G = num_q_heads/num_kv_heads in {1, 2, 4, 8}.
+ *   num_q_heads  as for kvq_decode_attn (G = num_q_heads/num_kv_heads <= 8).
  *   cu_q         device int32[num_seqs+1], non-decreasing, cu_q[0] = 0, cu_q[num_seqs] <=
  *                num_tokens: tokens cu_q[b] .. cu_q[b+1]-1 are the chunk of sequence b.
  *   seq_lens     device int32[num_seqs]: positions in the cache, the chunk included (the

@@ -189,7 +189,7 @@ def _prefill(desc, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(hq=6), kvq.KVQ_ERR_UNSUPPORTED),          # group 3: rows per wave not a multiple
+    (dict(hq=18), kvq.KVQ_ERR_UNSUPPORTED),         # group 9: above 8
     (dict(hq=3), kvq.KVQ_ERR_INVALID_ARG),
     (dict(cu=None), kvq.KVQ_ERR_INVALID_ARG),
     (dict(q=None), kvq.KVQ_ERR_INVALID_ARG),

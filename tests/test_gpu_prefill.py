@@ -50,7 +50,8 @@ def test_prefill_int4_ragged(hb):
     run_prefill(f"int4/b{hb}", [40, 17, 300, 1, 33], [9, 17, 40, 1, 16], hkv=2, group=4, hb=hb, seed=hb)
 
 
-@pytest.mark.parametrize("group,q_dtype", [(8, "f16"), (2, "bf16"), (1, "e4m3")])
+@pytest.mark.parametrize("group,q_dtype", [(8, "f16"), (2, "bf16"), (1, "e4m3"), (3, "bf16"), (5, "f16"),
+                                           (6, "bf16"), (7, "bf16")])
 def test_prefill_groups_and_dtypes(group, q_dtype):
     run_prefill(f"int4/G{group}/{q_dtype}", [70, 129, 5], [33, 129, 5], hkv=2, group=group, hb=64,
                 q_dtype=q_dtype, q_scale=0.8, sm_scale=0.07, seed=10 + group)
@@ -60,7 +61,7 @@ def test_prefill_long_prefix_many_tiles():
     run_prefill("int4/long", [3100, 700], [100, 64], hkv=2, group=4, hb=128, seed=20)
 
 
-@pytest.mark.parametrize("group,q_dtype", [(8, "e4m3"), (1, "bf16")])
+@pytest.mark.parametrize("group,q_dtype", [(8, "e4m3"), (1, "bf16"), (3, "e4m3"), (6, "bf16")])
 def test_prefill_mxfp4(group, q_dtype):
     run_prefill(f"mxfp4/G{group}", [300, 17, 1000], [30, 17, 7], hkv=2, group=group, hb=128,
                 fmt=oracle.FMT_MXFP4, q_dtype=q_dtype, seed=30 + group)

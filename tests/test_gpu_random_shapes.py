@@ -53,7 +53,6 @@ def test_random_step(seed):
 def test_random_prefill(seed):
     rng, fmt, rot, hb, b, hkv, group, lens, q_dtype = draw(seed)
     lens = [min(x, 1500) for x in lens]
-    group = 1 << (group.bit_length() - 1)  # the prefill kernel takes groups 1, 2, 4 and 8
     chunks = [int(rng.integers(1, min(x, 80) + 1)) for x in lens]
     run_prefill(f"random/{seed}: fmt{fmt} rot {rot} B{b} Hkv{hkv} G{group} lens {lens} chunks {chunks}", lens,
                 chunks, hkv=hkv, group=group, hb=hb, fmt=fmt, q_dtype="bf16" if q_dtype == "e4m3" else q_dtype,
