@@ -428,6 +428,29 @@ def hbm_copy_probe(dev, nbytes=1 << 30, repeats=10):
     return 2 * nbytes / us / 1e3
 
 
+def time_dequant(cache, dev, n_pages=1024, repeats=20):
+    """kvq_dequant_page over n_pages seeded pages of a llama layer cache (all 8 kv heads), plain
+    and rotated back: each page-head reads its 2176-byte block and writes K and V as fp32 16 x 128
+    (2 x 8 KiB), so the call is bound by its writes."""
+    ids = torch.from_numpy(np.random.default_rng(11).permutation(cache.num_pages)[:n_pages].astype(np.int32)).to(dev)
+    nbytes = n_pages * cache.num_kv_heads * (PAGE_HEAD + 2 * 16 * 128 * 4) + n_pages * 4
+    res = {"workload": f"{n_pages} pages x {cache.num_kv_heads} kv heads of a llama layer cache (INT4, Hadamard "
+                       f"{cache.had_block}) to fp32 K and V", "algorithmic_bytes": nbytes}
+    for name, unrot in (("plain", False), ("unrotated", True)):
+        settle(lambda: kvq.dequant_pages(cache, ids, unrotate=unrot))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(repeats):
+            kvq.dequant_pages(cache, ids, unrotate=unrot)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / repeats
+        res[f"us_{name}"] = round(us, 2)
+        res[f"GBps_{name}"] = round(nbytes / us / 1e3, 1)
+        res[f"frac_of_hbm_peak_{name}"] = round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)
+    return res
+
+
 def hbm_read_probe(dev, window=1 << 30, buf_bytes=1 << 30, repeats=20):
     """Read-only probe: GB/s of one launch over `window` bytes; launches cycle over the
     windows of a 1 GiB buffer, so that windows smaller than the 256 MB MALL are not re-read
@@ -682,6 +705,8 @@ def main():
     # the same probe at one step's byte count per launch (its launch and drain included)
     res["hbm_read_GBps_at_step_bytes"] = round(hbm_read_probe(dev, window=step_bytes, repeats=56), 1)
     res["step_frac_of_read_bw_at_step_bytes"] = round(achieved / res["hbm_read_GBps_at_step_bytes"], 4)
+    log("[bench] page dequantization")
+    res["dequant_pages"] = time_dequant(caches[0], dev, repeats=5 if args.profile_run else 20)
     del caches
     torch.cuda.empty_cache()
     if not args.no_prefill:

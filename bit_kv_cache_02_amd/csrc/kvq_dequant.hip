@@ -3,9 +3,10 @@
 //   INT4   y^ = fma(scale, code, zero): a single rounding of the exact value (token-wise INT4 with an
 //          fp16 scale and zero, SAW-INT4 summary, "Summary"/"Method").
 //   MXFP4  y^ = e2m1(code) * 2^(E-127), exact (FP4 with UE8M0 group scales, UltraQuant article).
-// With KVQ_UNROTATE the rotation is undone, x^ = R^T y^: for R_b (symmetric) by an fp32
-// Walsh-Hadamard butterfly in LDS, for the quaternion block rotation by the transposed 4 x 4
-// block matrices (IsoQuant abstract), staged in LDS.
+// With KVQ_UNROTATE the rotation is undone, x^ = R^T y^: for R_b (symmetric) by the fp32
+// Walsh-Hadamard butterfly of the attention kernels, for the quaternion block rotation by the
+// transposed 4 x 4 block matrices (IsoQuant abstract), both in registers (dequant_unrotate_kernel).
+#include "kvq_attn.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -22,11 +23,12 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
 
 }  // namespace
 
-// One workgroup per (page, kv head): 256 threads, thread = (slot s = tid/16, column a = tid%16);
-// each thread owns channels a + 32q + 16e (q = 0..3, e = 0..1) of slot s, i.e. row bytes 4a..4a+3.
+// Without KVQ_UNROTATE: one workgroup per (page, kv head): 256 threads, thread = (slot s = tid/16,
+// column a = tid%16); each thread owns channels a + 32q + 16e (q = 0..3, e = 0..1) of slot s, i.e.
+// row bytes 4a..4a+3; the values go through LDS so that the workgroup stores each of K and V as
+// 1 KiB runs.
 __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   __shared__ float buf[2][kPage][kHeadDim];
-  __shared__ float qm[kHeadDim / 4][4][4];  // quaternion block matrices
   const int tid = thread_id();
   const int s = tid >> 4, col = tid & 15;
   const int i = block_id_x() / p.hkv, h = block_id_x() % p.hkv;
@@ -55,48 +57,56 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
       }
     }
   }
-  if (p.unrotate && p.had_block == kQuatBlock && tid < kHeadDim / 4) {
-    float c[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      quat_coeffs(p.quat, p.quat_full, tid, r, false, c);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) qm[tid][r][j] = c[j];
-    }
-  }
   __syncthreads();
-  float scale = 1.0f;
-  if (p.unrotate && p.had_block == kQuatBlock) {
-    // x_c = sum_j M[j][c mod 4] y_(4 (c/4) + j) of block c/4; results go to registers first
-    float x[2][kPage * kHeadDim / 256];
-    for (int which = 0; which < 2; ++which)
-      for (int k = tid, n = 0; k < kPage * kHeadDim; k += 256, ++n) {
-        const int row = k >> 7, ch = k & 127, blk = ch >> 2, r = ch & 3;
-        const float* y = &buf[which][row][4 * blk];
-        x[which][n] = fmaf(qm[blk][3][r], y[3], fmaf(qm[blk][2][r], y[2], fmaf(qm[blk][1][r], y[1], qm[blk][0][r] * y[0])));
-      }
-    __syncthreads();
-    for (int which = 0; which < 2; ++which)
-      for (int k = tid, n = 0; k < kPage * kHeadDim; k += 256, ++n) (&buf[which][0][0])[k] = x[which][n];
-    __syncthreads();
-  } else if (p.unrotate && p.had_block > 1) {
-    for (int len = 1; len < p.had_block; len <<= 1) {
-      for (int k = tid; k < 2 * kPage * 64; k += 256) {
-        const int row = k >> 6, kk = k & 63;
-        const int jj = (kk / len) * 2 * len + (kk % len);
-        float* r = &buf[0][0][0] + row * kHeadDim;
-        const float u = r[jj], v = r[jj + len];
-        r[jj] = u + v;
-        r[jj + len] = u - v;
-      }
-      __syncthreads();
-    }
-    scale = p.had_block == 128 ? 0.08838834764831845f : 0.125f;
-  }
   const int64_t out_base = ((int64_t)i * p.hkv + h) * kPage * kHeadDim;
   for (int k = tid; k < kPage * kHeadDim; k += 256) {
-    p.out_k[out_base + k] = (&buf[0][0][0])[k] * scale;
-    p.out_v[out_base + k] = (&buf[1][0][0])[k] * scale;
+    p.out_k[out_base + k] = (&buf[0][0][0])[k];
+    p.out_v[out_base + k] = (&buf[1][0][0])[k];
+  }
+}
+
+// With KVQ_UNROTATE: one workgroup per (page, kv head), 4 waves; wave w takes 8 of the page-head's
+// 32 token vectors (waves 0, 1: K slots 0-7, 8-15; waves 2, 3: V slots), each held as one wave
+// holds a 128-vector:
+// channel `lane` in x0, channel `lane + 64` in x1.  The rotation is undone in registers, all 8
+// vectors at once (lane exchanges, no workgroup barrier), and each vector is stored as two
+// coalesced 256-byte runs.
+__global__ __launch_bounds__(256) void dequant_unrotate_kernel(DequantParams p) {
+  const int tid = thread_id();
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int which = wave >> 1;          // 0: K, 1: V
+  const int s0 = 8 * (wave & 1);        // first slot of this wave
+  const int i = block_id_x() / p.hkv, h = block_id_x() % p.hkv;
+  const uint8_t* base = p.pool + ((int64_t)p.page_ids[i] * p.hkv + h) * kPageHeadBytes;
+  // channel c sits in row byte 4 (c % 16) + c / 32, high nibble if bit 4 of c is set: channel
+  // `lane` in byte j0, channel `lane + 64` in byte j0 + 2, the same nibble
+  const int j0 = 4 * (lane & 15) + (lane >> 5), shift = 4 * ((lane >> 4) & 1);
+  float x0[8], x1[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int s = s0 + r;
+    const uint8_t* row = which ? base + kVCodesOff + 256 * (s >> 2) + (s & 3) : base + 64 * s;
+    const int step = which ? 4 : 1;  // V rows are interleaved by slot quads
+    const uint32_t c0 = (row[step * j0] >> shift) & 15u, c1 = (row[step * (j0 + 2)] >> shift) & 15u;
+    const uint32_t pw = *(const uint32_t*)(base + (which ? kVParamsOff : kKParamsOff) + 4 * s);
+    if (p.fmt == 0) {
+      const float sc = f16_bits_to_f32(pw & 0xFFFFu), z = f16_bits_to_f32(pw >> 16);
+      x0[r] = fmaf(sc, (float)c0, z);
+      x1[r] = fmaf(sc, (float)c1, z);
+    } else {
+      // groups of 32 channels: lane's channel in group lane / 32, lane + 64 in group 2 + lane / 32
+      const int g = lane >> 5;
+      x0[r] = ldexpf(e2m1_value(c0), (int)((pw >> (8 * g)) & 255u) - 127);
+      x1[r] = ldexpf(e2m1_value(c1), (int)((pw >> (8 * (g + 2))) & 255u) - 127);
+    }
+  }
+  attn::rotate_rows<8>(x0, x1, p.had_block, p.quat, p.quat_full, lane, true);
+  float* out = (which ? p.out_v : p.out_k) + (((int64_t)i * p.hkv + h) * kPage + s0) * kHeadDim;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    __builtin_nontemporal_store(x0[r], out + r * kHeadDim + lane);
+    __builtin_nontemporal_store(x1[r], out + r * kHeadDim + lane + 64);
   }
 }
 
@@ -145,7 +155,11 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
 }
 
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);
+  // without the rotation the LDS kernel writes fastest (measured); with it, the register kernel
+  if (p.unrotate)
+    hipLaunchKernelGGL(dequant_unrotate_kernel, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
