@@ -5,7 +5,7 @@
 //   MXFP4  y^ = e2m1(code) * 2^(E-127), exact (FP4 with UE8M0 group scales, UltraQuant article).
 // With KVQ_UNROTATE the rotation is undone, x^ = R^T y^: for R_b (symmetric) by the fp32
 // Walsh-Hadamard butterfly of the attention kernels, for the quaternion block rotation by the
-// transposed 4 x 4 block matrices (IsoQuant abstract), both in registers (dequant_unrotate_kernel).
+// transposed 4 x 4 block matrices (IsoQuant abstract), both in registers.
 #include "kvq_attn.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -23,10 +23,16 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
 
 }  // namespace
 
-// Without KVQ_UNROTATE: one workgroup per (page, kv head): 256 threads, thread = (slot s = tid/16,
-// column a = tid%16); each thread owns channels a + 32q + 16e (q = 0..3, e = 0..1) of slot s, i.e.
-// row bytes 4a..4a+3; the values go through LDS so that the workgroup stores each of K and V as
-// 1 KiB runs.
+// One workgroup per (page, kv head), 256 threads.  Load: thread = (slot s = tid/16, column
+// a = tid%16) takes row bytes 4a..4a+3 of slot s, i.e. channels a + 32q + 16e (q = 0..3, e = 0..1),
+// and writes the dequantized values to LDS.  With KVQ_UNROTATE, wave w then takes 8 of the
+// page-head's 32 token vectors (waves 0, 1: K slots 0-7, 8-15; waves 2, 3: V slots) as the
+// attention kernels hold a 128-vector (channel `lane` in x0, `lane + 64` in x1), undoes the
+// rotation in registers (lane exchanges, all 8 vectors at once) and puts them back.  Store: the
+// workgroup writes K and V as interleaved 1 KiB runs.  (Measured: loading each wave's vectors
+// straight into that layout, one byte load per channel pair, took 36.4 us against 25.5 for the
+// bench's 1024 pages x 8 kv heads, with or without the rotation.)
+template <bool UNROTATE>
 __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   __shared__ float buf[2][kPage][kHeadDim];
   const int tid = thread_id();
@@ -58,55 +64,27 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
     }
   }
   __syncthreads();
+  if constexpr (UNROTATE) {
+    const int lane = tid & 63, wave = tid >> 6;
+    const int which = wave >> 1, s0 = 8 * (wave & 1);
+    float x0[8], x1[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      x0[r] = buf[which][s0 + r][lane];
+      x1[r] = buf[which][s0 + r][lane + 64];
+    }
+    attn::rotate_rows<8>(x0, x1, p.had_block, p.quat, p.quat_full, lane, true);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {  // each wave rewrites only the rows it read
+      buf[which][s0 + r][lane] = x0[r];
+      buf[which][s0 + r][lane + 64] = x1[r];
+    }
+    __syncthreads();
+  }
   const int64_t out_base = ((int64_t)i * p.hkv + h) * kPage * kHeadDim;
   for (int k = tid; k < kPage * kHeadDim; k += 256) {
-    p.out_k[out_base + k] = (&buf[0][0][0])[k];
-    p.out_v[out_base + k] = (&buf[1][0][0])[k];
-  }
-}
-
-// With KVQ_UNROTATE: one workgroup per (page, kv head), 4 waves; wave w takes 8 of the page-head's
-// 32 token vectors (waves 0, 1: K slots 0-7, 8-15; waves 2, 3: V slots), each held as one wave
-// holds a 128-vector:
-// channel `lane` in x0, channel `lane + 64` in x1.  The rotation is undone in registers, all 8
-// vectors at once (lane exchanges, no workgroup barrier), and each vector is stored as two
-// coalesced 256-byte runs.
-__global__ __launch_bounds__(256) void dequant_unrotate_kernel(DequantParams p) {
-  const int tid = thread_id();
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int which = wave >> 1;          // 0: K, 1: V
-  const int s0 = 8 * (wave & 1);        // first slot of this wave
-  const int i = block_id_x() / p.hkv, h = block_id_x() % p.hkv;
-  const uint8_t* base = p.pool + ((int64_t)p.page_ids[i] * p.hkv + h) * kPageHeadBytes;
-  // channel c sits in row byte 4 (c % 16) + c / 32, high nibble if bit 4 of c is set: channel
-  // `lane` in byte j0, channel `lane + 64` in byte j0 + 2, the same nibble
-  const int j0 = 4 * (lane & 15) + (lane >> 5), shift = 4 * ((lane >> 4) & 1);
-  float x0[8], x1[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int s = s0 + r;
-    const uint8_t* row = which ? base + kVCodesOff + 256 * (s >> 2) + (s & 3) : base + 64 * s;
-    const int step = which ? 4 : 1;  // V rows are interleaved by slot quads
-    const uint32_t c0 = (row[step * j0] >> shift) & 15u, c1 = (row[step * (j0 + 2)] >> shift) & 15u;
-    const uint32_t pw = *(const uint32_t*)(base + (which ? kVParamsOff : kKParamsOff) + 4 * s);
-    if (p.fmt == 0) {
-      const float sc = f16_bits_to_f32(pw & 0xFFFFu), z = f16_bits_to_f32(pw >> 16);
-      x0[r] = fmaf(sc, (float)c0, z);
-      x1[r] = fmaf(sc, (float)c1, z);
-    } else {
-      // groups of 32 channels: lane's channel in group lane / 32, lane + 64 in group 2 + lane / 32
-      const int g = lane >> 5;
-      x0[r] = ldexpf(e2m1_value(c0), (int)((pw >> (8 * g)) & 255u) - 127);
-      x1[r] = ldexpf(e2m1_value(c1), (int)((pw >> (8 * (g + 2))) & 255u) - 127);
-    }
-  }
-  attn::rotate_rows<8>(x0, x1, p.had_block, p.quat, p.quat_full, lane, true);
-  float* out = (which ? p.out_v : p.out_k) + (((int64_t)i * p.hkv + h) * kPage + s0) * kHeadDim;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    __builtin_nontemporal_store(x0[r], out + r * kHeadDim + lane);
-    __builtin_nontemporal_store(x1[r], out + r * kHeadDim + lane + 64);
+    __builtin_nontemporal_store((&buf[0][0][0])[k], p.out_k + out_base + k);
+    __builtin_nontemporal_store((&buf[1][0][0])[k], p.out_v + out_base + k);
   }
 }
 
@@ -155,11 +133,10 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
 }
 
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
-  // without the rotation the LDS kernel writes fastest (measured); with it, the register kernel
   if (p.unrotate)
-    hipLaunchKernelGGL(dequant_unrotate_kernel, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
