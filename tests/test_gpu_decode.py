@@ -193,7 +193,7 @@ def test_decode_workspace_reuse(monkeypatch):
     assert int(counters.count_nonzero()) == 0
 
 
-@pytest.mark.parametrize("hb", [64, 128])
+@pytest.mark.parametrize("hb", [1, 64, 128])
 def test_dequant_pages(hb):
     rng = np.random.default_rng(30 + hb)
     lens = [40, 70]
@@ -211,6 +211,27 @@ def test_dequant_pages(hb):
     for got, ref in ((ku, kur), (vu, vur)):
         got = got.cpu().numpy().astype(np.float64)
         assert np.abs(got - ref).max() <= 1e-6 * np.abs(ref).max()
+    if hb == 1:  # no rotation to undo: the same values as the plain path
+        assert torch.equal(ku, k) and torch.equal(vu, v)
+
+
+def test_dequant_many_pages_all_heads():
+    # every page of a 2 x 2400-token cache with 8 kv heads, in a permuted order, both paths
+    rng = np.random.default_rng(64)
+    lens = [2400, 2399]
+    pool, table = oracle_cache(rng, lens, 8, 128)
+    print("[dequant] many pages", flush=True)
+    cache = kvq.Cache(pool.shape[0], 8, 128, pool=torch.from_numpy(pool).cuda())
+    ids = rng.permutation(np.concatenate([table[0, :150], table[1, :150]])).astype(np.int32)
+    for unrot in (False, True):
+        k, v = kvq.dequant_pages(cache, torch.from_numpy(ids).cuda(), unrotate=unrot)
+        kr, vr = oracle.dequant_pages(pool, ids, 128, unrotate=unrot)
+        for got, ref in ((k, kr), (v, vr)):
+            got = got.cpu().numpy().astype(np.float64)
+            if unrot:
+                assert np.abs(got - ref).max() <= 1e-6 * np.abs(ref).max()
+            else:
+                assert np.array_equal(got, ref.astype(np.float32))
 
 
 @pytest.mark.parametrize("scaled", [False, True])
@@ -262,6 +283,11 @@ def test_dequant_pages_mxfp4():
     # e2m1 * 2^(E-127) is exact in fp32
     assert np.array_equal(k.cpu().numpy(), kr.astype(np.float32))
     assert np.array_equal(v.cpu().numpy(), vr.astype(np.float32))
+    ku, vu = kvq.dequant_pages(cache, torch.from_numpy(ids).cuda(), unrotate=True)
+    kur, vur = oracle.dequant_pages(pool, ids, 128, oracle.FMT_MXFP4, unrotate=True)
+    for got, ref in ((ku, kur), (vu, vur)):
+        got = got.cpu().numpy().astype(np.float64)
+        assert np.abs(got - ref).max() <= 1e-6 * np.abs(ref).max()
 
 
 @pytest.mark.parametrize("group", [2, 3, 5, 6, 7])
