@@ -608,9 +608,9 @@ def main():
     ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--profile-run", action="store_true",
-                    help="run for rocprofv3: the fused steps as timed by default, the copy probe, "
-                         "three prefill appends, short long/ragged, tiny and MXFP4 legs; no "
-                         "two-launch step and no CPU leg")
+                    help="run for rocprofv3: the fused steps as timed by default, the copy and read "
+                         "probes, short page-dequantization legs, three prefill appends, short "
+                         "long/ragged, tiny and MXFP4 legs; no two-launch step and no CPU leg")
     args = ap.parse_args()
     if args.profile_run:
         args.no_cpu = True
