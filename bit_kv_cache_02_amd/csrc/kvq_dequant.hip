@@ -1,5 +1,5 @@
-// kvq_dequant_page: whole pages of the 4-bit cache back to fp32, plus the plain copy kernel used to
-// measure HBM bandwidth.
+// kvq_dequant_page: whole pages of the 4-bit cache back to fp32, plus the copy and read-only
+// kernels used to measure HBM bandwidth (kvq_hbm_copy, kvq_hbm_read).
 //   INT4   y^ = fma(scale, code, zero): a single rounding of the exact value (token-wise INT4 with an
 //          fp16 scale and zero, SAW-INT4 summary, "Summary"/"Method").
 //   MXFP4  y^ = e2m1(code) * 2^(E-127), exact (FP4 with UE8M0 group scales, UltraQuant article).
