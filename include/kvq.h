@@ -137,7 +137,11 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t kv_
 
 /*
  * Bytes of workspace kvq_decode_attn and kvq_decode_step need for these sizes (same
- * arguments as there).  The workspace holds the partial results of (sequence, kv head) pairs
+ * arguments as there).  No passage of the pages defines it: it is the storage of the split
+ * form of the online softmax (per split, the running maximum, the running sum and the
+ * unnormalised output of every query head), which a long sequence's decode uses to spread its
+ * pages over several workgroups, and which the pages' decode attention implies only as an
+ * implementation of the same softmax(q'.K'^T) V' result.  The workspace holds the partial results of (sequence, kv head) pairs
  * split over several workgroups and one counter per pair, which the last of a pair's
  * workgroups to finish uses to know that it merges the partials.  It must be zero-filled once
  * before its first use (e.g. hipMemset when it is allocated).  Every call leaves its counters
@@ -240,6 +244,12 @@ int kvq_prefill_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, flo
 
 /*
  * kvq_dequant_page -- dequantize whole pages (all 16 slots, all kv heads) to fp32.
+ * (SAW-INT4 summary, "Method": token-wise INT4 quantization -- read here as asymmetric, a
+ * value being the vector's stored fp16 scale times the code plus its stored fp16 zero;
+ * UltraQuant article, section on how the method works: FP4 KV elements with UE8M0 group
+ * scales, a value being the e2m1 element times its group's power of two.  The rotation undone
+ * with KVQ_UNROTATE is the block-diagonal Hadamard rotation of the SAW-INT4 "Method", or
+ * IsoQuant's quaternion block rotation.)
  *   page_ids     device int32[n], each < num_pages.
  *   out_k, out_v device float[n][num_kv_heads][16][128]; channel order is natural.
  *   flags        0: values in the rotated basis (y^ = scale*code + zero, one fp32 rounding,

@@ -199,6 +199,28 @@ def test_append_mxfp4_exact_grid():
     assert flips == 0
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_append_mxfp4_negative_values_rounding_to_zero(dtype):
+    # every group holds one element of magnitude 4 or 6 times 2^k (the exponent is exact) and 31
+    # elements with r = x / 2^k in (-0.24, -1e-3) or (1e-3, 0.24): all round to magnitude zero,
+    # far from the tie at 0.25 and from the sign boundary, so the negative ones must be code 8
+    # and the positive ones code 0, with no tolerated deviation
+    rng = np.random.default_rng(202)
+    t, hkv = 48, 2
+    k_exp = rng.integers(-8, 8, (t, hkv, 4))
+    mag = rng.uniform(1e-3, 0.24, (t, hkv, 4, 32))
+    r = np.where(rng.integers(0, 2, mag.shape) == 1, -mag, mag)
+    r[..., 0] = rng.choice([4.0, 6.0, -4.0, -6.0], (t, hkv, 4))
+    x = (r * 2.0 ** k_exp[..., None]).reshape(t, hkv, 128).astype(np.float32)
+    x = torch.from_numpy(x).to(TDT[dtype]).float().numpy()
+    table = np.array([[2, 0, 1]], np.int32)
+    cache, _, flips = run_append(f"mxfp4-neg-zero/{dtype}", x, x[::-1].copy(), [t], [0], table, 3, hkv, 1,
+                                 oracle.FMT_MXFP4, dtype)
+    assert flips == 0
+    codes, _ = parity.appended_entries(cache.pool.cpu().numpy(), np.array([0, t]), np.array([0]), table, "k")
+    assert (codes == 8).sum() > 1000 and (codes == 0).sum() > 1000
+
+
 @pytest.mark.parametrize("fmt", [oracle.FMT_INT4, oracle.FMT_MXFP4])
 @pytest.mark.parametrize("hb", [1, 128])
 def test_append_degenerate_vectors(fmt, hb):

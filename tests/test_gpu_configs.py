@@ -113,6 +113,82 @@ def test_config_llama():
     _check_decode_workload("llama", [0, 13, 31])
 
 
+def test_config_llama_step():
+    # the call the benchmark times, at its size: kvq_decode_step over 32 sequences x 4096 tokens,
+    # 8 kv heads (the 8-wave plan, 256 pages per (sequence, kv head), the appending waves also
+    # streaming the last page).  The GPU appends the 4095 cached tokens of every sequence, then
+    # the step appends token 4096 and attends.  Sampled sequences: the step token's bytes follow
+    # the append rules, the earlier bytes are unchanged, nothing else is written, and the
+    # attention matches the oracle run on the pool as the GPU left it.  A second step call with
+    # bf16 output (the benchmark's dtype) gives the round-to-nearest-even of the fp32 result.
+    w = wl.WORKLOADS["llama"]
+    sample = [0, 13, 31]
+    print("[config] llama step: building", flush=True)
+    lens = wl.seq_lens(w)
+    table, num_pages = wl.block_table(w, lens)
+    dev = torch.device("cuda")
+    cache = kvq.Cache(num_pages, w.num_kv_heads, w.had_block, w.fmt, fill=SENT)
+    bt = torch.from_numpy(table).to(dev)
+    pre = lens - 1
+    new_k = np.zeros((w.batch, w.num_kv_heads, 128), np.float32)
+    new_v = np.zeros_like(new_k)
+    for b0 in range(0, w.batch, 8):
+        bs = list(range(b0, b0 + 8))
+        ks, vs = [], []
+        for b in bs:
+            k, v = wl.sequence_kv(w, b, int(lens[b]))
+            ks.append(k[:-1])
+            vs.append(v[:-1])
+            new_k[b], new_v[b] = k[-1], v[-1]
+        cnt = np.zeros(w.batch, np.int64)
+        cnt[bs] = pre[bs]
+        cu = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+        kvq.append(cache, torch.from_numpy(np.concatenate(ks)).to(TDT[w.kv_dtype]).to(dev),
+                   torch.from_numpy(np.concatenate(vs)).to(TDT[w.kv_dtype]).to(dev),
+                   torch.from_numpy(cu).to(dev), torch.zeros(w.batch, dtype=torch.int32, device=dev),
+                   bt, int(pre.max()))
+    torch.cuda.synchronize()
+    pool0 = cache.pool.cpu().numpy()
+    q_t = torch.from_numpy(wl.queries(w)).to(QDT[w.q_dtype])
+    kn = torch.from_numpy(new_k).to(TDT[w.kv_dtype]).to(dev)
+    vn = torch.from_numpy(new_v).to(TDT[w.kv_dtype]).to(dev)
+    sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    out = kvq.decode_step(cache, kn, vn, q_t.to(dev), sl, bt, int(lens.max()), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    gpu_pool = cache.pool.cpu().numpy()
+
+    cu_pre = np.concatenate([[0], np.cumsum(pre)])
+    prior = parity.touched_mask(pool0.shape, cu_pre, np.zeros(w.batch, np.int64), table)
+    step_mask = parity.touched_mask(pool0.shape, np.arange(w.batch + 1), pre, table)
+    keep = ~step_mask
+    assert np.array_equal(gpu_pool[keep], pool0[keep]), "llama step: bytes outside the step tokens changed"
+    assert not (prior & step_mask).any()
+    flips = 0
+    for b in sample:
+        infos = {}
+        for which, x in (("k", new_k[b:b + 1]), ("v", new_v[b:b + 1])):
+            infos[which] = oracle.paged.encode(x, w.had_block, FMT[w.fmt])[2]
+        cu1 = np.array([0, 1])
+        st = pre[b:b + 1]
+        for which in ("k", "v"):
+            codes, params = parity.appended_entries(gpu_pool, cu1, st, table[b:b + 1], which)
+            flips += parity.check_int4_entries(codes, params, infos[which], f"llama-step/{b}/{which}")
+    ref = oracle.decode_attention(gpu_pool, q_t.float().numpy(), lens, table, w.had_block, FMT[w.fmt],
+                                  seqs=sample)
+    err = parity.attn_row_error(got[sample], ref[sample])
+    print(f"[config] llama step: {flips} tolerated flips, max row err {err.max():.3e} on sequences {sample}",
+          flush=True)
+    assert err.max() <= parity.ATTN_TOL
+
+    # the benchmark's output dtype: bf16 equals RNE of the fp32 result (the same token appended
+    # again at the same slot writes the same bytes)
+    out16 = kvq.decode_step(cache, kn, vn, q_t.to(dev), sl, bt, int(lens.max()), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.pool.cpu(), torch.from_numpy(gpu_pool))
+    assert torch.equal(out16.cpu(), out.cpu().to(torch.bfloat16))
+
+
 def test_config_long_ragged():
     w = wl.WORKLOADS["long"]
     lens = wl.seq_lens(w)
