@@ -697,7 +697,6 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // the same size (room for kCounterUnits units) for every call with at most that many units, so
 // such calls share one layout and a call never finds another call's partials where it expects
 // zeroed counters.
-constexpr size_t kCounterUnits = 16384;
 
 static size_t counter_bytes(size_t units) { return align256(4 * (units > kCounterUnits ? units : kCounterUnits)); }
 

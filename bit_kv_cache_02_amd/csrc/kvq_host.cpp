@@ -9,8 +9,16 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kvq_internal.h"
+
+// Scratch of kvq_decode_step_noalloc: the split-run partials and merge counters that the other
+// decode entry points keep in the caller's workspace.  One copy per device, held until the
+// process ends.  Host code never passes this name to a kernel: it is a host-side stand-in, and
+// the device address comes from hipGetSymbolAddress (scratch_for_device below).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -81,6 +89,56 @@ int device_check(const kvq::CheckParams& c, void* stream, const char* what) {
     default: msg = "unknown violation"; break;
   }
   return fail(KVQ_ERR_INVALID_ARG, "%s: KVQ_DEBUG_CHECKS: %s (index %d)", what, msg, index);
+}
+
+// Zero n 32-bit words (the scratch's merge counters).  A kernel rather than hipMemsetAsync, so
+// that a call made under stream capture records an ordinary kernel node.
+__global__ __launch_bounds__(256) void zero_words(uint32_t* p, int n) {
+  const int i = (int)(__builtin_amdgcn_workgroup_id_x() * 256 + __builtin_amdgcn_workitem_id_x());
+  if (i < n) p[i] = 0u;
+}
+
+// Per device: the device address of `scratch`, and whether its counter region has been cleared
+// by a launch that ran eagerly (not into a graph being captured).
+constexpr int kMaxScratchDevices = 64;
+struct ScratchSlot {
+  void* ptr;
+  bool cleared;
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxScratchDevices];
+
+// The scratch of the device that `stream` runs on (it must be the current device).  The first
+// call on a device looks up the array's address (hipGetSymbolAddress, with that device current)
+// and clears the merge counters on `stream`; every call that runs to completion leaves them at
+// zero again.  A clear recorded into a graph under capture is repeated until one runs eagerly.
+int scratch_for_device(hipStream_t stream, void** out) {
+  int dev = 0, sdev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  e = hipStreamGetDevice(stream, &sdev);
+  if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+  if (sdev != dev) return fail(KVQ_ERR_INVALID_ARG, "stream belongs to device %d, the current device is %d", sdev, dev);
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(KVQ_ERR_UNSUPPORTED, "device %d: scratch kept for devices 0..%d", dev, kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot& slot = g_scratch[dev];
+  if (!slot.ptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(KVQ_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    slot.ptr = p;
+  }
+  if (!slot.cleared) {
+    hipLaunchKernelGGL(zero_words, dim3((unsigned)((kvq::kCounterUnits + 255) / 256)), dim3(256), 0, stream,
+                       (uint32_t*)slot.ptr, (int)kvq::kCounterUnits);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "scratch counter clear launch");
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) slot.cleared = true;
+  }
+  *out = slot.ptr;
+  return KVQ_OK;
 }
 
 }  // namespace
@@ -179,7 +237,8 @@ static int decode_common(const kvq_cache* cache, const void* knew, const void* v
                          const void* q, int32_t q_dtype, float q_scale, int32_t num_q_heads, int32_t num_seqs,
                          const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
                          int32_t max_pages, float sm_scale, void* out, int32_t out_dtype, uint32_t flags,
-                         void* workspace, size_t workspace_bytes, void* stream, const char* what) {
+                         void* workspace, size_t workspace_bytes, void* stream, const char* what,
+                         bool use_scratch = false) {
   int st = decode_geometry(cache, num_q_heads, num_seqs, max_seq_len);
   if (st != KVQ_OK) return st;
   if (!q || !seq_lens || !block_table || !out) return fail(KVQ_ERR_INVALID_ARG, "q, seq_lens, block_table and out must not be NULL");
@@ -210,6 +269,17 @@ static int decode_common(const kvq_cache* cache, const void* knew, const void* v
   if ((int64_t)num_seqs * hkv * plan.nsplit > 0x7FFFFFFF) return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
   kvq::DecodeParams p;
   memset(&p, 0, sizeof(p));
+  if (use_scratch && need > 0) {
+    // the library's fixed scratch stands in for the workspace
+    if ((size_t)num_seqs * hkv > kvq::kCounterUnits)
+      return fail(KVQ_ERR_WORKSPACE, "%lld (sequence, kv head) pairs: the fixed scratch serves at most %zu",
+                  (long long)num_seqs * hkv, kvq::kCounterUnits);
+    if (need > kScratchBytes)
+      return fail(KVQ_ERR_WORKSPACE, "this call needs %zu bytes of scratch, above the fixed maximum of %zu", need,
+                  kScratchBytes);
+    workspace_bytes = kScratchBytes;
+    if (int s2 = scratch_for_device((hipStream_t)stream, &workspace)) return s2;
+  }
   if (need > 0) {
     if (!workspace) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (workspace_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes given, %zu required", workspace_bytes, need);
@@ -277,6 +347,18 @@ int kvq_decode_step(const kvq_cache* cache, const void* k, const void* v, int32_
   return decode_common(cache, k, v, kv_dtype, q, q_dtype, q_scale, num_q_heads, num_seqs, seq_lens,
                        max_seq_len, block_table, max_pages, sm_scale, out, out_dtype, flags, workspace,
                        workspace_bytes, stream, "kvq_decode_step launch");
+}
+
+int kvq_decode_step_noalloc(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype, const void* q,
+                            int32_t q_dtype, float q_scale, int32_t num_q_heads, int32_t num_seqs,
+                            const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                            int32_t max_pages, float sm_scale, void* out, int32_t out_dtype, uint32_t flags,
+                            void* stream) {
+  g_last_error[0] = 0;
+  if (!k || !v) return fail(KVQ_ERR_INVALID_ARG, "k and v must not be NULL");
+  return decode_common(cache, k, v, kv_dtype, q, q_dtype, q_scale, num_q_heads, num_seqs, seq_lens,
+                       max_seq_len, block_table, max_pages, sm_scale, out, out_dtype, flags, nullptr, 0, stream,
+                       "kvq_decode_step_noalloc launch", true);
 }
 
 int kvq_prefill_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, float q_scale, int32_t num_q_heads,

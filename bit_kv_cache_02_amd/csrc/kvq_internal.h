@@ -130,6 +130,9 @@ hipError_t run_check(const CheckParams& c, hipStream_t stream, int* code, int* i
 
 hipError_t launch_append(const AppendParams& p, bool bf16, int had_block, int fmt, hipStream_t stream);
 DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len);
+// the decode workspace's counter region has room for this many (sequence, kv head) units for
+// every call with at most that many, so such calls share one workspace layout
+constexpr size_t kCounterUnits = 16384;
 size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int hkv, int group);
 void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, int group, float** part_ml,
                      float** part_o, uint32_t** counters);

@@ -60,6 +60,9 @@ SIGNATURES = [
     ("kvq_decode_step", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _P, _I32, _P, _I32,
                                        ctypes.c_float, _I32, _I32, _P, _I32, _P, _I32, ctypes.c_float,
                                        _P, _I32, ctypes.c_uint32, _P, ctypes.c_size_t, _P]),
+    ("kvq_decode_step_noalloc", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _P, _I32, _P, _I32,
+                                               ctypes.c_float, _I32, _I32, _P, _I32, _P, _I32,
+                                               ctypes.c_float, _P, _I32, ctypes.c_uint32, _P]),
     ("kvq_prefill_attn", ctypes.c_int, [ctypes.POINTER(KvqCacheDesc), _P, _I32, ctypes.c_float, _I32, _I32,
                                         _I32, _P, _P, _I32, _I32, _P, _I32, ctypes.c_float, _P, _I32,
                                         ctypes.c_uint32, _P]),
@@ -251,6 +254,35 @@ def decode_step(cache: Cache, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
                                _flags(rotated, scaled_mfma), _ptr(workspace),
                                0 if workspace is None else workspace.numel(), _stream())
     _check(st, "kvq_decode_step")
+    return out
+
+
+def decode_step_noalloc(cache: Cache, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
+                        seq_lens: torch.Tensor, block_table: torch.Tensor, max_seq_len: int,
+                        out: torch.Tensor, q_scale: float = 1.0, sm_scale: Optional[float] = None,
+                        rotated: bool = False, scaled_mfma: bool = False) -> torch.Tensor:
+    """kvq_decode_step with the library's fixed device scratch instead of a workspace
+    (kvq_decode_step_noalloc): the caller passes `out`, and the call allocates nothing."""
+    _require(k, "k")
+    _require(v, "v")
+    _require(q, "q")
+    _require(seq_lens, "seq_lens", torch.int32)
+    _require(block_table, "block_table", torch.int32)
+    _require(out, "out")
+    b, hq, dim = q.shape
+    if k.shape != (b, cache.num_kv_heads, dim) or v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError(f"k and v must both be [{b}][{cache.num_kv_heads}][{dim}] of one dtype")
+    if out.shape != q.shape:
+        raise ValueError(f"out must be {tuple(q.shape)}")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    d = cache.desc()
+    st = lib().kvq_decode_step_noalloc(ctypes.byref(d), _ptr(k), _ptr(v), _DTYPE_CODE[k.dtype], _ptr(q),
+                                       _DTYPE_CODE[q.dtype], float(q_scale), hq, b, _ptr(seq_lens),
+                                       int(max_seq_len), _ptr(block_table), block_table.shape[1],
+                                       float(sm_scale), _ptr(out), _DTYPE_CODE[out.dtype],
+                                       _flags(rotated, scaled_mfma), _stream())
+    _check(st, "kvq_decode_step_noalloc")
     return out
 
 

@@ -215,6 +215,29 @@ int kvq_decode_step(const kvq_cache* cache, const void* k, const void* v, int32_
                     void* stream);
 
 /*
+ * kvq_decode_step_noalloc -- kvq_decode_step without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It allocates nothing.  The split-run partials and merge counters live in a
+ * fixed scratch array inside the library, 16 MiB per device, held by every device the library
+ * runs on until the process ends.
+ *
+ * Arguments and result are those of kvq_decode_step without `workspace` / `workspace_bytes`;
+ * the same kernels run.  `stream` must belong to the current device.
+ * Limits: at most 16384 (sequence, kv head) pairs, and a call whose kvq_decode_workspace_bytes
+ * exceeds 16 MiB (16777216 bytes) returns KVQ_ERR_WORKSPACE before any HIP call.
+ * The first call on a device looks the scratch up and clears its merge counters with a kernel on
+ * `stream` (a clear recorded into a graph under capture is repeated by later calls until one runs
+ * eagerly); every call that runs to completion leaves them at zero again.
+ * All calls on one device share that device's scratch: calls that overlap in time on one device
+ * (other streams, other threads, concurrent graph replays) race and give wrong results.
+ */
+int kvq_decode_step_noalloc(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype,
+                            const void* q, int32_t q_dtype, float q_scale, int32_t num_q_heads,
+                            int32_t num_seqs, const int32_t* seq_lens, int32_t max_seq_len,
+                            const int32_t* block_table, int32_t max_pages, float sm_scale, void* out,
+                            int32_t out_dtype, uint32_t flags, void* stream);
+
+/*
  * kvq_prefill_attn -- chunked-prefill attention over the 4-bit cache: the new tokens of a turn
  * attend over the resident prefix and, causally, over each other.
  * (UltraQuant article, section on what it showed: prefixes kept resident in the 4-bit cache

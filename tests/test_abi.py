@@ -250,3 +250,41 @@ def test_python_layer_raises_typed_errors():
         kvq._check(kvq.KVQ_ERR_INVALID_ARG, "x")
     with pytest.raises(kvq.KvqError):
         kvq._check(kvq.KVQ_ERR_HIP, "x")
+
+
+def _step_noalloc(desc, **kw):
+    args = dict(k=FAKE, v=FAKE, kvdt=kvq.BF16, q=FAKE, qdt=kvq.BF16, qs=1.0, hq=8, B=2, sl=FAKE, msl=100,
+                bt=FAKE, mp=8, sm=0.1, out=FAKE, odt=kvq.F32, flags=0)
+    args.update(kw)
+    return kvq.lib().kvq_decode_step_noalloc(ctypes.byref(desc), args["k"], args["v"], args["kvdt"], args["q"],
+                                             args["qdt"], args["qs"], args["hq"], args["B"], args["sl"],
+                                             args["msl"], args["bt"], args["mp"], args["sm"], args["out"],
+                                             args["odt"], args["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(kvdt=kvq.F32), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(hq=3), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(msl=129), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(q=None), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(flags=kvq.MX_SCALED_MFMA), kvq.KVQ_ERR_UNSUPPORTED),
+])
+def test_decode_step_noalloc_rejects_bad_args(kw, status):
+    assert _step_noalloc(_desc(), **kw) == status
+
+
+def test_decode_step_noalloc_limits():
+    # sizes beyond the fixed scratch are refused on the host, before any HIP call
+    lib = kvq.lib()
+    big = _desc(num_kv_heads=8, num_pages=1 << 22)
+    # 512 sequences x 8 kv heads of 128K tokens: the split partials need more than 16 MiB
+    need = lib.kvq_decode_workspace_bytes(ctypes.byref(big), 64, 512, 131072)
+    assert need > 16 << 20
+    assert _step_noalloc(big, hq=64, B=512, msl=131072, mp=8192) == kvq.KVQ_ERR_WORKSPACE
+    assert b"16777216" in lib.kvq_last_error()
+    # more (sequence, kv head) pairs than the scratch's counters serve, on a plan that splits
+    assert lib.kvq_decode_workspace_bytes(ctypes.byref(big), 8, 2049, 9600) > 0
+    assert _step_noalloc(big, hq=8, B=2049, msl=9600, mp=600) == kvq.KVQ_ERR_WORKSPACE
+    assert b"16384" in lib.kvq_last_error()
+    assert _step_noalloc(big, hq=64, B=0) == kvq.KVQ_OK
