@@ -116,57 +116,65 @@ def time_two_call_steps(w, caches, step, lens, steps, warmup):
     return app, dec, e0.elapsed_time(e1) * 1e3 / steps
 
 
-def step_graphs(w, caches, step, lens):
-    """HIP graphs of kvq_decode_step launches: one holding a step on every layer cache in turn,
-    and one per layer cache (for a step count that is not a multiple of the layer count)."""
+def step_graphs(w, caches, step, lens, steps):
+    """HIP graphs of kvq_decode_step launches cycling over the layer caches: one of
+    chunk = min(steps, 64) launches and, when steps is not a multiple of it, one of the remainder,
+    so that a timed run of `steps` launches is whole graph replays with every kernel launched back
+    to back inside them."""
     dev = step["q"].device
     max_len = int(lens.max())
     ws = kvq.make_workspace(caches[0], w.num_q_heads, w.batch, max_len, dev)
     out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    n_layers = len(caches)
 
-    def one(c):
-        kvq.decode_step(c, step["k"], step["v"], step["q"], step["lens"], step["bt"], max_len, out=out,
-                        workspace=ws)
+    def launches(first, count):
+        for i in range(first, first + count):
+            kvq.decode_step(caches[i % n_layers], step["k"], step["v"], step["q"], step["lens"], step["bt"],
+                            max_len, out=out, workspace=ws)
 
+    chunk = max(1, min(steps, 64))
+    rem = steps % chunk
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for c in caches:
-            one(c)
+        launches(0, n_layers)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    every = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(every):
-        for c in caches:
-            one(c)
-    single = []
-    for c in caches:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            one(c)
-        single.append(g)
+    main = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(main):
+        launches(0, chunk)
+    tail = None
+    if rem:
+        tail = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(tail):
+            launches(chunk, rem)
     torch.cuda.synchronize()
-    return every, single
+    return main, chunk, tail, rem
 
 
-def time_graph_steps(every, single, steps, warmup):
-    """Exactly `steps` steps: steps // L replays of the all-layers graph, then the remaining
-    steps from the per-layer graphs.  Returns the wall time and the launch stream's event time
-    per step over the same region."""
-    n_layers = len(single)
+def time_graph_steps(main, chunk, tail, rem, steps, warmup):
+    """Exactly `steps` launches: steps // chunk replays of the main graph, then the remainder
+    graph.  Every graph is replayed before timing (its first replay uploads it), the clocks settle
+    for ~0.3 s, and at least `warmup` launches run untimed.  Returns the wall time and the launch
+    stream's event time per launch over the timed region."""
+    def run():
+        for _ in range(steps // chunk):
+            main.replay()
+        if tail is not None:
+            tail.replay()
 
-    def run(n):
-        for _ in range(n // n_layers):
-            every.replay()
-        for i in range(n % n_layers):
-            single[i].replay()
-
-    run(warmup)
+    main.replay()
+    if tail is not None:
+        tail.replay()
+    torch.cuda.synchronize()
+    settle(main.replay)
+    for _ in range(-(-warmup // chunk)):
+        main.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    run(steps)
+    run()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -583,17 +591,36 @@ def code_sha256(paths):
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
+def profile_record(path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_source_sha256"):
+    """The committed rocprofv3 record of a kernel, if the kernel's code has not changed since it
+    was taken (else None)."""
+    try:
+        rec = json.load(open(path))
+        if rec.get(key) != code_sha256(src_path):
+            return None
+        return rec
+    except (OSError, ValueError):
+        return None
+
+
 def traffic_entry(algo_bytes, path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_source_sha256"):
     """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE, each
     scaled by what the counter reads for the bench's 1 GiB copy), if the kernel's code has not
     changed since they were taken."""
+    rec = profile_record(path, src_path, key)
     try:
-        rec = json.load(open(path))
-        src = code_sha256(src_path)
-        if rec.get(key) != src:
-            return None
-        return int(rec["hbm_bytes_per_launch"])
-    except (OSError, ValueError, KeyError):
+        return None if rec is None else int(rec["hbm_bytes_per_launch"])
+    except (KeyError, TypeError, ValueError):
+        return None
+
+
+def trace_avg_us(path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_source_sha256"):
+    """The kernel's average duration in the committed rocprofv3 kernel trace of bench.py
+    --profile-run, if the kernel's code has not changed since (else None)."""
+    rec = profile_record(path, src_path, key)
+    try:
+        return None if rec is None else float(rec["kernel_trace_avg_us"])
+    except (KeyError, TypeError, ValueError):
         return None
 
 
@@ -646,9 +673,9 @@ def main():
             "decode_frac_of_hbm_peak": round(dbytes / dec_avg_us / 1e3 / HBM_PEAK_GBPS, 4),
         }
     log("[bench] capturing the fused step into HIP graphs")
-    every, single = step_graphs(w, caches, step, lens)
+    graphs = step_graphs(w, caches, step, lens, args.steps)
     log("[bench] timing fused steps")
-    wall, step_us = time_graph_steps(every, single, args.steps, args.warmup)
+    wall, step_us = time_graph_steps(*graphs, args.steps, args.warmup)
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = step_bytes / step_us / 1e3
@@ -670,7 +697,7 @@ def main():
             "workload": "Llama-3-8B layer decode step: batch 32 x context 4096, 32 q / 8 kv heads, "
                         "head_dim 128, page 16, bf16 K/V/q, token-wise INT4 (fp16 scale+zero), Hadamard "
                         "block 128; append 1 token per sequence + decode attention in one launch "
-                        "(kvq_decode_step), one HIP graph replay per 8 steps; 8 layer caches cycled",
+                        "(kvq_decode_step), HIP graphs of up to 64 launches; 8 layer caches cycled",
             "batch": w.batch, "context": int(lens[0]), "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads, "had_block": w.had_block, "layers_cycled": args.layers,
             "out_dtype": "bf16",
@@ -689,10 +716,12 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic_entry(step_bytes),
+            "launch_us_events": round(step_us, 3),
+            "launch_us_kernel_trace": trace_avg_us(),
         },
         **res,
     }
-    del every, single
+    del graphs
     if not args.no_prefill:
         log("[bench] chunked-prefill attention")
         res["prefill_attention"] = time_prefill_attention(w, caches, lens, dev)

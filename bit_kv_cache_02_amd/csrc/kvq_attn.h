@@ -231,17 +231,68 @@ __device__ __forceinline__ PageI4 unpack_i4(const PageData<0>& pg, int vlimit, i
   return u;
 }
 
-// One set of 8 rows (A-tile rows 2g+limb) against an unpacked INT4 page.
-// valid0 / valid1: tokens of the page that rows x0 / x1 attend (decode: the same count).
+// The INT4 score path holds q' of a head as a 24-bit fixed-point number Q = rne(q' / delta),
+// delta = max|q'| / kQFix, split into three int8 limbs Q = 65536 hi + 256 mid + lo (hi in
+// [-122, 122], mid and lo in [-128, 127]); the limbs are A-tile rows of the integer MFMA, whose
+// output row r lands in lane group r / 4.  Two layouts:
+//   one head per lane group (at most 4 heads): rows 4g, 4g+1, 4g+2 hold hi, mid, lo of head g
+//     (row 4g+3 zero), so lane group g holds all of head g's partial sums; its p~ parts take
+//     rows 4g, 4g+1 of the p.V tile, so its accumulators are lane group g's rows too;
+//   two heads per lane group (5 to 8 heads, and the chunked prefill's row sets): rows 2g, 2g+1
+//     hold hi, mid of head g and row 2g of a second tile its lo (row 2g+1 zero), two more MFMAs
+//     per page; p~ parts in rows 2g, 2g+1.
+// Q carries ~23 bits of q' (an error of at most max|q'| / 1.6e7 per channel), far below the
+// fp32 arithmetic after it.
+constexpr float kQFix = 8000000.0f;
+
+// Byte of channel ch in a head's limb block [a2][jg][16] (the A-tile byte order): channel
+// (4 jg + w) + 32 q2 + 16 a2 sits at byte 4w + q2 of operand a2, lane group jg.
+__device__ __forceinline__ int qlimb_byte(int ch) {
+  const int c16 = ch & 15, c_hi = ch >> 4;
+  return (c_hi & 1) * 64 + (c16 >> 2) * 16 + 4 * (c16 & 3) + (c_hi >> 1);
+}
+
+// Quantize one head's q' (element lane in v0, lane + 64 in v1) to the three limbs, written at
+// block[0][byte], block[plane][byte], block[2 plane][byte] (plane: bytes between limb planes).
+// Returns 256 delta, the weight of the mid limb; *qsum gets delta * sum(Q), the sum of the q'
+// actually used.
+__device__ __forceinline__ float q_limbs(float v0, float v1, uint8_t* block, int plane, int lane, float* qsum) {
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const float delta = amax > 0.0f ? amax / kQFix : 1.0f;
+  const int q0 = (int)rintf(v0 / delta), q1 = (int)rintf(v1 / delta);
+  *qsum = delta * (float)wave_sum_i(q0 + q1);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    // balanced base-256 digits from the bottom, each in [-128, 127] (the top one within +-122)
+    const int Q = e ? q1 : q0;
+    const int lo = ((Q + 128) & 255) - 128, Q1 = (Q - lo) >> 8;
+    const int mid = ((Q1 + 128) & 255) - 128, hi = (Q1 - mid) >> 8;
+    uint8_t* dst = block + qlimb_byte(lane + 64 * e);
+    dst[0] = (uint8_t)(hi & 255);
+    dst[plane] = (uint8_t)(mid & 255);
+    dst[2 * plane] = (uint8_t)(lo & 255);
+  }
+  return 256.0f * delta;
+}
+
+// One set of 8 rows (two heads per lane group: A-tile rows 2g+limb) against an unpacked INT4
+// page.  valid0 / valid1: tokens of the page that rows x0 / x1 attend (decode: the same count).
 __device__ __forceinline__ void rows_i4(const PageI4& u, int valid0, int valid1, WaveState& s,
-                                        const i32x4 (&qa)[2], float alpha0, float beta0, float alpha1,
+                                        const i32x4 (&qa)[4], float alpha0, float beta0, float alpha1,
                                         float beta1, bool has0, bool has1, int n, int jg, bool a_row_used,
                                         _Float16 (*ptile)[kPage]) {
   const bool tv0 = n < valid0, tv1 = n < valid1;
 
-  // q'.c_t on the integer matrix cores
+  // Q.c_t on the integer matrix cores, exactly: hi and mid limbs in sc, lo in sl.  alpha = 256
+  // delta sm_scale log2(e) weighs the mid limb (|256 hi.c + mid.c| < 2^26 is exact in int32).
+  // The hi and mid limbs give the score to 2^-15 of its largest term, and that sets the running
+  // maximum (any reference value gives the same softmax); the lo limb's share joins while the
+  // maximum is reduced, off its dependency chain.
   i32x4 sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], u.kb0, i32x4{0, 0, 0, 0}, 0, 0, 0);
   sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], u.kb1, sc, 0, 0, 0);
+  i32x4 sl = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[2], u.kb0, i32x4{0, 0, 0, 0}, 0, 0, 0);
+  sl = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[3], u.kb1, sl, 0, 0, 0);
+  const int lo0 = sl[0], lo1 = sl[2];
 
   float x0 = fmaf((float)(sc[0] * 256 + sc[1]) * alpha0, u.sk, u.zk * beta0);
   float x1 = fmaf((float)(sc[2] * 256 + sc[3]) * alpha1, u.sk, u.zk * beta1);
@@ -249,6 +300,8 @@ __device__ __forceinline__ void rows_i4(const PageI4& u, int valid0, int valid1,
   x1 = tv1 ? x1 : -INFINITY;
 
   const float pm0 = row_max16(x0), pm1 = row_max16(x1);
+  x0 = fmaf((float)lo0 * (alpha0 * (1.0f / 256.0f)), u.sk, x0);
+  x1 = fmaf((float)lo1 * (alpha1 * (1.0f / 256.0f)), u.sk, x1);
   const float sv = u.sv, zv = u.zv;
   // The reference max m only moves when a score exceeds it by more than 2^8 (or when p~ = p * sv
   // could leave the fp16 range): any m gives the same softmax, and p <= 2^8 keeps the fp16 and
@@ -306,14 +359,92 @@ __device__ __forceinline__ void rows_i4(const PageI4& u, int valid0, int valid1,
   }
 }
 
+// One head per lane group (at most 4 heads, layout above): head jg's scores, online softmax
+// (statistics in s.m0, s.l0, s.pz0) and p.V (accumulator rows 0, 1 of lane group jg).
+__device__ __forceinline__ void rows_i4_one(const PageI4& u, int valid, WaveState& s, const i32x4 (&qa)[2],
+                                            float alpha, float beta, bool has, int n, int jg, bool a_row_used,
+                                            _Float16 (*ptile)[kPage]) {
+  const bool tv = n < valid;
+  // hi, mid, lo limb sums in sc[0], sc[1], sc[2]; the lo share joins after the maximum (as above)
+  i32x4 sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], u.kb0, i32x4{0, 0, 0, 0}, 0, 0, 0);
+  sc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], u.kb1, sc, 0, 0, 0);
+  float x = fmaf((float)(sc[0] * 256 + sc[1]) * alpha, u.sk, u.zk * beta);
+  x = tv ? x : -INFINITY;
+  const float pm = row_max16(x);
+  x = fmaf((float)sc[2] * (alpha * (1.0f / 256.0f)), u.sk, x);
+  const float sv = u.sv, zv = u.zv;
+  // the reference maximum moves as in rows_i4
+  if (__any(pm > s.m0 + 8.0f || (pm > s.m0 && sv > 128.0f))) {
+    const float mn = fmaxf(s.m0, pm);
+    const float f = __builtin_amdgcn_exp2f(s.m0 - mn);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s.acc[i][0] *= f;
+      s.acc[i][1] *= f;
+    }
+    s.l0 *= f;
+    s.pz0 *= f;
+    s.m0 = mn;
+  }
+  const float p = __builtin_amdgcn_exp2f(x - s.m0);
+  s.l0 += p;
+  const float zc = fmaf(8.0f, sv, zv);
+  s.pz0 = fmaf(p, zc, s.pz0);
+  // p~ = p * sv as fp16 high + low parts at p-tile rows 4 jg, 4 jg + 1 (token order as in rows_i4)
+  const float pt = p * sv;
+  const _Float16 h = (_Float16)pt;
+  const _Float16 r = (_Float16)(pt - (float)h);
+  const int pos = (n & ~3) | ((n & 1) << 1) | ((n >> 1) & 1);
+  if (has) {
+    ptile[4 * jg + 0][pos] = h;
+    ptile[4 * jg + 1][pos] = r;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const f16x4 pa = a_row_used ? *(const f16x4*)&ptile[n][4 * jg] : f16x4{0, 0, 0, 0};
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, u.blo[q], s.acc[2 * q], 0, 0, 0);
+    s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, u.bhi[q], s.acc[2 * q + 1], 0, 0, 0);
+  }
+}
+
+// HPL heads per lane group: 1 (rows_i4_one: head jg, statistics and operands of slot 0) or 2
+// (rows_i4: heads 2jg, 2jg+1).
+template <int HPL>
 __device__ __forceinline__ void process_page(const PageData<0>& pg, int valid0, int valid1, WaveState& s,
-                                             const i32x4 (&qa)[2],
+                                             const i32x4 (&qa)[4],
                                              float alpha0, float beta0, float alpha1, float beta1,
                                              bool has0, bool has1, int n, int jg, bool a_row_used,
                                              _Float16 (*ptile)[kPage]) {
-  rows_i4(unpack_i4(pg, max(valid0, valid1), n), valid0, valid1, s, qa, alpha0, beta0, alpha1, beta1, has0, has1, n,
-          jg, a_row_used,
-          ptile);
+  if constexpr (HPL == 1) {
+    const i32x4 q2[2] = {qa[0], qa[1]};
+    rows_i4_one(unpack_i4(pg, valid0, n), valid0, s, q2, alpha0, beta0, has0, n, jg, a_row_used, ptile);
+  } else {
+    rows_i4(unpack_i4(pg, max(valid0, valid1), n), valid0, valid1, s, qa, alpha0, beta0, alpha1, beta1, has0, has1,
+            n, jg, a_row_used, ptile);
+  }
+}
+
+// The A operands of the INT4 q.K tiles for lane row n (layouts above); limbs(l, g, a2) is the
+// 16-byte operand a2 of limb l of head g for this lane's row group.
+template <int HPL, typename Limbs>
+__device__ __forceinline__ void q_tiles_i4(const Limbs& limbs, int G, int n, i32x4 (&qa)[4]) {
+  const i32x4 zero = i32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int a2 = 0; a2 < 2; ++a2) {
+    if constexpr (HPL == 1) {
+      const int g = n >> 2, limb = n & 3;
+      qa[a2] = (g < G && limb < 3) ? limbs(limb, g, a2) : zero;
+      qa[2 + a2] = zero;
+    } else {
+      const int g = n >> 1, limb = n & 1;
+      qa[a2] = g < G ? limbs(limb, g, a2) : zero;
+      qa[2 + a2] = (g < G && limb == 0) ? limbs(2, g, a2) : zero;
+    }
+  }
 }
 
 // MXFP4 page: K and V are dequantized to fp16 tiles with their UE8M0 group scales by the gfx950

@@ -42,15 +42,15 @@ using namespace attn;
 
 template <int W>
 struct DecodeSmem {
-  // INT4: q' limbs in the byte order of the q.K A tile: [limb][g][a2][jg][16 bytes]
-  uint8_t qlimb[2][kMaxG][2][4][16];
+  // INT4: q' limbs (hi, mid, lo) in the byte order of the q.K A tile: [limb][g][a2][jg][16 bytes]
+  uint8_t qlimb[3][kMaxG][2][4][16];
   // MXFP4: q' as fp16 high/low parts in the A-tile order of the f16 q.K MFMA: [part][g][kk][jg][8]
   _Float16 qh[2][kMaxG][4][4][8];
   // MXFP4 on the scaled matrix cores: q' limbs as the e4m3 A tiles [tile][row][K] and their
   // UE8M0 scales [tile][row][channel group] (row 2g+t: limb t+1; tile 1 row 2g: limb 3)
   uint8_t q8[2][16][kHeadDim];
   uint8_t q8s[2][16][4];
-  float qdelta[kMaxG];
+  float qdelta[kMaxG];  // INT4: weight of the mid limb, 256 delta
   float qsum[kMaxG];
   _Float16 ptile[W][2 * kMaxG][kPage];  // p~ split into fp16 high/low parts, A-tile rows 2g+limb
   float wo[W][kMaxG][kHeadDim];
@@ -245,8 +245,9 @@ __device__ __forceinline__ void merge_runs(const DecodeParams& a, int64_t s0, in
 }  // namespace
 
 
-// FMT: 0 INT4; 1 MXFP4 (f16 tiles); 2 MXFP4 with q.K on the scaled FP8 x FP4 matrix cores
-template <int FMT, int W, int D>
+// FMT: 0 INT4; 1 MXFP4 (f16 tiles); 2 MXFP4 with q.K on the scaled FP8 x FP4 matrix cores.
+// HPL: heads per lane group of the INT4 page step (1: at most 4 heads, 2: more; MXFP4: 2).
+template <int FMT, int W, int D, int HPL>
 __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   constexpr int PF = FMT == 0 ? 0 : 1;  // page format
   __shared__ DecodeSmem<W> sm;
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   }
   const int G = a.group;
   const int n = lane & 15;   // token (QK, softmax) / output column (p.V)
-  const int jg = lane >> 4;  // row group: heads 2jg, 2jg+1
+  const int jg = lane >> 4;  // row group: head jg (HPL 1) or heads 2jg, 2jg+1
 
   // ---- 0. loads that depend on nothing: the query words, then this wave's block-table entries
   //         (the page loads wait for those, and with them for the query words issued just
@@ -374,8 +375,8 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
 #pragma unroll
   for (int d = 0; d < D; ++d) st[d] = load_page<PF>(page_base(d), d < npw, koff, voff, poff, qoff);
 
-  // ---- 2. q' = R_b (q_scale q) in registers, then 16-bit fixed point q' ~= delta_g * Q with
-  //         |Q| <= 32000, stored as two int8 limbs (Q = 256*hi + lo) in the A-tile byte order ----
+  // ---- 2. q' = R_b (q_scale q) in registers, then 24-bit fixed point q' ~= delta_g * Q,
+  //         stored as three int8 limbs in the A-tile byte order ----
 #pragma unroll
   for (int k = 0; k < kMaxHeadsPerWave; ++k) {
     const int g = wave + k * W;
@@ -399,23 +400,11 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
         }
         continue;
       }
-      const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-      const float delta = amax > 0.0f ? amax / 32000.0f : 1.0f;
-      const int q0 = (int)rintf(v0 / delta), q1 = (int)rintf(v1 / delta);
-      const int qs = wave_sum_i(q0 + q1);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int ch = lane + 64 * e, Q = e ? q1 : q0;
-        const int hi = (Q + 128) >> 8, lo = Q - 256 * hi;
-        // channel (4jg + w) + 32q2 + 16a2 sits at byte 4w + q2 of operand a2, lane group jg
-        const int c16 = ch & 15, c_hi = ch >> 4;
-        uint8_t* dst = &sm.qlimb[0][g][c_hi & 1][c16 >> 2][4 * (c16 & 3) + (c_hi >> 1)];
-        dst[0] = (uint8_t)(hi & 255);
-        dst[sizeof(sm.qlimb[0])] = (uint8_t)(lo & 255);
-      }
+      float qs;
+      const float w_mid = q_limbs(v0, v1, &sm.qlimb[0][g][0][0][0], (int)sizeof(sm.qlimb[0]), lane, &qs);
       if (lane == 0) {
-        sm.qdelta[g] = delta;
-        sm.qsum[g] = delta * (float)qs;  // sum of the q' actually used
+        sm.qdelta[g] = w_mid;
+        sm.qsum[g] = qs;  // sum of the q' actually used
       }
     }
   }
@@ -479,24 +468,25 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   if (lane == 0) sm.prog[wave] = 0;
   __syncthreads();
 
-  const int ga = n >> 1;   // A-tile row 2g+limb -> head of this lane's A row
+  const int ga = n >> 1;   // A-tile row 2g+limb -> head of this lane's A row (HPL 2)
   const int limb = n & 1;  // 0: high limb / high fp16 part, 1: low
-  const bool a_row_used = ga < G;
-  const bool has0 = 2 * jg < G, has1 = 2 * jg + 1 < G;
+  // p.V A-tile rows in use (p~ parts of an existing head), and the heads of this lane's score
+  // and accumulator rows: h0 (and h0 + 1 with two heads per lane group)
+  const bool a_row_used = HPL == 1 ? ((n & 3) < 2 && (n >> 2) < G) : ga < G;
+  const int h0 = HPL == 1 ? jg : 2 * jg;
+  const bool has0 = h0 < G, has1 = HPL == 2 && h0 + 1 < G;
   const float c2 = a.sm_scale_log2;
-  i32x4 qa[2];
+  i32x4 qa[4];
   f16x8 qh[4];
   i32x8 qa8[2];
   int qsa[2];
   float alpha0 = 0.f, beta0 = 0.f, alpha1 = 0.f, beta1 = 0.f;
   if constexpr (FMT == 0) {
-#pragma unroll
-    for (int a2 = 0; a2 < 2; ++a2)
-      qa[a2] = a_row_used ? *(const i32x4*)&sm.qlimb[limb][ga][a2][jg][0] : i32x4{0, 0, 0, 0};
-    alpha0 = has0 ? sm.qdelta[2 * jg] * c2 : 0.0f;
-    beta0 = has0 ? sm.qsum[2 * jg] * c2 : 0.0f;
-    alpha1 = has1 ? sm.qdelta[2 * jg + 1] * c2 : 0.0f;
-    beta1 = has1 ? sm.qsum[2 * jg + 1] * c2 : 0.0f;
+    q_tiles_i4<HPL>([&](int l, int g, int a2) { return *(const i32x4*)&sm.qlimb[l][g][a2][jg][0]; }, G, n, qa);
+    alpha0 = has0 ? sm.qdelta[h0] * c2 : 0.0f;
+    beta0 = has0 ? sm.qsum[h0] * c2 : 0.0f;
+    alpha1 = has1 ? sm.qdelta[h0 + 1] * c2 : 0.0f;
+    beta1 = has1 ? sm.qsum[h0 + 1] * c2 : 0.0f;
   } else if constexpr (FMT == 1) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -543,7 +533,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       if (i < npw) {
         if (app_wg && pw0 + W * i == last_pg) patch_appended<PF>(st[d], sm.arow, sm.aparam, app_slot, n, jg);
         if constexpr (FMT == 0)
-          process_page(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, s, qa, alpha0, beta0, alpha1, beta1,
+          process_page<HPL>(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, s, qa, alpha0, beta0, alpha1, beta1,
                        has0, has1, n, jg, a_row_used, sm.ptile[wave]);
         else if constexpr (FMT == 1)
           process_page_mx(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, valid0 - i * W * kPage, s, qh, c2,
@@ -566,13 +556,13 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       const f32x4 v = s.acc[2 * q + e];
       // INT4: undo the subnormal encoding (2^24, or 2^24/16 for the high nibbles); MXFP4: none
       const float sc = FMT != 0 ? 1.0f : (e ? 1048576.0f : 16777216.0f);
-      if (has0) sm.wo[wave][2 * jg][ch] = sc * (v[0] + v[1]) + pz0;
-      if (has1) sm.wo[wave][2 * jg + 1][ch] = sc * (v[2] + v[3]) + pz1;
+      if (has0) sm.wo[wave][h0][ch] = sc * (v[0] + v[1]) + pz0;
+      if (has1) sm.wo[wave][h0 + 1][ch] = sc * (v[2] + v[3]) + pz1;
     }
   }
   if (n == 0) {
-    if (has0) { sm.wm[wave][2 * jg] = s.m0; sm.wl[wave][2 * jg] = l0; }
-    if (has1) { sm.wm[wave][2 * jg + 1] = s.m1; sm.wl[wave][2 * jg + 1] = l1; }
+    if (has0) { sm.wm[wave][h0] = s.m0; sm.wl[wave][h0] = l0; }
+    if (has1) { sm.wm[wave][h0 + 1] = s.m1; sm.wl[wave][h0 + 1] = l1; }
   }
   __syncthreads();
 
@@ -723,19 +713,24 @@ hipError_t launch_decode(const DecodeParams& p, int variant, hipStream_t stream)
   const int fmt = variant;
   const int64_t units = (int64_t)p.num_seqs * p.hkv;
   const dim3 grid((unsigned)(units * p.plan.nsplit));
-#define KVQ_DECODE_CASE(F, WV, DV)                                                               \
-  if (fmt == F && p.plan.waves == WV && p.plan.depth == DV) {                                  \
-    hipLaunchKernelGGL((decode_kernel<F, WV, DV>), grid, dim3(WV * 64), 0, stream, p);          \
+  // INT4 with at most 4 query heads per kv head: one head per lane group
+  const int hpl = (fmt == 0 && p.group <= 4) ? 1 : 2;
+#define KVQ_DECODE_CASE(F, WV, DV, H)                                                            \
+  if (fmt == F && p.plan.waves == WV && p.plan.depth == DV && hpl == H) {                      \
+    hipLaunchKernelGGL((decode_kernel<F, WV, DV, H>), grid, dim3(WV * 64), 0, stream, p);       \
   } else
-  KVQ_DECODE_CASE(0, 4, 2) KVQ_DECODE_CASE(0, 4, 3) KVQ_DECODE_CASE(0, 4, 4)
-  KVQ_DECODE_CASE(0, 8, 2) KVQ_DECODE_CASE(0, 8, 3) KVQ_DECODE_CASE(0, 8, 4)
-  KVQ_DECODE_CASE(0, 16, 2)
-  KVQ_DECODE_CASE(1, 4, 2) KVQ_DECODE_CASE(1, 4, 3) KVQ_DECODE_CASE(1, 4, 4)
-  KVQ_DECODE_CASE(1, 8, 2) KVQ_DECODE_CASE(1, 8, 3) KVQ_DECODE_CASE(1, 8, 4)
-  KVQ_DECODE_CASE(1, 16, 2)
-  KVQ_DECODE_CASE(2, 4, 2) KVQ_DECODE_CASE(2, 4, 3) KVQ_DECODE_CASE(2, 4, 4)
-  KVQ_DECODE_CASE(2, 8, 2) KVQ_DECODE_CASE(2, 8, 3) KVQ_DECODE_CASE(2, 8, 4)
-  KVQ_DECODE_CASE(2, 16, 2) { return hipErrorInvalidValue; }
+  KVQ_DECODE_CASE(0, 4, 2, 1) KVQ_DECODE_CASE(0, 4, 3, 1) KVQ_DECODE_CASE(0, 4, 4, 1)
+  KVQ_DECODE_CASE(0, 8, 2, 1) KVQ_DECODE_CASE(0, 8, 3, 1) KVQ_DECODE_CASE(0, 8, 4, 1)
+  KVQ_DECODE_CASE(0, 16, 2, 1)
+  KVQ_DECODE_CASE(0, 4, 2, 2) KVQ_DECODE_CASE(0, 4, 3, 2) KVQ_DECODE_CASE(0, 4, 4, 2)
+  KVQ_DECODE_CASE(0, 8, 2, 2) KVQ_DECODE_CASE(0, 8, 3, 2) KVQ_DECODE_CASE(0, 8, 4, 2)
+  KVQ_DECODE_CASE(0, 16, 2, 2)
+  KVQ_DECODE_CASE(1, 4, 2, 2) KVQ_DECODE_CASE(1, 4, 3, 2) KVQ_DECODE_CASE(1, 4, 4, 2)
+  KVQ_DECODE_CASE(1, 8, 2, 2) KVQ_DECODE_CASE(1, 8, 3, 2) KVQ_DECODE_CASE(1, 8, 4, 2)
+  KVQ_DECODE_CASE(1, 16, 2, 2)
+  KVQ_DECODE_CASE(2, 4, 2, 2) KVQ_DECODE_CASE(2, 4, 3, 2) KVQ_DECODE_CASE(2, 4, 4, 2)
+  KVQ_DECODE_CASE(2, 8, 2, 2) KVQ_DECODE_CASE(2, 8, 3, 2) KVQ_DECODE_CASE(2, 8, 4, 2)
+  KVQ_DECODE_CASE(2, 16, 2, 2) { return hipErrorInvalidValue; }
 #undef KVQ_DECODE_CASE
   return hipGetLastError();
 }

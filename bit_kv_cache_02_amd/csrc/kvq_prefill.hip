@@ -36,7 +36,7 @@ struct PrefillWaveSmem {
   union {
     struct {
       union {
-        uint8_t qlimb[2][kSetRows * RS][2][4][16];  // INT4: q' limbs, as in decode
+        uint8_t qlimb[3][kSetRows * RS][2][4][16];  // INT4: q' limbs, as in decode
         _Float16 qh[2][kSetRows * RS][4][4][8];     // MXFP4: q' fp16 high/low parts
       };
       float qdelta[kSetRows * RS];
@@ -132,22 +132,11 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
           ws.q.qh[1][r][ch & 3][(ch >> 2) & 3][ch >> 4] = lo;
         }
       } else {
-        const float amax = wave_max(fmaxf(fabsf(v0[r]), fabsf(v1[r])));
-        const float delta = amax > 0.0f ? amax / 32000.0f : 1.0f;
-        const int q0 = (int)rintf(v0[r] / delta), q1 = (int)rintf(v1[r] / delta);
-        const int qs = wave_sum_i(q0 + q1);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int ch = lane + 64 * e, Q = e ? q1 : q0;
-          const int hi = (Q + 128) >> 8, lo = Q - 256 * hi;
-          const int c16 = ch & 15, c_hi = ch >> 4;
-          uint8_t* dst = &ws.q.qlimb[0][r][c_hi & 1][c16 >> 2][4 * (c16 & 3) + (c_hi >> 1)];
-          dst[0] = (uint8_t)(hi & 255);
-          dst[sizeof(ws.q.qlimb[0])] = (uint8_t)(lo & 255);
-        }
+        float qs;
+        const float w_mid = q_limbs(v0[r], v1[r], &ws.q.qlimb[0][r][0][0][0], (int)sizeof(ws.q.qlimb[0]), lane, &qs);
         if (lane == 0) {
-          ws.q.qdelta[r] = delta;
-          ws.q.qsum[r] = delta * (float)qs;
+          ws.q.qdelta[r] = w_mid;
+          ws.q.qsum[r] = qs;
         }
       }
     }
@@ -157,7 +146,7 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
   // Row set k holds rows 8k .. 8k+7; A-tile row 2g+limb of set k is row 8k + g.
   const int ga = n >> 1, limb = n & 1;
   const float c2 = a.sm_scale_log2;
-  i32x4 qa[RS][2];
+  i32x4 qa[RS][4];
   f16x8 qh[RS][4];
   float alpha0[RS], beta0[RS], alpha1[RS], beta1[RS];
   bool a_row_used[RS], has0[RS], has1[RS];
@@ -173,9 +162,11 @@ __global__ __launch_bounds__(W * 64) void prefill_kernel(PrefillParams a) {
     lim1[k] = pos0 + t_row1 + 1;
     alpha0[k] = beta0[k] = alpha1[k] = beta1[k] = 0.0f;
     if constexpr (FMT == 0) {
-#pragma unroll
-      for (int a2 = 0; a2 < 2; ++a2)
-        qa[k][a2] = a_row_used[k] ? *(const i32x4*)&ws.q.qlimb[limb][rbase + ga][a2][jg][0] : i32x4{0, 0, 0, 0};
+      // a set's 8 rows fill the tile's 8 row pairs, so the lo limbs take the second tile (only
+      // row pair ga is read)
+      q_tiles_i4<2>([&](int l, int g, int a2) {
+        return a_row_used[k] ? *(const i32x4*)&ws.q.qlimb[l][rbase + g][a2][jg][0] : i32x4{0, 0, 0, 0};
+      }, kSetRows, n, qa[k]);
       alpha0[k] = has0[k] ? ws.q.qdelta[rbase + 2 * jg] * c2 : 0.0f;
       beta0[k] = has0[k] ? ws.q.qsum[rbase + 2 * jg] * c2 : 0.0f;
       alpha1[k] = has1[k] ? ws.q.qdelta[rbase + 2 * jg + 1] * c2 : 0.0f;

@@ -47,7 +47,7 @@ def oracle_cache(rng, lens, hkv, hb, fmt=oracle.FMT_INT4, permute=True, dist="ll
 
 def run_decode(label, pool, table, lens, hq, hb, fmt=oracle.FMT_INT4, q=None, q_dtype="bf16",
                q_scale=1.0, sm_scale=None, out_dtype=torch.float32, rotated=False, seed=0,
-               check=True, scaled_mfma=False):
+               check=True, scaled_mfma=False, tol=parity.ATTN_TOL):
     print(f"[decode] {label}", flush=True)
     rng = np.random.default_rng(seed)
     b = len(lens)
@@ -73,7 +73,7 @@ def run_decode(label, pool, table, lens, hq, hb, fmt=oracle.FMT_INT4, q=None, q_
     err = parity.attn_row_error(got, ref)
     print(f"[decode] {label}: max row err {err.max():.3e}, p99.9 {np.quantile(err, 0.999):.3e}",
           flush=True)
-    assert err.max() <= parity.ATTN_TOL, f"{label}: row error {err.max():.3e}"
+    assert err.max() <= tol, f"{label}: row error {err.max():.3e}"
     return got
 
 
@@ -131,8 +131,38 @@ def test_decode_outlier_scores_and_sharp_softmax():
     rng = np.random.default_rng(24)
     lens = [513, 64]
     pool, table = oracle_cache(rng, lens, 1, 128)
-    run_decode("sharp", pool, table, lens, 4, 128, sm_scale=2.0)
+    run_decode("sharp", pool, table, lens, 4, 128, sm_scale=2.0, tol=2e-4)
     run_decode("flat", pool, table, lens, 4, 128, sm_scale=1e-3)
+
+
+@pytest.mark.parametrize("hb", [1, 128])
+def test_decode_sharper_softmax_with_stronger_outliers(hb):
+    # sm_scale 4 and x30 outlier channels in K: scores spread over hundreds, so the softmax is
+    # nearly one-hot and any error of the score path shows nearly undamped in the output (a
+    # 16-bit fixed-point q' would miss the 2e-3 rule here).  The INT4 score path (24-bit
+    # fixed-point q' on the integer matrix cores) keeps the row error ten times inside it.
+    rng = np.random.default_rng(28 + hb)
+    lens = [700, 33, 2049]
+    hkv = 2
+    n_pages = [-(-n // 16) for n in lens]
+    total = sum(n_pages) + 1
+    table = np.zeros((3, max(n_pages)), np.int32)
+    ids = rng.permutation(total)
+    off = 0
+    for b, n in enumerate(n_pages):
+        table[b, :n] = ids[off:off + n]
+        off += n
+    t = sum(lens)
+    k = rng.standard_normal((t, hkv, 128)).astype(np.float32)
+    k[:, :, [7, 40, 93]] *= 30
+    v = (rng.standard_normal((t, hkv, 128)) * 0.5).astype(np.float32)
+    k = torch.from_numpy(k).bfloat16().float().numpy()
+    v = torch.from_numpy(v).bfloat16().float().numpy()
+    pool = np.full((total, hkv, 2176), 0x5A, np.uint8)
+    oracle.append(pool, k, v, np.concatenate([[0], np.cumsum(lens)]), np.zeros(3, np.int64), table, hb)
+    q = rng.standard_normal((3, 8, 128)).astype(np.float32)
+    run_decode(f"sharper/b{hb}", pool, table, lens, 8, hb, q=q, sm_scale=4.0, tol=2e-4)
+    run_decode(f"sharp/b{hb}", pool, table, lens, 8, hb, q=q, sm_scale=2.0, tol=2e-4)
 
 
 def test_decode_page_permutation_invariance_and_determinism():
