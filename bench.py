@@ -436,6 +436,22 @@ def hbm_copy_probe(dev, nbytes=1 << 30, repeats=10):
     return 2 * nbytes / us / 1e3
 
 
+def hbm_fold4_probe(dev, out_bytes=1 << 28, repeats=10):
+    """The 4:1 read:write probe (kvq_hbm_fold4): 1 GiB read and 256 MiB written per launch;
+    GB/s of bytes moved (read + written)."""
+    src = torch.empty(4 * out_bytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(out_bytes, dtype=torch.uint8, device=dev)
+    settle(lambda: kvq.hbm_fold4(src, dst))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(repeats):
+        kvq.hbm_fold4(src, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / repeats
+    return 5 * out_bytes / us / 1e3
+
+
 def time_dequant(cache, dev, n_pages=1024, repeats=20):
     """kvq_dequant_page over n_pages seeded pages of a llama layer cache (all 8 kv heads), plain
     and rotated back: each page-head reads its 2176-byte block and writes K and V as fp32 16 x 128
@@ -734,6 +750,8 @@ def main():
     # the same probe at one step's byte count per launch (its launch and drain included)
     res["hbm_read_GBps_at_step_bytes"] = round(hbm_read_probe(dev, window=step_bytes, repeats=56), 1)
     res["step_frac_of_read_bw_at_step_bytes"] = round(achieved / res["hbm_read_GBps_at_step_bytes"], 4)
+    log("[bench] HBM 4:1 read:write probe")
+    res["hbm_fold4_GBps"] = round(hbm_fold4_probe(dev), 1)
     log("[bench] page dequantization")
     res["dequant_pages"] = time_dequant(caches[0], dev, repeats=5 if args.profile_run else 20)
     del caches
@@ -741,6 +759,7 @@ def main():
     if not args.no_prefill:
         log("[bench] prefill append")
         res["prefill_append"] = time_prefill_append(dev, repeats=3 if args.profile_run else 10)
+        res["prefill_append"]["frac_of_fold4_bw"] = round(res["prefill_append"]["GBps"] / res["hbm_fold4_GBps"], 4)
         res["prefill_append"]["traffic"] = traffic_entry(res["prefill_append"]["algorithmic_bytes"],
                                                          APPEND_TRAFFIC_FILE, APPEND_SRC, "append_source_sha256")
         torch.cuda.empty_cache()

@@ -511,6 +511,9 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
     // yields the issue slots, so the pair keep pace page group by page group.  Otherwise a
     // wave's priority falls as it progresses, so the waves that are behind get the issue slots.
     if constexpr (W == 8) {
+      // The volatile accesses go through a generic pointer, i.e. flat instructions, whose wait
+      // also drains this wave's page loads in flight once per group of pages.  Measured: LDS
+      // atomics in their place (ds_write / ds_read, no drain) made the llama step ~2% slower.
       if (lane == 0) *(volatile int*)&sm.prog[wave] = i0;
       const int mate = __builtin_amdgcn_readfirstlane(*(volatile const int*)&sm.prog[wave ^ 4]);
       if (i0 > mate) __builtin_amdgcn_s_setprio(0);

@@ -132,6 +132,32 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
   if (thread_id() == 0) sink[block_id_x()] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+__global__ __launch_bounds__(256) void fold4_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                   int64_t n_groups, int64_t per_block) {
+  // a 4:1 read:write stream in groups of 256 output vectors: output vector 256 m + t is the XOR
+  // of input vectors 1024 m + t + 256 k (k = 0..3), so every load and store instruction of a
+  // wave covers 1 KiB of consecutive bytes; each workgroup walks one contiguous chunk of groups,
+  // two groups (32 KiB read, 8 KiB written) per step.  Nontemporal loads (streamed once),
+  // default-policy stores.
+  const int64_t g0 = (int64_t)block_id_x() * per_block;
+  const int64_t g1 = g0 + per_block < n_groups ? g0 + per_block : n_groups;
+  const int t = thread_id();
+  int64_t g = g0;
+  for (; g + 1 < g1; g += 2) {
+    u32x4 a[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = __builtin_nontemporal_load(&src[1024 * (g + (k >> 2)) + t + 256 * (k & 3)]);
+    dst[256 * g + t] = a[0] ^ a[1] ^ a[2] ^ a[3];
+    dst[256 * (g + 1) + t] = a[4] ^ a[5] ^ a[6] ^ a[7];
+  }
+  if (g < g1) {
+    u32x4 a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = __builtin_nontemporal_load(&src[1024 * g + t + 256 * k]);
+    dst[256 * g + t] = a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+}
+
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
   if (p.unrotate)
     hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);
@@ -161,6 +187,17 @@ hipError_t launch_read(const void* src, size_t bytes, uint32_t* sink, hipStream_
   const int64_t per_block = (n16 + blocks - 1) / blocks;
   hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)src, n16, per_block,
                      sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold4(const void* src, void* dst, size_t dst_bytes, hipStream_t stream) {
+  // groups of 256 output vectors (4 KiB); 2048 workgroups (8 per CU), each a contiguous chunk
+  const int64_t groups = (int64_t)(dst_bytes / 4096);
+  int64_t blocks = groups < 2048 ? groups : 2048;
+  if (blocks < 1) blocks = 1;
+  const int64_t per_block = (groups + blocks - 1) / blocks;
+  hipLaunchKernelGGL(fold4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)src, (u32x4*)dst,
+                     groups, per_block);
   return hipGetLastError();
 }
 

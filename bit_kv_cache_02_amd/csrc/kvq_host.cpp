@@ -179,6 +179,8 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t kv_
   if (max_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "max_pages must be >= 1");
   if (max_pages > (1 << 24)) return fail(KVQ_ERR_UNSUPPORTED, "max_pages %d above 2^24", max_pages);
   if (max_new_tokens < 0) return fail(KVQ_ERR_INVALID_ARG, "max_new_tokens must be >= 0");
+  // the grid's second dimension counts groups of 4 pages per sequence (at most 65535)
+  if (max_new_tokens > 4000000) return fail(KVQ_ERR_UNSUPPORTED, "max_new_tokens %d above 4000000", max_new_tokens);
   if ((((uintptr_t)k) | ((uintptr_t)v)) & 15) return fail(KVQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
   if (num_seqs > 65535) return fail(KVQ_ERR_UNSUPPORTED, "num_seqs %d above 65535", num_seqs);
   if (num_tokens == 0 || num_seqs == 0 || max_new_tokens == 0) return KVQ_OK;
@@ -480,6 +482,15 @@ int kvq_hbm_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
   if (((uintptr_t)src & 15) || ((uintptr_t)sink & 3)) return fail(KVQ_ERR_INVALID_ARG, "src must be 16-byte and sink 4-byte aligned");
   if (bytes == 0) return KVQ_OK;
   return hip_status(kvq::launch_read(src, bytes, sink, (hipStream_t)stream), "kvq_hbm_read launch");
+}
+
+int kvq_hbm_fold4(const void* src, void* dst, size_t dst_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!src || !dst) return fail(KVQ_ERR_INVALID_ARG, "src and dst must not be NULL");
+  if (dst_bytes % 4096) return fail(KVQ_ERR_INVALID_ARG, "dst_bytes must be a multiple of 4096");
+  if ((((uintptr_t)src) | ((uintptr_t)dst)) & 15) return fail(KVQ_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  if (dst_bytes == 0) return KVQ_OK;
+  return hip_status(kvq::launch_fold4(src, dst, dst_bytes, (hipStream_t)stream), "kvq_hbm_fold4 launch");
 }
 
 }  // extern "C"

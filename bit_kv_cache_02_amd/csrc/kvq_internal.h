@@ -143,5 +143,6 @@ int prefill_tokens_per_tile(int group);
 hipError_t launch_prefill(const PrefillParams& p, int fmt, hipStream_t stream);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_fold4(const void* src, void* dst, size_t dst_bytes, hipStream_t stream);
 
 }  // namespace kvq

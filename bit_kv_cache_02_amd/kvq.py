@@ -72,6 +72,7 @@ SIGNATURES = [
     ("kvq_last_error", ctypes.c_char_p, []),
     ("kvq_hbm_copy", ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
     ("kvq_hbm_read", ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
+    ("kvq_hbm_fold4", ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
 ]
 
 
@@ -341,3 +342,14 @@ def hbm_read(src: torch.Tensor, sink: torch.Tensor):
         raise ValueError("hbm_read: sink must be a contiguous buffer of 4096 32-bit words")
     st = lib().kvq_hbm_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream())
     _check(st, "kvq_hbm_read")
+
+
+def hbm_fold4(src: torch.Tensor, dst: torch.Tensor):
+    """The 4:1 read:write probe over 16-byte vectors: dst vector 256m + t = XOR of src vectors
+    1024m + t + 256k, k = 0..3 (dst: a multiple of 4096 bytes)."""
+    _require(src, "src")
+    _require(dst, "dst")
+    nbytes = dst.numel() * dst.element_size()
+    if src.numel() * src.element_size() != 4 * nbytes:
+        raise ValueError("src must hold exactly 4 times the bytes of dst")
+    _check(lib().kvq_hbm_fold4(_ptr(src), _ptr(dst), nbytes, _stream()), "kvq_hbm_fold4")

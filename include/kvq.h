@@ -307,6 +307,16 @@ int kvq_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
  */
 int kvq_hbm_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * kvq_hbm_fold4 -- a 4:1 read:write streaming kernel over 16-byte vectors in groups of 256
+ * output vectors: dst vector 256 m + t = XOR of src vectors 1024 m + t + 256 k, k = 0..3.  Not
+ * part of the method: it measures the HBM bandwidth of a contiguous stream with the append's
+ * read:write mix (about 3.8:1 for bf16 in, 4-bit out), its ceiling.
+ * src: device, 4 * dst_bytes bytes; dst: device, dst_bytes bytes (a multiple of 4096); both
+ * 16-byte aligned, not overlapping.  dst_bytes == 0 writes nothing and returns KVQ_OK.
+ */
+int kvq_hbm_fold4(const void* src, void* dst, size_t dst_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -112,6 +112,7 @@ def test_mxfp4_needs_full_rotation():
     (dict(mp=0), kvq.KVQ_ERR_INVALID_ARG),
     (dict(mx=-2), kvq.KVQ_ERR_INVALID_ARG),
     (dict(k=ctypes.c_void_p(4100)), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(mx=4000001), kvq.KVQ_ERR_UNSUPPORTED),
 ])
 def test_append_rejects_bad_args(kw, status):
     assert _append(_desc(), **kw) == status
@@ -241,6 +242,10 @@ def test_dequant_and_copy_reject_bad_args():
     assert lib.kvq_hbm_read(FAKE, 16, None, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_hbm_read(ctypes.c_void_p(4096 + 8), 16, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_hbm_read(FAKE, 0, FAKE, None) == kvq.KVQ_OK
+    assert lib.kvq_hbm_fold4(FAKE, FAKE, 4096 + 16, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_hbm_fold4(None, FAKE, 4096, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_hbm_fold4(ctypes.c_void_p(4096 + 8), FAKE, 4096, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_hbm_fold4(FAKE, FAKE, 0, None) == kvq.KVQ_OK
 
 
 def test_python_layer_raises_typed_errors():
