@@ -179,8 +179,6 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t kv_
   if (max_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "max_pages must be >= 1");
   if (max_pages > (1 << 24)) return fail(KVQ_ERR_UNSUPPORTED, "max_pages %d above 2^24", max_pages);
   if (max_new_tokens < 0) return fail(KVQ_ERR_INVALID_ARG, "max_new_tokens must be >= 0");
-  // the grid's second dimension counts groups of 4 pages per sequence (at most 65535)
-  if (max_new_tokens > 4000000) return fail(KVQ_ERR_UNSUPPORTED, "max_new_tokens %d above 4000000", max_new_tokens);
   if ((((uintptr_t)k) | ((uintptr_t)v)) & 15) return fail(KVQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
   if (num_seqs > 65535) return fail(KVQ_ERR_UNSUPPORTED, "num_seqs %d above 65535", num_seqs);
   if (num_tokens == 0 || num_seqs == 0 || max_new_tokens == 0) return KVQ_OK;
