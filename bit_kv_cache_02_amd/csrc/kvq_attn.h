@@ -203,12 +203,16 @@ struct PageI4 {
 __device__ __forceinline__ PageI4 unpack_i4(const PageData<0>& pg, int vlimit, int n) {
   const uint32_t M4 = 0x0F0F0F0Fu, M16 = 0x000F000Fu;
   PageI4 u;
-  const uint32_t vp = n < vlimit ? pg.vp : 0u;
+  // parameters of slots past the attended count are zeroed: those slots hold whatever the pool
+  // held (fp16 inf / NaN possible), and a masked score must stay -inf after the lo limb's share
+  // s_k * lo joins it
+  const bool live = n < vlimit;
+  const uint32_t vp = live ? pg.vp : 0u, kp = live ? pg.kp : 0u;
   u.kb0 = i32x4{(int)(pg.k[0] & M4), (int)(pg.k[1] & M4), (int)(pg.k[2] & M4), (int)(pg.k[3] & M4)};
   u.kb1 = i32x4{(int)((pg.k[0] >> 4) & M4), (int)((pg.k[1] >> 4) & M4), (int)((pg.k[2] >> 4) & M4),
                 (int)((pg.k[3] >> 4) & M4)};
-  u.sk = f16_bits_to_f32(pg.kp & 0xFFFFu);
-  u.zk = f16_bits_to_f32(pg.kp >> 16);
+  u.sk = f16_bits_to_f32(kp & 0xFFFFu);
+  u.zk = f16_bits_to_f32(kp >> 16);
   u.sv = f16_bits_to_f32(vp & 0xFFFFu);
   u.zv = f16_bits_to_f32(vp >> 16);
   // V codes as fp16 subnormals: word q of the lane holds row byte 4n+q of 4 tokens.  Low nibbles

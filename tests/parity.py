@@ -121,11 +121,13 @@ def check_mxfp4_entries(codes_gpu, ebytes_gpu, info, label=""):
 def check_append(gpu_pool, oracle_pool, infos, cu_new, start_pos, block_table, fmt, sentinel, label="",
                  prior_mask=None):
     """All append rules; returns the number of tolerated deviations.  ``prior_mask`` marks
-    bytes written by earlier appends into the same pool (excluded from the sentinel check)."""
+    bytes written by earlier appends into the same pool (excluded from the sentinel check).
+    ``sentinel``: the byte every untouched position holds, or the whole pool as it was before
+    the append (a pool of random bytes)."""
     mask = touched_mask(gpu_pool.shape, cu_new, start_pos, block_table)
     if prior_mask is not None:
         mask = mask | prior_mask
-    untouched_ok = gpu_pool[~mask] == sentinel
+    untouched_ok = gpu_pool[~mask] == (sentinel[~mask] if isinstance(sentinel, np.ndarray) else sentinel)
     assert untouched_ok.all(), f"{label}: {(~untouched_ok).sum()} bytes outside appended slots changed"
     flips = 0
     for which in ("k", "v"):

@@ -82,11 +82,22 @@ def test_unwritten_slots_do_not_leak(fmt, fill):
     rng = np.random.default_rng(204)
     lens = [40, 17, 300, 1]
     pool, table = oracle_cache(rng, lens, 2, 128, fmt=fmt, fill=fill)
-    for scaled in ((False, True) if fmt == oracle.FMT_MXFP4 else (False,)):
-        run_decode(f"limits/garbage fmt{fmt} {fill} scaled={scaled}", pool, table, lens, 8, 128, fmt=fmt, seed=6,
-                   scaled_mfma=scaled)
+    # 8 and 16 query heads over 2 kv heads: group 4 and 8 (the two INT4 score layouts)
+    for hq in (8, 16):
+        for scaled in ((False, True) if fmt == oracle.FMT_MXFP4 else (False,)):
+            run_decode(f"limits/garbage fmt{fmt} {fill} hq{hq} scaled={scaled}", pool, table, lens, hq, 128,
+                       fmt=fmt, seed=6, scaled_mfma=scaled)
     run_prefill(f"limits/garbage prefill fmt{fmt} {fill}", [40, 17, 300], [9, 17, 40], hkv=2, group=4, hb=128,
                 fmt=fmt, seed=7, fill=fill)
+
+
+@pytest.mark.parametrize("group", [4, 8])
+def test_step_int4_with_random_bytes_in_the_last_page(group):
+    # random fp16 parameters (inf and NaN among them) in the slots past each sequence's end, on
+    # both INT4 score layouts (one head per lane group for 4 heads, two for 8)
+    from tests.test_gpu_step import run_step
+    run_step(f"limits/random step int4 G{group}", [1, 17, 300, 2000], hkv=2, group=group, hb=128, seed=9 + group,
+             fill="random")
 
 
 @pytest.mark.parametrize("scaled", [False, True])

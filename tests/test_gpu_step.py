@@ -55,7 +55,10 @@ def run_step(label, lens, hkv, group, hb, fmt="int4", kv_dtype="bf16", q_dtype="
         k_all.append(k)
         v_all.append(v)
     # cache before the step: tokens 0 .. L-2
-    pool0 = np.full((total, hkv, 2176), fill, np.uint8)
+    if isinstance(fill, str):  # "random": every byte outside the appended slots random
+        pool0 = rng.integers(0, 256, (total, hkv, 2176), dtype=np.uint8)
+    else:
+        pool0 = np.full((total, hkv, 2176), fill, np.uint8)
     pre = lens - 1
     cu_pre = np.concatenate([[0], np.cumsum(pre)])
     if pre.sum() > 0:
@@ -84,7 +87,8 @@ def run_step(label, lens, hkv, group, hb, fmt="int4", kv_dtype="bf16", q_dtype="
     new = parity.touched_mask(pool0.shape, cu1, pre, table)
     pool_ref = pool0.copy()
     infos = oracle.append(pool_ref, knew, vnew, cu1, pre, table, hb, FMT[fmt])
-    flips = parity.check_append(gpu_pool, pool_ref, infos, cu1, pre, table, FMT[fmt], fill, label,
+    flips = parity.check_append(gpu_pool, pool_ref, infos, cu1, pre, table, FMT[fmt],
+                                pool0 if isinstance(fill, str) else fill, label,
                                 prior_mask=prior)
     keep = prior & ~new
     assert np.array_equal(gpu_pool[keep], pool0[keep]), f"{label}: earlier tokens' bytes changed"
