@@ -189,6 +189,56 @@ def test_config_llama_step():
     assert torch.equal(out16.cpu(), out.cpu().to(torch.bfloat16))
 
 
+def test_config_prefill_attention():
+    # the chunked-prefill launch the benchmark times, at its size: 32 sequences whose last 512 of
+    # 4096 positions are a new turn attending causally over the resident prefix and each other,
+    # 32 q / 8 kv heads.  The cache is the GPU's append of the llama workload; sampled chunk tokens
+    # (the first, middle and last query tiles) of sequences 0 and 31 are checked against the
+    # oracle's attention over that pool, and a bf16 output (the benchmark's dtype) against the
+    # round-to-nearest-even of the fp32 one.
+    from oracle.attention import decode_attention_one, gather_sequence
+    w = wl.WORKLOADS["llama"]
+    chunk = 512
+    print("[config] prefill attention: building", flush=True)
+    lens = wl.seq_lens(w)
+    table, num_pages = wl.block_table(w, lens)
+    dev = torch.device("cuda")
+    cache = kvq.Cache(num_pages, w.num_kv_heads, w.had_block, w.fmt, fill=SENT)
+    bt = torch.from_numpy(table).to(dev)
+    for b0 in range(0, w.batch, 8):
+        bs = list(range(b0, b0 + 8))
+        kv = [wl.sequence_kv(w, b, int(lens[b])) for b in bs]
+        cnt = np.zeros(w.batch, np.int64)
+        cnt[bs] = lens[bs]
+        cu = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+        kvq.append(cache, torch.from_numpy(np.concatenate([k for k, _ in kv])).to(TDT[w.kv_dtype]).to(dev),
+                   torch.from_numpy(np.concatenate([v for _, v in kv])).to(TDT[w.kv_dtype]).to(dev),
+                   torch.from_numpy(cu).to(dev), torch.zeros(w.batch, dtype=torch.int32, device=dev), bt,
+                   int(lens.max()))
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((w.batch * chunk, w.num_q_heads, 128)).astype(np.float32)
+    q_t = torch.from_numpy(q).to(torch.bfloat16)
+    cu_q = torch.arange(0, w.batch * chunk + 1, chunk, dtype=torch.int32, device=dev)
+    sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    out = kvq.prefill_attn(cache, q_t.to(dev), cu_q, sl, bt, int(lens.max()), chunk, out_dtype=torch.float32)
+    out16 = kvq.prefill_attn(cache, q_t.to(dev), cu_q, sl, bt, int(lens.max()), chunk, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert torch.equal(out16.cpu(), out.cpu().to(torch.bfloat16))
+    pool = cache.pool.cpu().numpy()
+    qn = q_t.float().numpy()
+    worst = 0.0
+    for b in (0, 31):
+        k_rot, v_rot = gather_sequence(pool, table[b], int(lens[b]), w.had_block, FMT[w.fmt])
+        for j in list(range(0, 64)) + list(range(256, 272)) + list(range(448, 512)):
+            i = b * chunk + j
+            pos = int(lens[b]) - chunk + j
+            ref = decode_attention_one(qn[i], k_rot[:, :pos + 1], v_rot[:, :pos + 1], w.had_block)
+            worst = max(worst, parity.attn_row_error(got[i], ref).max())
+    print(f"[config] prefill attention: max row err {worst:.3e} on sequences 0, 31 (288 tokens)", flush=True)
+    assert worst <= parity.ATTN_TOL
+
+
 def test_config_long_ragged():
     w = wl.WORKLOADS["long"]
     lens = wl.seq_lens(w)
