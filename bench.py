@@ -15,7 +15,6 @@ the measured copy and read-only bandwidths, the prefill-append throughput (64 x 
 without rotation) and the CPU oracle's rate on a bounded sample.
 """
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -28,15 +27,11 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from bit_kv_cache_02_amd import kvq, workloads as wl  # noqa: E402
+from bit_kv_cache_02_amd import kvq, profsum, workloads as wl  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 PAGE_HEAD = 2176
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_llama_traffic.json")
-CSRC = os.path.join(ROOT, "bit_kv_cache_02_amd", "csrc")
-DECODE_SRC = [os.path.join(CSRC, f) for f in ("kvq_decode.hip", "kvq_attn.h", "kvq_device.h")]
-APPEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_prefill_traffic.json")
-APPEND_SRC = [os.path.join(CSRC, f) for f in ("kvq_append.hip", "kvq_device.h")]
+
 
 
 def log(*a):
@@ -596,44 +591,34 @@ def cpu_per_workload(budget_s=2.0):
     return res
 
 
-def code_sha256(paths):
-    """sha256 of the code of the given source files: comment-only edits leave it unchanged."""
-    lines = []
-    for path in paths:
-        for line in open(path, encoding="utf-8"):
-            code = line.split("//", 1)[0].rstrip()
-            if code:
-                lines.append(code)
-    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
-
-
-def profile_record(path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_source_sha256"):
-    """The committed rocprofv3 record of a kernel, if the kernel's code has not changed since it
-    was taken (else None)."""
+def profile_record(leg):
+    """The committed rocprofv3 record of a leg's kernel (profiles/<leg>_traffic.json), if the
+    kernel's code has not changed since it was taken (else None)."""
+    _, _, src, key, _ = profsum.LEGS[leg]
     try:
-        rec = json.load(open(path))
-        if rec.get(key) != code_sha256(src_path):
+        rec = json.load(open(os.path.join(ROOT, "profiles", f"{leg}_traffic.json")))
+        if rec.get(key) != profsum.code_sha256(src):
             return None
         return rec
     except (OSError, ValueError):
         return None
 
 
-def traffic_entry(algo_bytes, path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_source_sha256"):
+def traffic_entry(leg):
     """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE, each
     scaled by what the counter reads for the bench's 1 GiB copy), if the kernel's code has not
     changed since they were taken."""
-    rec = profile_record(path, src_path, key)
+    rec = profile_record(leg)
     try:
         return None if rec is None else int(rec["hbm_bytes_per_launch"])
     except (KeyError, TypeError, ValueError):
         return None
 
 
-def trace_avg_us(path=TRAFFIC_FILE, src_path=DECODE_SRC, key="decode_source_sha256"):
+def trace_avg_us(leg):
     """The kernel's average duration in the committed rocprofv3 kernel trace of bench.py
     --profile-run, if the kernel's code has not changed since (else None)."""
-    rec = profile_record(path, src_path, key)
+    rec = profile_record(leg)
     try:
         return None if rec is None else float(rec["kernel_trace_avg_us"])
     except (KeyError, TypeError, ValueError):
@@ -726,14 +711,14 @@ def main():
         "decode_workspace_bytes": decode_workspace_bytes(caches[0], w.num_q_heads, w.batch, int(lens.max())),
         "roofline": {
             "bound": "hbm",
-            "kernel": "kvq::decode_kernel<0, 8, 3> (kvq_decode_step: append + decode attention, INT4)",
+            "kernel": "kvq::decode_kernel<0, 8, 3, 1> (kvq_decode_step: append + decode attention, INT4)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic_entry(step_bytes),
+            "traffic": traffic_entry("decode_step_llama"),
             "launch_us_events": round(step_us, 3),
-            "launch_us_kernel_trace": trace_avg_us(),
+            "launch_us_kernel_trace": trace_avg_us("decode_step_llama"),
         },
         **res,
     }
@@ -741,6 +726,8 @@ def main():
     if not args.no_prefill:
         log("[bench] chunked-prefill attention")
         res["prefill_attention"] = time_prefill_attention(w, caches, lens, dev)
+        res["prefill_attention"]["roofline"]["traffic"] = traffic_entry("prefill_attention")
+        res["prefill_attention"]["us_kernel_trace"] = trace_avg_us("prefill_attention")
     log("[bench] HBM copy probe")
     res["hbm_copy_GBps"] = round(hbm_copy_probe(dev), 1)
     res["step_frac_of_copy_bw"] = round(achieved / res["hbm_copy_GBps"], 4)
@@ -754,22 +741,28 @@ def main():
     res["hbm_fold4_GBps"] = round(hbm_fold4_probe(dev), 1)
     log("[bench] page dequantization")
     res["dequant_pages"] = time_dequant(caches[0], dev, repeats=5 if args.profile_run else 20)
+    res["dequant_pages"]["traffic_plain"] = traffic_entry("dequant_plain")
+    res["dequant_pages"]["traffic_unrotated"] = traffic_entry("dequant_rotated")
     del caches
     torch.cuda.empty_cache()
     if not args.no_prefill:
         log("[bench] prefill append")
         res["prefill_append"] = time_prefill_append(dev, repeats=3 if args.profile_run else 10)
         res["prefill_append"]["frac_of_fold4_bw"] = round(res["prefill_append"]["GBps"] / res["hbm_fold4_GBps"], 4)
-        res["prefill_append"]["traffic"] = traffic_entry(res["prefill_append"]["algorithmic_bytes"],
-                                                         APPEND_TRAFFIC_FILE, APPEND_SRC, "append_source_sha256")
+        res["prefill_append"]["traffic"] = traffic_entry("append_prefill")
+        res["prefill_append"]["us_kernel_trace"] = trace_avg_us("append_prefill")
         torch.cuda.empty_cache()
     log("[bench] long/ragged decode")
     res["long_ragged_decode"] = time_long_decode(dev, replays=5 if args.profile_run else 25)
+    res["long_ragged_decode"]["traffic"] = traffic_entry("decode_long_ragged")
+    res["long_ragged_decode"]["us_kernel_trace"] = trace_avg_us("decode_long_ragged")
     log("[bench] tiny decode step")
     res["tiny_step"] = time_tiny_step(dev, replays=100 if args.profile_run else 400)
     if not args.no_mxfp4:
         log("[bench] MXFP4 decode (f16-tile and scaled-MFMA q.K)")
         res["mxfp4_decode"] = time_mxfp4_decode(dev, repeats=3 if args.profile_run else 40)
+        res["mxfp4_decode"]["traffic"] = traffic_entry("decode_mxfp4")
+        res["mxfp4_decode"]["us_kernel_trace"] = trace_avg_us("decode_mxfp4")
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)
