@@ -269,7 +269,8 @@ def time_long_decode(dev, replays=25):
 
 def time_mxfp4_decode(dev, repeats=40):
     """MXFP4 decode, 64 x 16K contexts, 64 q / 8 kv heads, fp8 e4m3 queries, over 2 alternating
-    pools (2.3 GB, beyond the Infinity Cache): q.K on f16 tiles vs the scaled FP8 x FP4 MFMA."""
+    pools (2.3 GB, beyond the Infinity Cache): both contractions on f16 tiles vs both on the scaled
+    FP8 x FP4 MFMA (FP8 queries, FP8-quantized attention weights)."""
     from concurrent.futures import ThreadPoolExecutor
     w = wl.WORKLOADS["mxfp4"]
     lens = wl.seq_lens(w)
@@ -759,10 +760,12 @@ def main():
     log("[bench] tiny decode step")
     res["tiny_step"] = time_tiny_step(dev, replays=100 if args.profile_run else 400)
     if not args.no_mxfp4:
-        log("[bench] MXFP4 decode (f16-tile and scaled-MFMA q.K)")
+        log("[bench] MXFP4 decode (f16 tiles and scaled FP8 x FP4 MFMA)")
         res["mxfp4_decode"] = time_mxfp4_decode(dev, repeats=3 if args.profile_run else 40)
         res["mxfp4_decode"]["traffic"] = traffic_entry("decode_mxfp4")
         res["mxfp4_decode"]["us_kernel_trace"] = trace_avg_us("decode_mxfp4")
+        res["mxfp4_decode"]["traffic_scaled_mfma"] = traffic_entry("decode_mxfp4_scaled")
+        res["mxfp4_decode"]["us_kernel_trace_scaled_mfma"] = trace_avg_us("decode_mxfp4_scaled")
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w, budget_s=args.cpu_budget)

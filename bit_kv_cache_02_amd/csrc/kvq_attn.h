@@ -677,6 +677,186 @@ __device__ __forceinline__ void process_page_mx_scaled(const PageData<1>& pg, in
                 n, jg, a_row_used, ptile);
 }
 
+// p.V of an MXFP4 cache on the scaled matrix cores as well (UltraQuant article, section on how
+// the method works: FP8-quantized attention weights against the FP4 V tensors with their UE8M0
+// group scales): v_mfma_scale_f32_32x32x64_f8f6f4, 64 tokens (4 pages) per MFMA, one MFMA per V
+// channel group of 32 (the output columns).  Operand layouts (checked on the device): A (e4m3)
+// lane l is row l%32, bytes 0-15 hold K 16(l/32)+j and bytes 16-31 hold K 32+16(l/32)+j; B (e2m1)
+// lane l is column l%32, nibble i (low nibble first) holds K 32(l/32)+i; each lane supplies the
+// scale of its row / column for the 32-long K block l/32; D register i of lane l is row
+// 8(i/4)+4(l/32)+i%4, column l%32.
+//
+// The V codes go in raw (B scale 1); V's UE8M0 scale belongs to (token, channel group), which the
+// MFMA's per-(column, K block) B scale cannot express, so it moves into the A side:
+// p~[h][t] = p[h][t] * 2^(E_v[t][group] - 127), one A operand per channel group.  p~ enters as
+// three e4m3 limbs (rows 8(h/2)+4(h%2)+t of the A tile, t = limb; row t = 3 stays zero), each with
+// one UE8M0 scale per 32 tokens: limb t is what the limbs before it left, scaled so that the
+// block's largest magnitude lands in [128, 256).  Three limbs keep ~12 bits of p~ relative to
+// its block maximum.  Per page, the wave stages the V codes transposed (channel-major nibbles)
+// and the V exponents in LDS; every fourth page it updates the running maximum once for the four
+// pages, builds the limbs (lane 8h + 2g + kb: head h, channel group g, 32-token block kb) and
+// runs the four MFMAs.
+struct ScaledStage {
+  uint8_t vt[4][32][32];   // V codes of group g, column c (channel 32g+c), 64 tokens as nibbles
+  int32_t ve[4][64];       // V exponent - 127 of group g, token
+  union {
+    float p[kMaxG][64];              // p of the group's tokens, per head
+    uint8_t a8[4][3 * kMaxG][64];    // e4m3 limbs of p~: group, row 3h+t, token
+  };
+  uint8_t as[4][3 * kMaxG][2];       // their UE8M0 scales per 32-token block
+};
+
+// Scores of one page on the scaled matrix cores, masked, into x0 / x1 (heads 2jg, 2jg+1 of
+// token n), and the page's V codes and exponents staged for slot d of the 4-page group.
+__device__ __forceinline__ void scaled_stage_page(const PageData<1>& pg, int valid, const i32x8 (&qa8)[2],
+                                                  const int (&qsa)[2], float c2, int n, int jg, int d,
+                                                  ScaledStage& st, float& x0, float& x1) {
+  const f32x4 sc = scores_mx_scaled(pg, qa8, qsa, jg);
+  const bool tv = n < valid;
+  x0 = tv ? (sc[0] + sc[1]) * c2 : -INFINITY;
+  x1 = tv ? (sc[2] + sc[3]) * c2 : -INFINITY;
+  // V word q: row bytes 4n+q of tokens 4jg .. 4jg+3 (byte r: token 4jg+r); its low nibbles are
+  // channel n+32q (column n of group q), its high nibbles channel n+32q+16 (column n+16).  The
+  // four nibbles of a column go to token positions 16d+4jg .. +3: one 16-bit store.
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t Y = pg.v[q];
+    const uint32_t lo = Y & 0x0F0F0F0Fu, hi = (Y >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lo2 = lo | (lo >> 4), hi2 = hi | (hi >> 4);  // bytes 0 and 2 hold the pairs
+    *(uint16_t*)&st.vt[q][n][8 * d + 2 * jg] = (uint16_t)perm(0u, lo2, 0x0C0C0200u);
+    *(uint16_t*)&st.vt[q][n + 16][8 * d + 2 * jg] = (uint16_t)perm(0u, hi2, 0x0C0C0200u);
+  }
+  // exponents of token 4jg + n (lanes n < 4), zero past the sequence's end: their p is 0 anyway,
+  // and a stray byte then cannot matter
+  if (n < 4) {
+    const int t = 4 * jg + n;
+    const uint32_t wn = n == 0 ? pg.vp4[0] : (n == 1 ? pg.vp4[1] : (n == 2 ? pg.vp4[2] : pg.vp4[3]));
+    const uint32_t w = t < valid ? wn : 0x7F7F7F7Fu;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) st.ve[g][16 * d + t] = (int)((w >> (8 * g)) & 255u) - 127;
+  }
+}
+
+// p.V accumulators of the scaled path: one 32x32 tile per channel group.
+struct ScaledAcc {
+  f32x16 c[4];
+};
+
+// The 4-page group's softmax and p.V on the scaled matrix cores (layout above).  xs0 / xs1: the
+// masked scores of the group's pages (heads 2jg, 2jg+1 of token n; -inf for pages past the
+// wave's last).
+__device__ __forceinline__ void scaled_flush(const float (&xs0)[4], const float (&xs1)[4], WaveState& s,
+                                             ScaledAcc& acc, ScaledStage& st, int G, bool has0, bool has1, int n,
+                                             int jg, int lane) {
+  // ---- running maximum, once for the four pages (p <= 2^8 keeps every partial sum in range) ----
+  const float pm0 = row_max16(fmaxf(fmaxf(xs0[0], xs0[1]), fmaxf(xs0[2], xs0[3])));
+  const float pm1 = row_max16(fmaxf(fmaxf(xs1[0], xs1[1]), fmaxf(xs1[2], xs1[3])));
+  if (__any(pm0 > s.m0 + 8.0f || pm1 > s.m1 + 8.0f)) {
+    const float mn0 = fmaxf(s.m0, pm0), mn1 = fmaxf(s.m1, pm1);
+    const float f0 = __builtin_amdgcn_exp2f(s.m0 - mn0), f1 = __builtin_amdgcn_exp2f(s.m1 - mn1);
+    s.l0 *= f0;
+    s.l1 *= f1;
+    s.m0 = mn0;
+    s.m1 = mn1;
+    // accumulator rows of lane half b hold heads 2a + b (registers 4a .. 4a+3): head 2a is lane
+    // group a's first head, 2a+1 its second
+    const int b = lane >> 5;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float fa0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f0), 16 * a));
+      const float fa1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f1), 16 * a));
+      const float f = b ? fa1 : fa0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int t = 0; t < 3; ++t) acc.c[g][4 * a + t] *= f;
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float p0 = __builtin_amdgcn_exp2f(xs0[d] - s.m0), p1 = __builtin_amdgcn_exp2f(xs1[d] - s.m1);
+    s.l0 += p0;
+    s.l1 += p1;
+    if (has0) st.p[2 * jg][16 * d + n] = p0;
+    if (has1) st.p[2 * jg + 1][16 * d + n] = p1;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // ---- e4m3 limbs of p~ = p * 2^(E_v - 127): lane 8h + 2g + kb, 32 tokens ----
+  const int h = lane >> 3, g = (lane >> 1) & 3, kb = lane & 1;
+  float v[32];
+  if (h < G) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const f32x4 pv = *(const f32x4*)&st.p[h][32 * kb + 4 * w];
+      const i32x4 ev = *(const i32x4*)&st.ve[g][32 * kb + 4 * w];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * w + r] = ldexpf(pv[r], ev[r]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  }
+  // every lane has read its p before any limb overwrites them (a8 shares their bytes)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+    // UE8M0 scale 2^(floor(log2 m) - 7): the largest magnitude scales into [128, 256), inside
+    // e4m3's range (448), so no element saturates
+    const int sc = max((int)((__float_as_uint(m) >> 23) & 255u) - 7, 0);
+    const float inv = ldexpf(1.0f, 127 - sc), scl = ldexpf(1.0f, sc - 127);
+    uint32_t wd[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w] * inv, v[4 * w + 1] * inv, 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2] * inv, v[4 * w + 3] * inv, pk, true);
+      wd[w] = (uint32_t)pk;
+      if (t < 2) {
+        v[4 * w + 0] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(pk, 0), scl, v[4 * w + 0]);
+        v[4 * w + 1] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(pk, 1), scl, v[4 * w + 1]);
+        v[4 * w + 2] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(pk, 2), scl, v[4 * w + 2]);
+        v[4 * w + 3] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(pk, 3), scl, v[4 * w + 3]);
+      }
+    }
+    if (h < G) {
+      *(u32x4*)&st.a8[g][3 * h + t][32 * kb] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+      *(u32x4*)&st.a8[g][3 * h + t][32 * kb + 16] = u32x4{wd[4], wd[5], wd[6], wd[7]};
+      st.as[g][3 * h + t][kb] = (uint8_t)sc;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // ---- the four MFMAs: A row r = 8(h/2) + 4(h%2) + t of lane r + 32 b ----
+  const int r = lane & 31, b = lane >> 5;
+  const int ha = 2 * (r >> 3) + ((r >> 2) & 1), ta = r & 3;
+  const bool used = ta < 3 && ha < G;
+  const int row = 3 * ha + ta;
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg) {
+    const u32x4 a0 = used ? *(const u32x4*)&st.a8[gg][row][16 * b] : u32x4{0, 0, 0, 0};
+    const u32x4 a1 = used ? *(const u32x4*)&st.a8[gg][row][32 + 16 * b] : u32x4{0, 0, 0, 0};
+    const int sa = used ? (int)st.as[gg][row][b] : 127;
+    const u32x4 bv = *(const u32x4*)&st.vt[gg][r][16 * b];
+    const i32x8 A = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const i32x8 B = i32x8{(int)bv[0], (int)bv[1], (int)bv[2], (int)bv[3], 0, 0, 0, 0};
+    // format codes: 0 = fp8 e4m3 (A), 4 = fp4 e2m1 (B); B scale 127 = 1
+    acc.c[gg] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc.c[gg], 0, 4, 0, sa, 0, 127);
+  }
+  // the operands are in registers before the next group's staging overwrites them
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Rotate one row's normalised o' (element lane in o0, lane + 64 in o1) back and store it at
 // row `row` of a [rows][128] output of dtype `out_dtype`.
 __device__ __forceinline__ void store_row(void* out, int64_t row, int out_dtype, int rotated, int had_block,

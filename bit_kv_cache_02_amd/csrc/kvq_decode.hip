@@ -16,7 +16,8 @@
 //            p_t*sv_t enters split into an fp16 high part and an fp16 low part (rows 2g and
 //            2g+1), which keeps ~22 bits of it.
 // MXFP4 pages convert to fp16 tiles with the group scale applied (v_cvt_scalef32_pk_f16_fp4) and
-// run both contractions on the f16 matrix cores.
+// run both contractions on the f16 matrix cores; with KVQ_MX_SCALED_MFMA both run on the scaled
+// FP8 x FP4 matrix cores straight on the stored codes instead (layouts in kvq_attn.h).
 // kvq_decode_step runs the same kernel with the append folded in: the workgroup that streams a
 // sequence's last page also rotates and quantizes that step's new K/V token (a wave butterfly),
 // writes it into the page, and substitutes its bytes into the page registers it streams.
@@ -34,13 +35,15 @@
 
 #include <stdlib.h>
 
+#include <type_traits>
+
 namespace kvq {
 
 namespace {
 
 using namespace attn;
 
-template <int W>
+template <int W, int FMT>
 struct DecodeSmem {
   // INT4: q' limbs (hi, mid, lo) in the byte order of the q.K A tile: [limb][g][a2][jg][16 bytes]
   uint8_t qlimb[3][kMaxG][2][4][16];
@@ -53,7 +56,13 @@ struct DecodeSmem {
   float qdelta[kMaxG];  // INT4: weight of the mid limb, 256 delta
   float qsum[kMaxG];
   _Float16 ptile[W][2 * kMaxG][kPage];  // p~ split into fp16 high/low parts, A-tile rows 2g+limb
-  float wo[W][kMaxG][kHeadDim];
+  // each wave's partial output (after its pages); on the scaled MXFP4 path the same bytes hold
+  // the wave's staging while it streams
+  union WaveBuf {
+    float wo[kMaxG][kHeadDim];
+    std::conditional_t<FMT == 2, ScaledStage, float> st;
+  };
+  WaveBuf wb[W];
   float wm[W][kMaxG];
   float wl[W][kMaxG];
   // fused step: codes of the appended K (0) and V (1) vectors, their packed 64-byte rows and
@@ -245,12 +254,12 @@ __device__ __forceinline__ void merge_runs(const DecodeParams& a, int64_t s0, in
 }  // namespace
 
 
-// FMT: 0 INT4; 1 MXFP4 (f16 tiles); 2 MXFP4 with q.K on the scaled FP8 x FP4 matrix cores.
+// FMT: 0 INT4; 1 MXFP4 (f16 tiles); 2 MXFP4 with q.K and p.V on the scaled FP8 x FP4 matrix cores.
 // HPL: heads per lane group of the INT4 page step (1: at most 4 heads, 2: more; MXFP4: 2).
 template <int FMT, int W, int D, int HPL>
 __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   constexpr int PF = FMT == 0 ? 0 : 1;  // page format
-  __shared__ DecodeSmem<W> sm;
+  __shared__ DecodeSmem<W, FMT> sm;
   const int tid = thread_id();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -501,6 +510,14 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   s.l0 = s.l1 = s.pz0 = s.pz1 = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) s.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // scaled MXFP4 path: the p.V tiles and the masked scores of the current 4-page group
+  static_assert(FMT != 2 || NB == 4, "the scaled path takes its pages in groups of four");
+  ScaledAcc sacc;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc.c[g][i] = 0.0f;
+  float xs0[4], xs1[4];
   const int valid0 = L - pw0 * kPage;
   const int late_bias = (a.plan.balanced && 2 * block_id_x() >= a.num_seqs * a.hkv * a.plan.nsplit) ? 1 : 0;
   for (int i0 = 0; i0 < npw; i0 += NB) {
@@ -542,8 +559,12 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
           process_page_mx(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, valid0 - i * W * kPage, s, qh, c2,
                           has0, has1, n, jg, a_row_used, sm.ptile[wave]);
         else
-          process_page_mx_scaled(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, valid0 - i * W * kPage, s,
-                                 qa8, qsa, c2, has0, has1, n, jg, a_row_used, sm.ptile[wave]);
+          scaled_stage_page(st[d], valid0 - i * W * kPage, qa8, qsa, c2, n, jg, d, sm.wb[wave].st, xs0[d], xs1[d]);
+      } else if constexpr (FMT == 2) {
+        xs0[d] = xs1[d] = -INFINITY;
+      }
+      if constexpr (FMT == 2) {
+        if (d == NB - 1) scaled_flush(xs0, xs1, s, sacc, sm.wb[wave].st, G, has0, has1, n, jg, lane);
       }
     }
   }
@@ -551,16 +572,29 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   // ---- 4. wave partial -> LDS ----
   const float l0 = row_sum16(s.l0), l1 = row_sum16(s.l1);
   const float pz0 = row_sum16(s.pz0), pz1 = row_sum16(s.pz1);
+  if constexpr (FMT == 2) {
+    // tile register 4a + t of lane half b: head 2a + b, limb t, channel 32g + lane % 32
+    const int bh = lane >> 5, col = lane & 31;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int h = 2 * a4 + bh;
+      if (h < G) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          sm.wb[wave].wo[h][32 * g + col] = sacc.c[g][4 * a4] + sacc.c[g][4 * a4 + 1] + sacc.c[g][4 * a4 + 2];
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4 && FMT != 2; ++q) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int ch = n + 32 * q + 16 * e;
       const f32x4 v = s.acc[2 * q + e];
       // INT4: undo the subnormal encoding (2^24, or 2^24/16 for the high nibbles); MXFP4: none
       const float sc = FMT != 0 ? 1.0f : (e ? 1048576.0f : 16777216.0f);
-      if (has0) sm.wo[wave][h0][ch] = sc * (v[0] + v[1]) + pz0;
-      if (has1) sm.wo[wave][h0 + 1][ch] = sc * (v[2] + v[3]) + pz1;
+      if (has0) sm.wb[wave].wo[h0][ch] = sc * (v[0] + v[1]) + pz0;
+      if (has1) sm.wb[wave].wo[h0 + 1][ch] = sc * (v[2] + v[3]) + pz1;
     }
   }
   if (n == 0) {
@@ -578,8 +612,8 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const float f = exp2f(sm.wm[w][g] - M);
-      O0 = fmaf(f, sm.wo[w][g][lane], O0);
-      O1 = fmaf(f, sm.wo[w][g][lane + 64], O1);
+      O0 = fmaf(f, sm.wb[w].wo[g][lane], O0);
+      O1 = fmaf(f, sm.wb[w].wo[g][lane + 64], O1);
       Ls = fmaf(f, sm.wl[w][g], Ls);
     }
     if (pieces == 1) {
@@ -718,8 +752,10 @@ hipError_t launch_decode(const DecodeParams& p, int variant, hipStream_t stream)
   const dim3 grid((unsigned)(units * p.plan.nsplit));
   // INT4 with at most 4 query heads per kv head: one head per lane group
   const int hpl = (fmt == 0 && p.group <= 4) ? 1 : 2;
+  // the scaled MXFP4 path takes its pages in groups of four: three in flight plus one
+  const int depth = fmt == 2 ? 3 : p.plan.depth;
 #define KVQ_DECODE_CASE(F, WV, DV, H)                                                            \
-  if (fmt == F && p.plan.waves == WV && p.plan.depth == DV && hpl == H) {                      \
+  if (fmt == F && p.plan.waves == WV && depth == DV && hpl == H) {                             \
     hipLaunchKernelGGL((decode_kernel<F, WV, DV, H>), grid, dim3(WV * 64), 0, stream, p);       \
   } else
   KVQ_DECODE_CASE(0, 4, 2, 1) KVQ_DECODE_CASE(0, 4, 3, 1) KVQ_DECODE_CASE(0, 4, 4, 1)
@@ -731,9 +767,7 @@ hipError_t launch_decode(const DecodeParams& p, int variant, hipStream_t stream)
   KVQ_DECODE_CASE(1, 4, 2, 2) KVQ_DECODE_CASE(1, 4, 3, 2) KVQ_DECODE_CASE(1, 4, 4, 2)
   KVQ_DECODE_CASE(1, 8, 2, 2) KVQ_DECODE_CASE(1, 8, 3, 2) KVQ_DECODE_CASE(1, 8, 4, 2)
   KVQ_DECODE_CASE(1, 16, 2, 2)
-  KVQ_DECODE_CASE(2, 4, 2, 2) KVQ_DECODE_CASE(2, 4, 3, 2) KVQ_DECODE_CASE(2, 4, 4, 2)
-  KVQ_DECODE_CASE(2, 8, 2, 2) KVQ_DECODE_CASE(2, 8, 3, 2) KVQ_DECODE_CASE(2, 8, 4, 2)
-  KVQ_DECODE_CASE(2, 16, 2, 2) { return hipErrorInvalidValue; }
+  KVQ_DECODE_CASE(2, 4, 3, 2) KVQ_DECODE_CASE(2, 8, 3, 2) { return hipErrorInvalidValue; }
 #undef KVQ_DECODE_CASE
   return hipGetLastError();
 }

@@ -14,6 +14,7 @@ constexpr int kKParamsOff = 2048;
 constexpr int kVParamsOff = 2112;
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;

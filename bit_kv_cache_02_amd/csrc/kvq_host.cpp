@@ -321,7 +321,7 @@ static int decode_common(const kvq_cache* cache, const void* knew, const void* v
     c.num_pages = cache->num_pages;
     if (int st = device_check(c, stream, what)) return st;
   }
-  // kernel variant 2: MXFP4 with q.K on the scaled matrix cores
+  // kernel variant 2: MXFP4 with q.K and p.V on the scaled matrix cores
   const int variant = (flags & KVQ_MX_SCALED_MFMA) ? 2 : cache->format;
   return hip_status(kvq::launch_decode(p, variant, (hipStream_t)stream), what);
 }

@@ -202,7 +202,7 @@ def decode_attn(cache: Cache, q: torch.Tensor, seq_lens: torch.Tensor, block_tab
                 workspace: Optional[torch.Tensor] = None, scaled_mfma: bool = False) -> torch.Tensor:
     """softmax(q'.K'^T) V' over the paged cache, rotated back (kvq_decode_attn).
 
-    scaled_mfma (MXFP4 caches): q.K on the scaled FP8 x FP4 matrix cores (KVQ_MX_SCALED_MFMA).
+    scaled_mfma (MXFP4 caches): q.K and p.V on the scaled FP8 x FP4 matrix cores (KVQ_MX_SCALED_MFMA).
     """
     _require(q, "q")
     _require(seq_lens, "seq_lens", torch.int32)

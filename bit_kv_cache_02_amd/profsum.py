@@ -63,6 +63,9 @@ LEGS = {
                            "decode_source_sha256", "long/ragged decode (kvq_decode_attn, balanced cut)"),
     "decode_mxfp4": (r"decode_kernel<1, ", ("mxfp4_decode", "algorithmic_bytes"), DECODE_SRC,
                      "decode_source_sha256", "MXFP4 decode, f16-tile q.K path (kvq_decode_attn)"),
+    "decode_mxfp4_scaled": (r"decode_kernel<2, ", ("mxfp4_decode", "algorithmic_bytes"), DECODE_SRC,
+                            "decode_source_sha256", "MXFP4 decode, both contractions on the scaled FP8 x FP4 "
+                            "matrix cores (kvq_decode_attn, KVQ_MX_SCALED_MFMA)"),
     "dequant_rotated": (r"dequant_kernel<true>", ("dequant_pages", "algorithmic_bytes"), DEQUANT_SRC,
                         "dequant_source_sha256", "page dequantization rotated back (kvq_dequant_page)"),
     "dequant_plain": (r"dequant_kernel<false>", ("dequant_pages", "algorithmic_bytes"), DEQUANT_SRC,

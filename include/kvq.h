@@ -78,7 +78,7 @@ typedef enum { KVQ_F16 = 0, KVQ_BF16 = 1, KVQ_F32 = 2, KVQ_FP8_E4M3 = 3 } kvq_dt
 
 /* kvq_decode_attn flags */
 #define KVQ_OUT_ROTATED 1u /* leave the output in the rotated basis (skip the final R_b) */
-#define KVQ_MX_SCALED_MFMA 2u /* MXFP4 caches: q.K on the scaled FP8 x FP4 matrix cores    */
+#define KVQ_MX_SCALED_MFMA 2u /* MXFP4 caches: q.K and p.V on the scaled FP8 x FP4 matrix cores */
 /* kvq_dequant_page flags */
 #define KVQ_UNROTATE 1u    /* return R_b * y^ (the original basis) instead of y^          */
 
@@ -172,13 +172,22 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_q_heads,
  *                o = R^T sum_t softmax_t(sm_scale * q'.k^'_t) v^'_t (q' = R q; R^T = R_b for
  *                the Hadamard rotation), or the rotated-basis
  *                result with KVQ_OUT_ROTATED.
- *   flags        KVQ_OUT_ROTATED (above) and, for MXFP4 caches only, KVQ_MX_SCALED_MFMA: the
- *                q.K contraction then runs on v_mfma_scale_f32_16x16x128_f8f6f4 straight on the
- *                stored e2m1 K codes and their UE8M0 bytes (UltraQuant article, section on how the
- *                method works: FP8 queries, FP4 KV, UE8M0 group scales, native scaled MFMA on
- *                CDNA4), with q' carried as three MXFP8 limbs; p.V is unchanged.  The result
- *                agrees with the default path to the same tolerance.  KVQ_ERR_UNSUPPORTED on an
- *                INT4 cache; any other bit is KVQ_ERR_INVALID_ARG.
+ *   flags        KVQ_OUT_ROTATED (above) and, for MXFP4 caches only, KVQ_MX_SCALED_MFMA: both
+ *                contractions then run on the scaled FP8 x FP4 matrix cores straight on the
+ *                stored e2m1 codes (UltraQuant article, section on how the method works: FP8
+ *                queries, FP4 KV, UE8M0 group scales, native scaled MFMA on CDNA4).  q.K:
+ *                v_mfma_scale_f32_16x16x128_f8f6f4 on the K codes and their UE8M0 bytes, q'
+ *                carried as three MXFP8 limbs.  p.V: v_mfma_scale_f32_32x32x64_f8f6f4 on the V
+ *                codes, 64 tokens and one 32-channel group per product, with the attention
+ *                weights FP8-quantized: p times the token's V group scale as three e4m3 limbs,
+ *                one UE8M0 scale per 32 tokens.  The default (fp16 tiles) is the faster one and
+ *                the more exact: a scaled MFMA sums its products to about 2^-14.5 of the largest
+ *                one (measured), so the scores carry an error that grows with
+ *                sm_scale * max|q'_i k'_i|; the row error stays within 2e-3 up to about 50 for
+ *                that product.  The default path dequantizes K and V of an MXFP4 cache into fp16
+ *                tiles, so their values must stay below 65504 in magnitude; the scaled path has
+ *                no such limit.  KVQ_ERR_UNSUPPORTED on an INT4 cache; any other bit is
+ *                KVQ_ERR_INVALID_ARG.
  *   workspace    device, >= kvq_decode_workspace_bytes(...) bytes, 256-byte aligned; calls
  *                that overlap in time (other streams) need workspaces of their own.
  * Decode does not append: a decode step is kvq_append then kvq_decode_attn on one stream, or

@@ -165,6 +165,66 @@ def test_decode_sharper_softmax_with_stronger_outliers(hb):
     run_decode(f"sharp/b{hb}", pool, table, lens, 8, hb, q=q, sm_scale=2.0, tol=2e-4)
 
 
+def _mxfp4_pool(rng, lens, hkv, k, v):
+    n_pages = [-(-n // 16) for n in lens]
+    total = sum(n_pages) + 1
+    table = np.zeros((len(lens), max(n_pages)), np.int32)
+    ids = rng.permutation(total)
+    off = 0
+    for b, n in enumerate(n_pages):
+        table[b, :n] = ids[off:off + n]
+        off += n
+    pool = np.full((total, hkv, 2176), 0x5A, np.uint8)
+    oracle.append(pool, k, v, np.concatenate([[0], np.cumsum(lens)]), np.zeros(len(lens), np.int64), table, 128,
+                  oracle.FMT_MXFP4)
+    return pool, table
+
+
+@pytest.mark.parametrize("scaled", [False, True])
+def test_decode_mxfp4_sharp_softmax(scaled):
+    # x30 outlier channels in K: a nearly one-hot softmax whose maximum keeps rising along the
+    # sequence (the running maximum moves inside and across the scaled path's 4-page groups).
+    # The f16-tile path takes sm_scale 2.  The scaled path takes sm_scale 1: a scaled FP8 x FP4
+    # MFMA sums its products to ~2^-14.5 of the largest one (measured on the device), so its
+    # score error grows with sm_scale * max|q'_i k'_i| (~50 here); at sm_scale 2 the row error
+    # reaches 2.07e-3, just past the 2e-3 rule
+    rng = np.random.default_rng(41)
+    lens = [700, 33, 2049, 64]
+    hkv = 2
+    t = sum(lens)
+    k = rng.standard_normal((t, hkv, 128)).astype(np.float32)
+    k[:, :, [7, 40, 93]] *= 30
+    k *= np.linspace(0.5, 1.5, t, dtype=np.float32)[:, None, None]
+    v = (rng.standard_normal((t, hkv, 128)) * 0.5).astype(np.float32)
+    k = torch.from_numpy(k).bfloat16().float().numpy()
+    v = torch.from_numpy(v).bfloat16().float().numpy()
+    pool, table = _mxfp4_pool(rng, lens, hkv, k, v)
+    q = rng.standard_normal((len(lens), 16, 128)).astype(np.float32)
+    run_decode(f"mxfp4/sharp/scaled={scaled}", pool, table, lens, 16, 128, fmt=oracle.FMT_MXFP4, q=q,
+               sm_scale=1.0 if scaled else 2.0, scaled_mfma=scaled)
+
+
+@pytest.mark.parametrize("scaled", [False, True])
+def test_decode_mxfp4_values_over_a_wide_range(scaled):
+    # V tokens scaled by 2^k, k uniform in [-20, kmax]: their UE8M0 group scales differ by up to
+    # 2^40 inside one 32-token block, which the scaled path folds into the attention weights
+    # before their FP8 limbs take one scale per block (kmax 20).  The f16-tile path dequantizes
+    # V into fp16 tiles, so its values must stay below 65504 (kmax 12)
+    rng = np.random.default_rng(42)
+    lens = [515, 96, 1200]
+    hkv = 2
+    t = sum(lens)
+    k = rng.standard_normal((t, hkv, 128)).astype(np.float32)
+    v = (rng.standard_normal((t, hkv, 128)) * 0.5).astype(np.float32)
+    v *= np.exp2(rng.integers(-20, (20 if scaled else 12) + 1, t)).astype(np.float32)[:, None, None]
+    k = torch.from_numpy(k).bfloat16().float().numpy()
+    v = torch.from_numpy(v).bfloat16().float().numpy()
+    pool, table = _mxfp4_pool(rng, lens, hkv, k, v)
+    q = rng.standard_normal((len(lens), 8, 128)).astype(np.float32)
+    run_decode(f"mxfp4/wide-v/scaled={scaled}", pool, table, lens, 8, 128, fmt=oracle.FMT_MXFP4, q=q,
+               scaled_mfma=scaled)
+
+
 def test_decode_page_permutation_invariance_and_determinism():
     rng = np.random.default_rng(25)
     lens = [200, 45]
