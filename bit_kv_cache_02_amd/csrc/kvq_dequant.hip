@@ -158,6 +158,48 @@ __global__ __launch_bounds__(256) void fold4_kernel(const u32x4* __restrict__ sr
   }
 }
 
+// The append's memory traffic without its arithmetic: same grid, waves, pages per wave, lane
+// map, buffer descriptors and cache policies as append_kernel, for sequences of new_tokens
+// tokens from position 0.  Lane (n, g) reads the 16-byte words at bytes 16 g + 64 j (j = 0..3)
+// of token 16 p + n's row and stores their XOR where the append stores its code row piece, plus
+// the first word where the append stores the token's parameters (lanes g = 0).
+__global__ __launch_bounds__(256) void append_pattern_kernel(const uint8_t* __restrict__ k,
+                                                             const uint8_t* __restrict__ v,
+                                                             const int32_t* __restrict__ block_table,
+                                                             uint8_t* __restrict__ pool, int hkv, int new_tokens,
+                                                             int max_pages) {
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(thread_id() >> 6);
+  const int hk = block_id_z() * 4 + wave;
+  if (hk >= 2 * hkv) return;
+  const int is_v = hk >= hkv;
+  const int h = is_v ? hk - hkv : hk;
+  const int b = block_id_y();
+  const int pg_begin = block_id_x() * kAppendPagesPerWave;
+  const int pg_end = min(pg_begin + kAppendPagesPerWave, new_tokens / kPage);
+  if (pg_begin >= pg_end) return;
+  const int npg = pg_end - pg_begin;
+  const int page_ids = lane < npg ? block_table[(int64_t)b * max_pages + pg_begin + lane] : 0;
+  const int n = lane & 15, g = lane >> 4;
+  const int row_stride = hkv * kHeadDim * 2;
+  const uint8_t* src = (is_v ? v : k) + ((int64_t)b * new_tokens * hkv + h) * (kHeadDim * 2);
+  for (int i = 0; i < npg; ++i) {
+    const int pos0 = (pg_begin + i) * kPage;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (int64_t)pos0 * row_stride, kPage * row_stride);
+    u32x4 x = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      x ^= __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, n * row_stride + 16 * g + 64 * j, 0, 0));
+    const int page_id = __builtin_amdgcn_readlane(page_ids, i);
+    const __amdgpu_buffer_rsrc_t pr =
+        make_rsrc(pool + ((int64_t)page_id * hkv + h) * (int64_t)kPageHeadBytes, kPageHeadBytes);
+    const int off = is_v ? kVCodesOff + 256 * (n >> 2) + 64 * g + 16 * (n & 3) : 64 * n + 16 * g;
+    __builtin_amdgcn_raw_buffer_store_b128(x, pr, off, 0, 2);  // 2: nontemporal, as the append
+    const int poff = g == 0 ? (is_v ? kVParamsOff : kKParamsOff) + 4 * n : attn::kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b32(x[0], pr, poff, 0, 2);
+  }
+}
+
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
   if (p.unrotate)
     hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);
@@ -198,6 +240,16 @@ hipError_t launch_fold4(const void* src, void* dst, size_t dst_bytes, hipStream_
   const int64_t per_block = (groups + blocks - 1) / blocks;
   hipLaunchKernelGGL(fold4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)src, (u32x4*)dst,
                      groups, per_block);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_pattern(const void* k, const void* v, const int32_t* block_table, void* pool, int hkv,
+                                 int num_seqs, int new_tokens, int max_pages, hipStream_t stream) {
+  const int pages = new_tokens / kPage;
+  const dim3 grid((unsigned)((pages + kAppendPagesPerWave - 1) / kAppendPagesPerWave), (unsigned)num_seqs,
+                  (unsigned)((2 * hkv + 3) / 4));
+  hipLaunchKernelGGL(append_pattern_kernel, grid, dim3(256), 0, stream, (const uint8_t*)k, (const uint8_t*)v,
+                     block_table, (uint8_t*)pool, hkv, new_tokens, max_pages);
   return hipGetLastError();
 }
 

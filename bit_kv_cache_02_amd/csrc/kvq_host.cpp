@@ -491,4 +491,23 @@ int kvq_hbm_fold4(const void* src, void* dst, size_t dst_bytes, void* stream) {
   return hip_status(kvq::launch_fold4(src, dst, dst_bytes, (hipStream_t)stream), "kvq_hbm_fold4 launch");
 }
 
+int kvq_hbm_append_pattern(const void* k, const void* v, int32_t num_kv_heads, int32_t num_seqs,
+                           int32_t new_tokens, const int32_t* block_table, int32_t max_pages, void* pool,
+                           void* stream) {
+  g_last_error[0] = 0;
+  if (!k || !v || !block_table || !pool) return fail(KVQ_ERR_INVALID_ARG, "k, v, block_table and pool must not be NULL");
+  if ((((uintptr_t)k) | ((uintptr_t)v) | ((uintptr_t)pool)) & 15)
+    return fail(KVQ_ERR_INVALID_ARG, "k, v and pool must be 16-byte aligned");
+  if ((uintptr_t)block_table & 3) return fail(KVQ_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+  if (num_kv_heads < 1 || num_kv_heads > 1024) return fail(KVQ_ERR_INVALID_ARG, "num_kv_heads must be in [1, 1024]");
+  if (num_seqs < 0 || num_seqs > 65535) return fail(KVQ_ERR_INVALID_ARG, "num_seqs must be in [0, 65535]");
+  if (new_tokens < 0 || new_tokens % 16) return fail(KVQ_ERR_INVALID_ARG, "new_tokens must be a non-negative multiple of 16");
+  if (max_pages < 0 || (int64_t)new_tokens > 16 * (int64_t)max_pages)
+    return fail(KVQ_ERR_INVALID_ARG, "new_tokens must be at most 16 * max_pages");
+  if (num_seqs == 0 || new_tokens == 0) return KVQ_OK;
+  return hip_status(kvq::launch_append_pattern(k, v, block_table, pool, num_kv_heads, num_seqs, new_tokens, max_pages,
+                                               (hipStream_t)stream),
+                    "kvq_hbm_append_pattern launch");
+}
+
 }  // extern "C"

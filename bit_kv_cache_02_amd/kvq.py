@@ -73,6 +73,8 @@ SIGNATURES = [
     ("kvq_hbm_copy", ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
     ("kvq_hbm_read", ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
     ("kvq_hbm_fold4", ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+    ("kvq_hbm_append_pattern", ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
+                                              ctypes.c_int32, _P, _P]),
 ]
 
 
@@ -353,3 +355,20 @@ def hbm_fold4(src: torch.Tensor, dst: torch.Tensor):
     if src.numel() * src.element_size() != 4 * nbytes:
         raise ValueError("src must hold exactly 4 times the bytes of dst")
     _check(lib().kvq_hbm_fold4(_ptr(src), _ptr(dst), nbytes, _stream()), "kvq_hbm_fold4")
+
+
+def hbm_append_pattern(k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor, pool: torch.Tensor,
+                       new_tokens: int):
+    """The append's memory traffic without its arithmetic (kvq_hbm_append_pattern): k, v
+    [num_seqs * new_tokens][Hkv][128] 2-byte elements, block_table int32 [num_seqs][max_pages],
+    pool uint8 [pages][Hkv][2176]."""
+    for t, n in ((k, "k"), (v, "v"), (pool, "pool")):
+        _require(t, n)
+    _require(block_table, "block_table", torch.int32)
+    if k.element_size() != 2 or v.shape != k.shape or k.dim() != 3 or k.shape[2] != HEAD_DIM:
+        raise ValueError("k and v must be [T][Hkv][128] with 2-byte elements")
+    num_seqs, max_pages = block_table.shape
+    if k.shape[0] != num_seqs * new_tokens:
+        raise ValueError("k must hold num_seqs * new_tokens rows")
+    _check(lib().kvq_hbm_append_pattern(_ptr(k), _ptr(v), k.shape[1], num_seqs, int(new_tokens), _ptr(block_table),
+                                        max_pages, _ptr(pool), _stream()), "kvq_hbm_append_pattern")

@@ -326,6 +326,25 @@ int kvq_hbm_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
  */
 int kvq_hbm_fold4(const void* src, void* dst, size_t dst_bytes, void* stream);
 
+/*
+ * kvq_hbm_append_pattern -- the memory traffic of kvq_append without its arithmetic.  Not part
+ * of the method: it measures what the append's access pattern allows (the caller's K and V rows
+ * read per kv head, 16 tokens per page, the page-head blocks written through the block table),
+ * with the same waves, lane map and cache policies as the append.
+ * k, v: device [num_seqs * new_tokens][num_kv_heads][128] 2-byte elements, sequence b's tokens
+ * at rows b * new_tokens ..; block_table: device int32 [num_seqs][max_pages] (page ids trusted,
+ * as for kvq_append); pool: device [pages][num_kv_heads][2176].  k, v and pool 16-byte aligned;
+ * new_tokens a multiple of 16, at most 16 * max_pages; 1 <= num_kv_heads <= 1024.
+ * Written, for sequence b, kv head h, page p = block_table[b][j] (j < new_tokens / 16), token
+ * slot n (0..15) and g = 0..3, with X = the XOR of the 16-byte words at bytes 16 g + 64 i
+ * (i = 0..3) of the row of token 16 j + n:  K: X at byte 64 n + 16 g of the page-head block
+ * and its first 32-bit word at 2048 + 4 n (g = 0 only); V: X at 1024 + 256 (n / 4) + 64 g +
+ * 16 (n % 4) and the first word at 2112 + 4 n.  Nothing else is written.
+ */
+int kvq_hbm_append_pattern(const void* k, const void* v, int32_t num_kv_heads, int32_t num_seqs,
+                           int32_t new_tokens, const int32_t* block_table, int32_t max_pages, void* pool,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

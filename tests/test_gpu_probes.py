@@ -51,3 +51,40 @@ def test_fold4_probe(out_bytes):
     v = host.reshape(-1, 4, 256, 4)  # [group m][k][t][4 words]
     want = v[:, 0] ^ v[:, 1] ^ v[:, 2] ^ v[:, 3]
     assert np.array_equal(dst.cpu().numpy().view(np.uint32).reshape(-1, 256, 4), want)
+
+
+@pytest.mark.parametrize("hkv,num_seqs,new_tokens", [(1, 1, 16), (2, 3, 80), (8, 2, 512), (3, 1, 64)])
+def test_append_pattern_probe(hkv, num_seqs, new_tokens):
+    # the append's traffic without its arithmetic: for each (sequence, kv head, K|V, page,
+    # slot n, g) the XOR of the row words at bytes 16 g + 64 i, written where the append writes
+    # that lane's code piece, its first word where the append writes the slot's parameters
+    print(f"[probes] append pattern hkv {hkv} seqs {num_seqs} tokens {new_tokens}", flush=True)
+    rng = np.random.default_rng(hkv * 100 + num_seqs * 10 + new_tokens)
+    t = num_seqs * new_tokens
+    kh = rng.integers(0, 1 << 16, (t, hkv, 128), dtype=np.uint16)
+    vh = rng.integers(0, 1 << 16, (t, hkv, 128), dtype=np.uint16)
+    pages = new_tokens // 16
+    total = num_seqs * pages + 3
+    table = rng.permutation(total)[:num_seqs * pages].reshape(num_seqs, pages).astype(np.int32)
+    table = np.concatenate([table, np.zeros((num_seqs, 1), np.int32)], axis=1)  # one spare entry
+    pool = torch.full((total, hkv, 2176), 0xA5, dtype=torch.uint8, device="cuda")
+    kvq.hbm_append_pattern(torch.from_numpy(kh.view(np.int16)).cuda(), torch.from_numpy(vh.view(np.int16)).cuda(),
+                           torch.from_numpy(table).cuda(), pool, new_tokens)
+    torch.cuda.synchronize()
+    got = pool.cpu().numpy()
+    want = np.full_like(got, 0xA5)
+    for which, src in ((0, kh), (1, vh)):
+        rows = src.view(np.uint8).reshape(num_seqs, pages, 16, hkv, 256)  # [b][page][slot][h][byte]
+        words = rows.reshape(num_seqs, pages, 16, hkv, 4, 4, 16)  # [..][i (64-byte piece)][g][16 bytes]
+        x = words[..., 0, :, :] ^ words[..., 1, :, :] ^ words[..., 2, :, :] ^ words[..., 3, :, :]  # [b][p][n][h][g][16]
+        for b in range(num_seqs):
+            for j in range(pages):
+                blk = want[table[b, j]]  # [h][2176]
+                for n in range(16):
+                    for g in range(4):
+                        off = 64 * n + 16 * g if which == 0 else 1024 + 256 * (n // 4) + 64 * g + 16 * (n % 4)
+                        blk[:, off:off + 16] = x[b, j, n, :, g]
+                    poff = (2048 if which == 0 else 2112) + 4 * n
+                    blk[:, poff:poff + 4] = x[b, j, n, :, 0, :4]
+    assert np.array_equal(got, want)
+
