@@ -690,9 +690,9 @@ __device__ __forceinline__ void process_page_mx_scaled(const PageData<1>& pg, in
 // MFMA's per-(column, K block) B scale cannot express, so it moves into the A side:
 // p~[h][t] = p[h][t] * 2^(E_v[t][group] - 127), one A operand per channel group.  p~ enters as
 // three e4m3 limbs (rows 8(h/2)+4(h%2)+t of the A tile, t = limb; row t = 3 stays zero), each with
-// one UE8M0 scale per 32 tokens: limb t is what the limbs before it left, scaled so that the
-// block's largest magnitude lands in [128, 256).  Three limbs keep ~12 bits of p~ relative to
-// its block maximum.  Per page, the wave stages the V codes transposed (channel-major nibbles)
+// one UE8M0 scale per 32 tokens: limb 0 scales the block's largest magnitude into [128, 256),
+// limb t > 0 is what the limbs before it left, at 2^-4 of the previous scale (a bound on that
+// remainder).  Three limbs keep ~11 bits of p~ relative to its block maximum.  Per page, the wave stages the V codes transposed (channel-major nibbles)
 // and the V exponents in LDS; every fourth page it updates the running maximum once for the four
 // pages, builds the limbs (lane 8h + 2g + kb: head h, channel group g, 32-token block kb) and
 // runs the four MFMAs.
@@ -803,14 +803,16 @@ __device__ __forceinline__ void scaled_flush(const float (&xs0)[4], const float 
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // limb 0's UE8M0 scale: 2^(floor(log2 m) - 7) for the block's largest magnitude m, which then
+  // scales into [128, 256), inside e4m3's range (448), so no element saturates.  A limb's rounding
+  // error is at most half an e4m3 step in the binade of that maximum, i.e. 8 in the scaled units,
+  // so the next limb's scale is 2^-4 of this one: its elements scale into (-128, 128)
+  float m = 0.0f;
 #pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    float m = 0.0f;
+  for (int i = 0; i < 32; ++i) m = fmaxf(m, v[i]);  // p~ >= 0
+  int sc = max((int)((__float_as_uint(m) >> 23) & 255u) - 7, 0);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
-    // UE8M0 scale 2^(floor(log2 m) - 7): the largest magnitude scales into [128, 256), inside
-    // e4m3's range (448), so no element saturates
-    const int sc = max((int)((__float_as_uint(m) >> 23) & 255u) - 7, 0);
+  for (int t = 0; t < 3; ++t, sc = max(sc - 4, 0)) {
     const float inv = ldexpf(1.0f, 127 - sc), scl = ldexpf(1.0f, sc - 127);
     uint32_t wd[8];
 #pragma unroll
@@ -819,10 +821,11 @@ __device__ __forceinline__ void scaled_flush(const float (&xs0)[4], const float 
       pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2] * inv, v[4 * w + 3] * inv, pk, true);
       wd[w] = (uint32_t)pk;
       if (t < 2) {
-        v[4 * w + 0] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(pk, 0), scl, v[4 * w + 0]);
-        v[4 * w + 1] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(pk, 1), scl, v[4 * w + 1]);
-        v[4 * w + 2] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(pk, 2), scl, v[4 * w + 2]);
-        v[4 * w + 3] = fmaf(-__builtin_amdgcn_cvt_f32_fp8(pk, 3), scl, v[4 * w + 3]);
+        const f32x2 d01 = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false), d23 = __builtin_amdgcn_cvt_pk_f32_fp8(pk, true);
+        v[4 * w + 0] = fmaf(-d01[0], scl, v[4 * w + 0]);
+        v[4 * w + 1] = fmaf(-d01[1], scl, v[4 * w + 1]);
+        v[4 * w + 2] = fmaf(-d23[0], scl, v[4 * w + 2]);
+        v[4 * w + 3] = fmaf(-d23[1], scl, v[4 * w + 3]);
       }
     }
     if (h < G) {
