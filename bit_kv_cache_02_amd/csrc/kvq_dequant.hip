@@ -88,6 +88,114 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   }
 }
 
+// INT4 pages rotated back with the Hadamard block b in {64, 128}: x = R (s c + z 1) =
+// (s / sqrt(b)) H c + z sqrt(b) e_0 per block (H_b 1 = b e_0 for the Sylvester matrix).  H c is a
+// product of integers, so it runs on the f16 matrix cores exactly: the codes enter as the fp16
+// subnormals c 2^-24 (a nibble mask), H as +-1, and the fp32 sums of at most 128 products of
+// 4-bit codes are exact.  v_mfma_f32_16x16x32_f16 with A = rows of H (16 output channels) and
+// B = 32 codes x 16 tokens: lane (n, q) of the B operand of step kb holds the 8 nibbles of code
+// row word 4q + kb of token n, i.e. input channels (4q + kb) + 16e, e = 0..7; the output leaves
+// lane (n, q) with output channels 16 tile + 4q .. +3 of token n (one 16-byte store).  With
+// input channel c = a + 16e (a < 16) and output channel j = n + 16 tile, H[j][c] =
+// (-1)^popc(n & a) (-1)^popc(tile & e) (b = 64: zero unless e / 4 == tile / 4, and tile & e
+// taken mod 4), so a lane's A operand for (tile, step) is one pattern over e per tile, negated
+// by the lane's sign (-1)^popc(n & (4q + kb)).  Waves 0, 1 take K (output tiles 0-3, 4-7),
+// waves 2, 3 take V.
+template <int HB>
+__global__ __launch_bounds__(256) void dequant_rot_i4_kernel(DequantParams p) {
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(thread_id() >> 6);
+  const int which = wave >> 1, upper = wave & 1;  // K | V; output tiles 4 upper .. 4 upper + 3
+  const int n = lane & 15, q = lane >> 4;
+  const int i = block_id_x() / p.hkv, h = block_id_x() % p.hkv;
+  const uint8_t* base = p.pool + ((int64_t)p.page_ids[i] * p.hkv + h) * kPageHeadBytes;
+
+  // ---- the code row words 4q .. 4q+3 of token n, and the token's parameters ----
+  uint32_t w[4];
+  if (which == 0) {
+    const u32x4 x = *(const u32x4*)(base + 64 * n + 16 * q);
+    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+  } else {
+    // V: byte s of row word 4q + r of token n sits at 1024 + 256 (n/4) + 64 q + 16 r + 4 s + n%4
+    const uint8_t* vb = base + kVCodesOff + 256 * (n >> 2) + 64 * q;
+    const uint32_t m = n & 3;
+    const uint32_t sel = 0x0C0C0000u | ((4u + m) << 8) | m;  // byte m of each of two words
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const u32x4 x = *(const u32x4*)(vb + 16 * r);
+      w[r] = perm(perm(x[3], x[2], sel), perm(x[1], x[0], sel), 0x05040100u);
+    }
+  }
+  const uint32_t pw = *(const uint32_t*)(base + (which ? kVParamsOff : kKParamsOff) + 4 * n);
+
+  // ---- B operands: nibble e of word 4q + kb -> element e, as c 2^-24 ----
+  f16x8 bop[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint32_t lo = w[kb] & 0x0F0F0F0Fu, hi = (w[kb] >> 4) & 0x0F0F0F0Fu;
+    bop[kb] = __builtin_bit_cast(f16x8, u32x4{perm(hi, lo, 0x0C040C00u), perm(hi, lo, 0x0C050C01u),
+                                               perm(hi, lo, 0x0C060C02u), perm(hi, lo, 0x0C070C03u)});
+  }
+
+  // ---- the products ----
+  f32x4 acc[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    // pattern over e of output tile 4 upper + tt (+1 0x3C00, -1 0xBC00, 0)
+    uint32_t pat[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const int e = 2 * d + hlf;
+        uint32_t v16;
+        if (HB == 128) {
+          const int par = (__builtin_popcount(tt & e) + (upper & (e >> 2))) & 1;
+          v16 = par ? 0xBC00u : 0x3C00u;
+        } else {
+          const bool same = (e >> 2) == upper;
+          v16 = same ? (((__builtin_popcount(tt & e & 3)) & 1) ? 0xBC00u : 0x3C00u) : 0u;
+        }
+        word |= v16 << (16 * hlf);
+      }
+      pat[d] = word;
+    }
+    acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t flip = (__builtin_popcount(n & (4 * q + kb)) & 1) ? 0x80008000u : 0u;
+      const f16x8 aop = __builtin_bit_cast(f16x8, u32x4{pat[0] ^ flip, pat[1] ^ flip, pat[2] ^ flip, pat[3] ^ flip});
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[kb], acc[tt], 0, 0, 0);
+    }
+  }
+
+  // ---- x = (s 2^24 / sqrt(b)) acc + z sqrt(b) at the first channel of each block; store ----
+  constexpr float kIsb = HB == 128 ? 0.08838834764831845f : 0.125f;
+  constexpr float kSb = HB == 128 ? 11.313708498984761f : 8.0f;
+  const float sc = f16_bits_to_f32(pw & 0xFFFFu) * (16777216.0f * kIsb);
+  const float zb = f16_bits_to_f32(pw >> 16) * kSb;
+  // the tiles go through LDS, so that the workgroup writes K and V as whole 512-byte token rows
+  // (16-byte stores straight from the tile layout cover 64-byte pieces 512 bytes apart: slower)
+  __shared__ __attribute__((aligned(16))) float buf[2][kPage][kHeadDim];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int tile = 4 * upper + tt;
+    // output channel 16 tile + 4q + r; the block's first channel: r = 0, q = 0 and tile 0 (b = 128)
+    // or tile 0, 4 (b = 64)
+    const bool first = q == 0 && (HB == 128 ? tile == 0 : (tile & 3) == 0);
+    *(f32x4*)&buf[which][n][16 * tile + 4 * q] =
+        f32x4{fmaf(acc[tt][0], sc, first ? zb : 0.0f), acc[tt][1] * sc, acc[tt][2] * sc, acc[tt][3] * sc};
+  }
+  __syncthreads();
+  const int64_t out_base = (int64_t)block_id_x() * kPage * kHeadDim;
+  const int tid = thread_id();
+  for (int k = tid; k < kPage * kHeadDim; k += 256) {
+    __builtin_nontemporal_store((&buf[0][0][0])[k], p.out_k + out_base + k);
+    __builtin_nontemporal_store((&buf[1][0][0])[k], p.out_v + out_base + k);
+  }
+}
+
 // Bandwidth probes.  Each workgroup streams one contiguous chunk of the buffer, 4 KiB per
 // wave-group step (256 lanes x 16 B), several steps' loads in flight before they are used:
 // whole DRAM rows are read while open, which a grid-stride walk (neighbouring kilobytes from
@@ -201,7 +309,12 @@ __global__ __launch_bounds__(256) void append_pattern_kernel(const uint8_t* __re
 }
 
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
-  if (p.unrotate)
+  const unsigned grid = (unsigned)((int64_t)p.n * p.hkv);
+  if (p.unrotate && p.fmt == 0 && p.had_block == 128)
+    hipLaunchKernelGGL(dequant_rot_i4_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
+  else if (p.unrotate && p.fmt == 0 && p.had_block == 64)
+    hipLaunchKernelGGL(dequant_rot_i4_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
+  else if (p.unrotate)
     hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)((int64_t)p.n * p.hkv)), dim3(256), 0, stream, p);

@@ -66,8 +66,9 @@ LEGS = {
     "decode_mxfp4_scaled": (r"decode_kernel<2, ", ("mxfp4_decode", "algorithmic_bytes"), DECODE_SRC,
                             "decode_source_sha256", "MXFP4 decode, both contractions on the scaled FP8 x FP4 "
                             "matrix cores (kvq_decode_attn, KVQ_MX_SCALED_MFMA)"),
-    "dequant_rotated": (r"dequant_kernel<true>", ("dequant_pages", "algorithmic_bytes"), DEQUANT_SRC,
-                        "dequant_source_sha256", "page dequantization rotated back (kvq_dequant_page)"),
+    "dequant_rotated": (r"dequant_rot_i4_kernel<128>", ("dequant_pages", "algorithmic_bytes"), DEQUANT_SRC,
+                        "dequant_source_sha256", "page dequantization rotated back, INT4 Hadamard 128 on the "
+                        "matrix cores (kvq_dequant_page)"),
     "dequant_plain": (r"dequant_kernel<false>", ("dequant_pages", "algorithmic_bytes"), DEQUANT_SRC,
                       "dequant_source_sha256", "page dequantization, rotated basis (kvq_dequant_page)"),
     "prefill_attention": (r"prefill_kernel<0>", ("prefill_attention", "kv_bytes_once"), PREFILL_SRC,
