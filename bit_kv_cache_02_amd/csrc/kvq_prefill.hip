@@ -237,25 +237,43 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       const int j = s_vj;
       const int ch = (j >> 2) + 32 * (j & 3);
       const uint32_t x = r.vc;
-      _Float16 vlo[4], vhi[4];
+      if constexpr (FMT == 0) {
+        // in packed fp16, tokens (0, 2) and (1, 3) of the quad per register: the codes c become
+        // exact fp16 values as (1024 + c) - 1024, and one packed fma rounds s c + z to fp16 once
+        uint32_t par[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const bool valid = blk * kBlk + key0 + rr < L;  // slots past the sequence: V taken as 0
-        if constexpr (FMT == 0) {
-          const uint32_t par = valid ? r.vp[rr] : 0u;
-          const float sv = f16_bits_to_f32(par & 0xFFFFu), zv = f16_bits_to_f32(par >> 16);
-          const uint32_t byte = (x >> (8 * rr)) & 255u;
-          vlo[rr] = (_Float16)fmaf(sv, (float)(byte & 15u), zv);
-          vhi[rr] = (_Float16)fmaf(sv, (float)(byte >> 4), zv);
-        } else {
+        for (int rr = 0; rr < 4; ++rr) par[rr] = blk * kBlk + key0 + rr < L ? r.vp[rr] : 0u;  // past L: V = 0
+        typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+        const h2 s02 = __builtin_bit_cast(h2, perm(par[2], par[0], 0x05040100u));
+        const h2 z02 = __builtin_bit_cast(h2, perm(par[2], par[0], 0x07060302u));
+        const h2 s13 = __builtin_bit_cast(h2, perm(par[3], par[1], 0x05040100u));
+        const h2 z13 = __builtin_bit_cast(h2, perm(par[3], par[1], 0x07060302u));
+        const h2 k1024 = __builtin_bit_cast(h2, 0x64006400u);
+        const uint32_t M = 0x000F000Fu, B = 0x64006400u;
+        const h2 clo02 = __builtin_bit_cast(h2, (x & M) | B) - k1024;
+        const h2 clo13 = __builtin_bit_cast(h2, ((x >> 8) & M) | B) - k1024;
+        const h2 chi02 = __builtin_bit_cast(h2, ((x >> 4) & M) | B) - k1024;
+        const h2 chi13 = __builtin_bit_cast(h2, ((x >> 12) & M) | B) - k1024;
+        const uint32_t vlo02 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(clo02, s02, z02));
+        const uint32_t vlo13 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(clo13, s13, z13));
+        const uint32_t vhi02 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(chi02, s02, z02));
+        const uint32_t vhi13 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(chi13, s13, z13));
+        // back to token order 0, 1, 2, 3
+        *(u32x2*)&st.vt[ch][vp0] = u32x2{perm(vlo13, vlo02, 0x05040100u), perm(vlo13, vlo02, 0x07060302u)};
+        *(u32x2*)&st.vt[ch + 16][vp0] = u32x2{perm(vhi13, vhi02, 0x05040100u), perm(vhi13, vhi02, 0x07060302u)};
+      } else {
+        _Float16 vlo[4], vhi[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const bool valid = blk * kBlk + key0 + rr < L;  // slots past the sequence: V taken as 0
           const float sc = valid ? ue8m0_scale(r.vp[rr], 8 * (j & 3)) : 0.0f;
           const f16x2 hv = cvt_fp4(x, sc, rr);
           vlo[rr] = hv[0];
           vhi[rr] = hv[1];
         }
+        *(f16x4*)&st.vt[ch][vp0] = f16x4{vlo[0], vlo[1], vlo[2], vlo[3]};
+        *(f16x4*)&st.vt[ch + 16][vp0] = f16x4{vhi[0], vhi[1], vhi[2], vhi[3]};
       }
-      *(f16x4*)&st.vt[ch][vp0] = f16x4{vlo[0], vlo[1], vlo[2], vlo[3]};
-      *(f16x4*)&st.vt[ch + 16][vp0] = f16x4{vhi[0], vhi[1], vhi[2], vhi[3]};
     }
   };
 
