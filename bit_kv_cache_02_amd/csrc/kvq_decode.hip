@@ -6,8 +6,8 @@
 // Per page (16 tokens x 128 channels, one 2176-byte page-head block) each wave does:
 //   scores   S[g][t] = sk_t * (q'_g . c_t) + zk_t * sum(q'_g)      (INT4: y^ = s*c + z)
 //            q'_g . c_t runs on v_mfma_i32_16x16x64_i8 straight on the 4-bit codes: q' is held as
-//            a 16-bit fixed-point number split into two int8 limbs (rows 2g, 2g+1 of the A tile),
-//            so the contraction is exact integer arithmetic;
+//            a 24-bit fixed-point number split into three int8 limbs (A-tile rows; layouts in
+//            kvq_attn.h), so the contraction is exact integer arithmetic;
 //   softmax  online, in the log2 domain; DPP row reductions over the 16 tokens;
 //   p.V      O'[g][ch] += sum_t (p_t sv_t) (c_t[ch] - 8) + sum_t p_t (zv_t + 8 sv_t)
 //            the first sum runs on v_mfma_f32_16x16x16_f16: the codes enter as the exact fp16

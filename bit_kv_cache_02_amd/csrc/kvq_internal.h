@@ -136,7 +136,7 @@ constexpr size_t kCounterUnits = 16384;
 size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int hkv, int group);
 void carve_workspace(void* ws, const DecodePlan& plan, int num_seqs, int hkv, int group, float** part_ml,
                      float** part_o, uint32_t** counters);
-// variant: 0 INT4, 1 MXFP4, 2 MXFP4 with q.K on the scaled FP8 x FP4 matrix cores
+// variant: 0 INT4, 1 MXFP4, 2 MXFP4 with q.K and p.V on the scaled FP8 x FP4 matrix cores
 hipError_t launch_decode(const DecodeParams& p, int variant, hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
 int prefill_tokens_per_tile(int group);

@@ -92,7 +92,7 @@ def _check_decode_workload(name, sample):
     q_t = torch.from_numpy(q).to(QDT[w.q_dtype])
     ref = oracle.decode_attention(pool_o, q_t.float().numpy(), lens, table, w.had_block, FMT[w.fmt],
                                   seqs=sample)
-    # MXFP4: also the path with q.K on the scaled FP8 x FP4 matrix cores
+    # MXFP4: also the path with both contractions on the scaled FP8 x FP4 matrix cores
     for scaled in ((False, True) if w.fmt == "mxfp4" else (False,)):
         out = kvq.decode_attn(cache, q_t.to(dev), torch.from_numpy(lens.astype(np.int32)).to(dev),
                               torch.from_numpy(table).to(dev), int(lens.max()), out_dtype=torch.float32,
