@@ -361,17 +361,23 @@ def time_prefill_append(dev, repeats=10):
         torch.cuda.synchronize()
         res[hb] = float(np.median([a.elapsed_time(b) for a, b in evs]) * 1e3)
         del pools
-    # the same traffic without the arithmetic (kvq_hbm_append_pattern), into the same kind of pools
+    # the same traffic without the arithmetic (kvq_hbm_append_pattern), into the same kind of pools:
+    # in the append's order, and one workgroup per page, on this workload's scattered pages and on
+    # the same pages in order
     pools = [torch.empty((num_pages, w.num_kv_heads, PAGE_HEAD), dtype=torch.uint8, device=dev) for _ in range(2)]
     new_tokens = int(lens[0])
-    settle(lambda: kvq.hbm_append_pattern(k, v, bt, pools[0], new_tokens), 0.1)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(repeats)]
-    for i in range(repeats):
-        evs[i][0].record()
-        kvq.hbm_append_pattern(k, v, bt, pools[i % 2], new_tokens)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    pattern_us = float(np.median([a.elapsed_time(b) for a, b in evs]) * 1e3)
+    bt_inorder = torch.arange(w.batch * table.shape[1], dtype=torch.int32, device=dev).reshape(table.shape)
+    bt_inorder = torch.minimum(bt_inorder, torch.tensor(num_pages - 1, dtype=torch.int32, device=dev))
+    pattern_us = {}
+    for name, order, tbl in (("own", 0, bt), ("page", 1, bt), ("page_in_order", 1, bt_inorder)):
+        settle(lambda: kvq.hbm_append_pattern(k, v, tbl, pools[0], new_tokens, order), 0.1)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(repeats)]
+        for i in range(repeats):
+            evs[i][0].record()
+            kvq.hbm_append_pattern(k, v, tbl, pools[i % 2], new_tokens, order)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        pattern_us[name] = float(np.median([a.elapsed_time(b) for a, b in evs]) * 1e3)
     del pools
     n_tok = int(lens.sum())
     nbytes = append_bytes(n_tok, w.num_kv_heads)
@@ -387,8 +393,10 @@ def time_prefill_append(dev, repeats=10):
         "tokens_per_s": round(n_tok / res[128] * 1e6, 1),
         "frac_of_hbm_peak": round(nbytes / res[128] / 1e3 / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes": nbytes,
-        "us_access_pattern_probe": round(pattern_us, 2),
-        "frac_of_access_pattern_probe": round(pattern_us / res[128], 4),
+        "us_access_pattern_probe": round(pattern_us["own"], 2),
+        "frac_of_access_pattern_probe": round(pattern_us["own"] / res[128], 4),
+        "us_access_pattern_probe_page_major": round(pattern_us["page"], 2),
+        "us_access_pattern_probe_page_major_pages_in_order": round(pattern_us["page_in_order"], 2),
     }
 
 

@@ -308,6 +308,36 @@ __global__ __launch_bounds__(256) void append_pattern_kernel(const uint8_t* __re
   }
 }
 
+// The same traffic in another order: one workgroup per (page, sequence) with one wave per (K|V,
+// kv head), so the workgroup reads the page's tokens of all kv heads (one contiguous run of
+// 16 token rows for K and one for V) and writes all of the page's head blocks.
+__global__ __launch_bounds__(1024) void append_pattern_page_kernel(const uint8_t* __restrict__ k,
+                                                                  const uint8_t* __restrict__ v,
+                                                                  const int32_t* __restrict__ block_table,
+                                                                  uint8_t* __restrict__ pool, int hkv,
+                                                                  int new_tokens, int max_pages) {
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(thread_id() >> 6);
+  if (wave >= 2 * hkv) return;
+  const int is_v = wave >= hkv;
+  const int h = is_v ? wave - hkv : wave;
+  const int b = block_id_y(), pg = block_id_x();
+  const int n = lane & 15, g = lane >> 4;
+  const int row_stride = hkv * kHeadDim * 2;
+  const uint8_t* src = (is_v ? v : k) + (((int64_t)b * new_tokens + pg * kPage) * hkv + h) * (kHeadDim * 2);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, kPage * row_stride);
+  u32x4 x = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    x ^= __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, n * row_stride + 16 * g + 64 * j, 0, 0));
+  const int page_id = block_table[(int64_t)b * max_pages + pg];
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(pool + ((int64_t)page_id * hkv + h) * (int64_t)kPageHeadBytes, kPageHeadBytes);
+  const int off = is_v ? kVCodesOff + 256 * (n >> 2) + 64 * g + 16 * (n & 3) : 64 * n + 16 * g;
+  __builtin_amdgcn_raw_buffer_store_b128(x, pr, off, 0, 2);
+  const int poff = g == 0 ? (is_v ? kVParamsOff : kKParamsOff) + 4 * n : attn::kOutOfRange;
+  __builtin_amdgcn_raw_buffer_store_b32(x[0], pr, poff, 0, 2);
+}
+
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)p.n * p.hkv);
   if (p.unrotate && p.fmt == 0 && p.had_block == 128)
@@ -357,8 +387,13 @@ hipError_t launch_fold4(const void* src, void* dst, size_t dst_bytes, hipStream_
 }
 
 hipError_t launch_append_pattern(const void* k, const void* v, const int32_t* block_table, void* pool, int hkv,
-                                 int num_seqs, int new_tokens, int max_pages, hipStream_t stream) {
+                                 int num_seqs, int new_tokens, int max_pages, int page_major, hipStream_t stream) {
   const int pages = new_tokens / kPage;
+  if (page_major) {
+    hipLaunchKernelGGL(append_pattern_page_kernel, dim3((unsigned)pages, (unsigned)num_seqs), dim3(1024), 0, stream,
+                       (const uint8_t*)k, (const uint8_t*)v, block_table, (uint8_t*)pool, hkv, new_tokens, max_pages);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((pages + kAppendPagesPerWave - 1) / kAppendPagesPerWave), (unsigned)num_seqs,
                   (unsigned)((2 * hkv + 3) / 4));
   hipLaunchKernelGGL(append_pattern_kernel, grid, dim3(256), 0, stream, (const uint8_t*)k, (const uint8_t*)v,

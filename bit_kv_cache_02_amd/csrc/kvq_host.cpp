@@ -493,7 +493,7 @@ int kvq_hbm_fold4(const void* src, void* dst, size_t dst_bytes, void* stream) {
 
 int kvq_hbm_append_pattern(const void* k, const void* v, int32_t num_kv_heads, int32_t num_seqs,
                            int32_t new_tokens, const int32_t* block_table, int32_t max_pages, void* pool,
-                           void* stream) {
+                           uint32_t order, void* stream) {
   g_last_error[0] = 0;
   if (!k || !v || !block_table || !pool) return fail(KVQ_ERR_INVALID_ARG, "k, v, block_table and pool must not be NULL");
   if ((((uintptr_t)k) | ((uintptr_t)v) | ((uintptr_t)pool)) & 15)
@@ -504,9 +504,11 @@ int kvq_hbm_append_pattern(const void* k, const void* v, int32_t num_kv_heads, i
   if (new_tokens < 0 || new_tokens % 16) return fail(KVQ_ERR_INVALID_ARG, "new_tokens must be a non-negative multiple of 16");
   if (max_pages < 0 || (int64_t)new_tokens > 16 * (int64_t)max_pages)
     return fail(KVQ_ERR_INVALID_ARG, "new_tokens must be at most 16 * max_pages");
+  if (order > 1) return fail(KVQ_ERR_INVALID_ARG, "order must be 0 or 1");
+  if (order == 1 && num_kv_heads > 8) return fail(KVQ_ERR_UNSUPPORTED, "order 1 takes at most 8 kv heads");
   if (num_seqs == 0 || new_tokens == 0) return KVQ_OK;
   return hip_status(kvq::launch_append_pattern(k, v, block_table, pool, num_kv_heads, num_seqs, new_tokens, max_pages,
-                                               (hipStream_t)stream),
+                                               (int)order, (hipStream_t)stream),
                     "kvq_hbm_append_pattern launch");
 }
 

@@ -74,7 +74,7 @@ SIGNATURES = [
     ("kvq_hbm_read", ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
     ("kvq_hbm_fold4", ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
     ("kvq_hbm_append_pattern", ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
-                                              ctypes.c_int32, _P, _P]),
+                                              ctypes.c_int32, _P, ctypes.c_uint32, _P]),
 ]
 
 
@@ -358,10 +358,10 @@ def hbm_fold4(src: torch.Tensor, dst: torch.Tensor):
 
 
 def hbm_append_pattern(k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor, pool: torch.Tensor,
-                       new_tokens: int):
+                       new_tokens: int, order: int = 0):
     """The append's memory traffic without its arithmetic (kvq_hbm_append_pattern): k, v
     [num_seqs * new_tokens][Hkv][128] 2-byte elements, block_table int32 [num_seqs][max_pages],
-    pool uint8 [pages][Hkv][2176]."""
+    pool uint8 [pages][Hkv][2176]; order 0 the append's own, 1 one workgroup per page."""
     for t, n in ((k, "k"), (v, "v"), (pool, "pool")):
         _require(t, n)
     _require(block_table, "block_table", torch.int32)
@@ -371,4 +371,4 @@ def hbm_append_pattern(k: torch.Tensor, v: torch.Tensor, block_table: torch.Tens
     if k.shape[0] != num_seqs * new_tokens:
         raise ValueError("k must hold num_seqs * new_tokens rows")
     _check(lib().kvq_hbm_append_pattern(_ptr(k), _ptr(v), k.shape[1], num_seqs, int(new_tokens), _ptr(block_table),
-                                        max_pages, _ptr(pool), _stream()), "kvq_hbm_append_pattern")
+                                        max_pages, _ptr(pool), int(order), _stream()), "kvq_hbm_append_pattern")

@@ -340,10 +340,14 @@ int kvq_hbm_fold4(const void* src, void* dst, size_t dst_bytes, void* stream);
  * (i = 0..3) of the row of token 16 j + n:  K: X at byte 64 n + 16 g of the page-head block
  * and its first 32-bit word at 2048 + 4 n (g = 0 only); V: X at 1024 + 256 (n / 4) + 64 g +
  * 16 (n % 4) and the first word at 2112 + 4 n.  Nothing else is written.
+ * order 0: the append's own order (one wave per (sequence, kv head, K|V) and run of 4 pages, four
+ * such waves per workgroup); order 1: one workgroup per (sequence, page) holding a wave per
+ * (K|V, kv head), which reads the page's token rows of all kv heads together and writes all of
+ * its head blocks (at most 8 kv heads, else KVQ_ERR_UNSUPPORTED).  Both write the same bytes.
  */
 int kvq_hbm_append_pattern(const void* k, const void* v, int32_t num_kv_heads, int32_t num_seqs,
                            int32_t new_tokens, const int32_t* block_table, int32_t max_pages, void* pool,
-                           void* stream);
+                           uint32_t order, void* stream);
 
 #ifdef __cplusplus
 }

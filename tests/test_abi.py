@@ -247,14 +247,16 @@ def test_dequant_and_copy_reject_bad_args():
     assert lib.kvq_hbm_fold4(FAKE, FAKE, 0, None) == kvq.KVQ_OK
     # the append-pattern probe: argument checks (no launch)
     ap = lib.kvq_hbm_append_pattern
-    assert ap(None, FAKE, 8, 1, 16, FAKE, 1, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
-    assert ap(FAKE, FAKE, 8, 1, 24, FAKE, 2, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG  # not a multiple of 16
-    assert ap(FAKE, FAKE, 8, 1, 48, FAKE, 2, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG  # beyond 16 * max_pages
-    assert ap(FAKE, FAKE, 0, 1, 16, FAKE, 1, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
-    assert ap(FAKE, FAKE, 1025, 1, 16, FAKE, 1, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
-    assert ap(ctypes.c_void_p(4096 + 8), FAKE, 8, 1, 16, FAKE, 1, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
-    assert ap(FAKE, FAKE, 8, 0, 16, FAKE, 1, FAKE, None) == kvq.KVQ_OK
-    assert ap(FAKE, FAKE, 8, 1, 0, FAKE, 1, FAKE, None) == kvq.KVQ_OK
+    assert ap(None, FAKE, 8, 1, 16, FAKE, 1, FAKE, 0, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert ap(FAKE, FAKE, 8, 1, 24, FAKE, 2, FAKE, 0, None) == kvq.KVQ_ERR_INVALID_ARG  # not a multiple of 16
+    assert ap(FAKE, FAKE, 8, 1, 48, FAKE, 2, FAKE, 0, None) == kvq.KVQ_ERR_INVALID_ARG  # beyond 16 * max_pages
+    assert ap(FAKE, FAKE, 0, 1, 16, FAKE, 1, FAKE, 0, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert ap(FAKE, FAKE, 1025, 1, 16, FAKE, 1, FAKE, 0, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert ap(ctypes.c_void_p(4096 + 8), FAKE, 8, 1, 16, FAKE, 1, FAKE, 0, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert ap(FAKE, FAKE, 8, 0, 16, FAKE, 1, FAKE, 0, None) == kvq.KVQ_OK
+    assert ap(FAKE, FAKE, 8, 1, 0, FAKE, 1, FAKE, 0, None) == kvq.KVQ_OK
+    assert ap(FAKE, FAKE, 8, 1, 16, FAKE, 1, FAKE, 2, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert ap(FAKE, FAKE, 9, 1, 16, FAKE, 1, FAKE, 1, None) == kvq.KVQ_ERR_UNSUPPORTED
 
 
 def test_python_layer_raises_typed_errors():

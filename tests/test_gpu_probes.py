@@ -67,11 +67,15 @@ def test_append_pattern_probe(hkv, num_seqs, new_tokens):
     total = num_seqs * pages + 3
     table = rng.permutation(total)[:num_seqs * pages].reshape(num_seqs, pages).astype(np.int32)
     table = np.concatenate([table, np.zeros((num_seqs, 1), np.int32)], axis=1)  # one spare entry
-    pool = torch.full((total, hkv, 2176), 0xA5, dtype=torch.uint8, device="cuda")
-    kvq.hbm_append_pattern(torch.from_numpy(kh.view(np.int16)).cuda(), torch.from_numpy(vh.view(np.int16)).cuda(),
-                           torch.from_numpy(table).cuda(), pool, new_tokens)
+    pools = []
+    for order in (0, 1):  # the append's order, one workgroup per page: the same bytes
+        pool = torch.full((total, hkv, 2176), 0xA5, dtype=torch.uint8, device="cuda")
+        kvq.hbm_append_pattern(torch.from_numpy(kh.view(np.int16)).cuda(), torch.from_numpy(vh.view(np.int16)).cuda(),
+                               torch.from_numpy(table).cuda(), pool, new_tokens, order)
+        pools.append(pool)
     torch.cuda.synchronize()
-    got = pool.cpu().numpy()
+    got = pools[0].cpu().numpy()
+    assert np.array_equal(pools[1].cpu().numpy(), got)
     want = np.full_like(got, 0xA5)
     for which, src in ((0, kh), (1, vh)):
         rows = src.view(np.uint8).reshape(num_seqs, pages, 16, hkv, 256)  # [b][page][slot][h][byte]
