@@ -89,7 +89,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
 }
 
 // INT4 pages rotated back with the Hadamard block b in {64, 128}: x = R (s c + z 1) =
-// (s / sqrt(b)) H c + z sqrt(b) e_0 per block (H_b 1 = b e_0 for the Sylvester matrix).  H c is a
+// (s / sqrt(b)) H c + z sqrt(b) e_0 per block (H_b 1 = b e_0 for the Sylvester matrix; the first
+// channel is taken with centred codes, below).  H c is a
 // product of integers, so it runs on the f16 matrix cores exactly: the codes enter as the fp16
 // subnormals c 2^-24 (a nibble mask), H as +-1, and the fp32 sums of at most 128 products of
 // 4-bit codes are exact.  v_mfma_f32_16x16x32_f16 with A = rows of H (16 output channels) and
@@ -173,8 +174,14 @@ __global__ __launch_bounds__(256) void dequant_rot_i4_kernel(DequantParams p) {
   // ---- x = (s 2^24 / sqrt(b)) acc + z sqrt(b) at the first channel of each block; store ----
   constexpr float kIsb = HB == 128 ? 0.08838834764831845f : 0.125f;
   constexpr float kSb = HB == 128 ? 11.313708498984761f : 8.0f;
-  const float sc = f16_bits_to_f32(pw & 0xFFFFu) * (16777216.0f * kIsb);
-  const float zb = f16_bits_to_f32(pw >> 16) * kSb;
+  // At a block's first channel the two terms are each about (s / sqrt(b)) sum(c), up to ~100 times
+  // the result, and would cancel in fp32.  With the codes centred, H (c - 8) = H c - 8 b e_0, that
+  // channel is (acc - 8 b 2^-24) s' + (z + 8 s) sqrt(b): the subtraction and z + 8 s are exact in
+  // fp32 (the first an integer times 2^-24 below 2^12, the second from two fp16 values).
+  const float s16 = f16_bits_to_f32(pw & 0xFFFFu);
+  const float sc = s16 * (16777216.0f * kIsb);
+  const float zb = (f16_bits_to_f32(pw >> 16) + 8.0f * s16) * kSb;
+  constexpr float k8b = 8.0f * HB / 16777216.0f;
   // the tiles go through LDS, so that the workgroup writes K and V as whole 512-byte token rows
   // (16-byte stores straight from the tile layout cover 64-byte pieces 512 bytes apart: slower)
   __shared__ __attribute__((aligned(16))) float buf[2][kPage][kHeadDim];
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(256) void dequant_rot_i4_kernel(DequantParams p) {
     // or tile 0, 4 (b = 64)
     const bool first = q == 0 && (HB == 128 ? tile == 0 : (tile & 3) == 0);
     *(f32x4*)&buf[which][n][16 * tile + 4 * q] =
-        f32x4{fmaf(acc[tt][0], sc, first ? zb : 0.0f), acc[tt][1] * sc, acc[tt][2] * sc, acc[tt][3] * sc};
+        f32x4{first ? fmaf(acc[tt][0] - k8b, sc, zb) : acc[tt][0] * sc, acc[tt][1] * sc, acc[tt][2] * sc, acc[tt][3] * sc};
   }
   __syncthreads();
   const int64_t out_base = (int64_t)block_id_x() * kPage * kHeadDim;

@@ -65,6 +65,17 @@ def test_degenerate_vectors_append_and_decode(fmt, hb):
     cache, pool_o, _ = run_append(f"limits/degenerate fmt{fmt} b{hb}", k, v, lens, [0], table, total, 1, hb,
                                   fmt, "bf16")
     run_decode(f"limits/degenerate decode fmt{fmt} b{hb}", pool_o, table, lens, 4, hb, fmt=fmt, seed=4)
+    # page dequantization of the same pages, rotated basis (exact) and rotated back (INT4 b = 64 / 128 on the
+    # matrix cores: a zero scale leaves only the zero point's share, z sqrt(b) at each block's first channel)
+    ids = np.unique(table[0, :2]).astype(np.int32)  # the two full pages of the 40 tokens
+    dcache = kvq.Cache(pool_o.shape[0], 1, hb, "int4" if fmt == oracle.FMT_INT4 else "mxfp4",
+                       pool=torch.from_numpy(pool_o).cuda())
+    for unrot in (False, True):
+        gk, gv = kvq.dequant_pages(dcache, torch.from_numpy(ids).cuda(), unrotate=unrot)
+        rk, rv = oracle.dequant_pages(pool_o, ids, hb, fmt, unrotate=unrot)
+        for got, ref in ((gk, rk), (gv, rv)):
+            got = got.cpu().numpy().astype(np.float64)
+            assert np.abs(got - ref).max() <= 1e-6 * max(np.abs(ref).max(), 1e-30), f"dequant unrotate={unrot}"
     # all-zero keys and values: uniform softmax, zero output
     z = np.zeros((16, 1, 128), np.float32)
     table0, total0 = ragged_table(rng, [16], [0])
