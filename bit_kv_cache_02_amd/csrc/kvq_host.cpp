@@ -74,6 +74,22 @@ bool debug_checks() {
   return e && e[0] && strcmp(e, "0") != 0;
 }
 
+// KVQ_LOG (environment, read on every call): one line per launching call on stderr with the
+// call's shape and the launch plan the library chose for it.
+bool log_on() {
+  const char* e = getenv("KVQ_LOG");
+  return e && e[0] && strcmp(e, "0") != 0;
+}
+
+void log_line(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  fputs("kvq: ", stderr);
+  vfprintf(stderr, fmt, ap);
+  fputc('\n', stderr);
+  va_end(ap);
+}
+
 int device_check(const kvq::CheckParams& c, void* stream, const char* what) {
   int code = 0, index = 0;
   const hipError_t e = kvq::run_check(c, (hipStream_t)stream, &code, &index);
@@ -209,6 +225,12 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t kv_
     c.num_pages = cache->num_pages;
     if (int st = device_check(c, stream, "kvq_append")) return st;
   }
+  if (log_on())
+    log_line("kvq_append: %d tokens, %d seqs, %d kv heads, max_new_tokens %d, had_block %d, format %d, "
+             "grid %d x %d x %d workgroups of 4 waves (%d pages per wave)",
+             num_tokens, num_seqs, cache->num_kv_heads, max_new_tokens, cache->had_block, cache->format,
+             ((max_new_tokens + 15) / 16 + 1 + kvq::kAppendPagesPerWave - 1) / kvq::kAppendPagesPerWave, num_seqs,
+             (2 * cache->num_kv_heads + 3) / 4, kvq::kAppendPagesPerWave);
   return hip_status(kvq::launch_append(p, kv_dtype == KVQ_BF16, cache->had_block, cache->format, (hipStream_t)stream),
                     "kvq_append launch");
 }
@@ -323,6 +345,12 @@ static int decode_common(const kvq_cache* cache, const void* knew, const void* v
   }
   // kernel variant 2: MXFP4 with q.K and p.V on the scaled matrix cores
   const int variant = (flags & KVQ_MX_SCALED_MFMA) ? 2 : cache->format;
+  if (log_on())
+    log_line("%s: %d seqs, %d q / %d kv heads, max_seq_len %d, variant %d (0 INT4, 1 MXFP4, 2 MXFP4 scaled), "
+             "%d waves, depth %d, %s, up to %d runs of at most %d pages per (sequence, kv head), %lld workgroups",
+             what, num_seqs, num_q_heads, cache->num_kv_heads, max_seq_len, variant, plan.waves, plan.depth,
+             plan.balanced ? "balanced cut" : "fixed splits", plan.nsplit, plan.pages_per_split,
+             (long long)num_seqs * cache->num_kv_heads * plan.nsplit);
   return hip_status(kvq::launch_decode(p, variant, (hipStream_t)stream), what);
 }
 
@@ -427,6 +455,11 @@ int kvq_prefill_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, flo
     c.num_pages = cache->num_pages;
     if (int st = device_check(c, stream, "kvq_prefill_attn")) return st;
   }
+  if (log_on())
+    log_line("kvq_prefill_attn: %d tokens, %d seqs, %d q / %d kv heads, max_q_len %d, format %d, %d tiles of %d "
+             "tokens, %lld workgroups of 8 waves",
+             num_tokens, num_seqs, num_q_heads, cache->num_kv_heads, max_q_len, cache->format, (int)tiles,
+             kvq::prefill_tokens_per_tile(group), (long long)num_seqs * cache->num_kv_heads * tiles);
   return hip_status(kvq::launch_prefill(p, cache->format, (hipStream_t)stream), "kvq_prefill_attn launch");
 }
 
@@ -461,6 +494,13 @@ int kvq_dequant_page(const kvq_cache* cache, const int32_t* page_ids, int32_t n,
     c.num_pages = cache->num_pages;
     if (int st = device_check(c, stream, "kvq_dequant_page")) return st;
   }
+  if (log_on())
+    log_line("kvq_dequant_page: %d pages, %d kv heads, format %d, had_block %d, %s, %lld workgroups", n,
+             cache->num_kv_heads, cache->format, cache->had_block,
+             !p.unrotate ? "rotated basis"
+                         : (p.fmt == 0 && (p.had_block == 64 || p.had_block == 128) ? "rotated back on the matrix cores"
+                                                                                    : "rotated back by butterfly"),
+             (long long)n * cache->num_kv_heads);
   return hip_status(kvq::launch_dequant(p, (hipStream_t)stream), "kvq_dequant_page launch");
 }
 

@@ -92,3 +92,25 @@ def test_append_pattern_probe(hkv, num_seqs, new_tokens):
                     blk[:, poff:poff + 4] = x[b, j, n, :, 0, :4]
     assert np.array_equal(got, want)
 
+
+
+def test_launch_plan_log(capfd, monkeypatch):
+    # KVQ_LOG=1: one line per launching call on stderr, with the plan the library chose
+    import oracle
+    from tests.test_gpu_decode import oracle_cache
+    rng = np.random.default_rng(91)
+    pool, table = oracle_cache(rng, [40, 1000], 2, 128)
+    cache = kvq.Cache(pool.shape[0], 2, 128, pool=torch.from_numpy(pool).cuda())
+    q = torch.randn((2, 8, 128), dtype=torch.bfloat16).cuda()
+    lens = torch.tensor([40, 1000], dtype=torch.int32).cuda()
+    bt = torch.from_numpy(table).cuda()
+    kvq.decode_attn(cache, q, lens, bt, 1000)
+    torch.cuda.synchronize()
+    assert "kvq:" not in capfd.readouterr().err  # silent by default
+    monkeypatch.setenv("KVQ_LOG", "1")
+    kvq.decode_attn(cache, q, lens, bt, 1000)
+    kvq.dequant_pages(cache, torch.from_numpy(table[0, :2].copy()).cuda(), unrotate=True)
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    assert "kvq: kvq_decode_attn launch: 2 seqs, 8 q / 2 kv heads, max_seq_len 1000, variant 0" in err
+    assert "kvq: kvq_dequant_page: 2 pages, 2 kv heads, format 0, had_block 128, rotated back on the matrix cores" in err
