@@ -25,8 +25,8 @@
 //                 in the order the score layout gives them (bits 2 and 3 of the key swapped), and V^
 //                 is laid out in LDS in that same order.
 // The pages of the block after next load into registers while a block is computed and the next
-// one staged; each page id is loaded one step before its page.  The low part of q'' stays in LDS
-// (its high part in registers), so that a wave fits two per SIMD.  Query rotation and the final
+// one staged; each page id is loaded one step before its page.  Both parts of q'' stay in
+// registers (they pass through LDS once, into the B-operand order).  Query rotation and the final
 // rotation back run in fp32 in registers, 16 rows of a wave at a time, through LDS.
 #include "kvq_attn.h"
 #include "kvq_device.h"
@@ -68,7 +68,7 @@ struct alignas(16) PrefillSmem {
     alignas(16) _Float16 qst[kWaves][kRows / 2][kHeadDim];    // prologue: q'' high parts of 16 rows per wave
     alignas(16) float orow[kWaves][kRows / 2][kHeadDim + 4];  // epilogue: 16 output rows per wave
   } u;
-  alignas(16) _Float16 qlo[kWaves][kRows][kKPitch];  // q'' low parts: [row][slot], read as B operands
+  alignas(16) _Float16 qlo[kWaves][kRows][kKPitch];  // prologue: q'' low parts [row][slot], B-operand order
 };
 
 // The global words one thread stages per block: one K code row word, one V code word, the V
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   //         parts in the B-operand order (16 rows at a time through LDS); row r is token
   //         tw0 + r/G, query head r%G; rows that belong to no token are zero ----
   const float c2 = a.sm_scale_log2;
-  f16x8 qh[8];
+  f16x8 qh[8], ql[8];
   float qsum = 0.0f;  // sum of the q'' actually used (INT4 zero points)
   {
     const int esz = __builtin_amdgcn_readfirstlane(a.q_dtype == DT_F32 ? 4 : (a.q_dtype == DT_E4M3 ? 1 : 2));
@@ -161,9 +161,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     }
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      const f16x8 lo = *(const f16x8*)&sm.qlo[wave][col][16 * kb + 8 * half];
+      ql[kb] = *(const f16x8*)&sm.qlo[wave][col][16 * kb + 8 * half];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qsum += (float)qh[kb][j] + (float)lo[j];
+      for (int j = 0; j < 8; ++j) qsum += (float)qh[kb][j] + (float)ql[kb][j];
     }
     qsum += xor_lane<32>(qsum, lane);
   }
@@ -311,20 +311,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     for (int i = 0; i < 16; ++i) s[i] = 0.0f;
     // the operands of step kb + 2 are read while step kb multiplies (three register sets), so the
     // LDS latency stays off the matrix cores' chain
-    f16x8 ka[3], ql[3];
+    f16x8 ka[3];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      ka[kb] = *(const f16x8*)&st.k[col][16 * kb + 8 * half];
-      ql[kb] = *(const f16x8*)&sm.qlo[wave][col][16 * kb + 8 * half];
-    }
+    for (int kb = 0; kb < 2; ++kb) ka[kb] = *(const f16x8*)&st.k[col][16 * kb + 8 * half];
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      if (kb + 2 < 8) {
-        ka[(kb + 2) % 3] = *(const f16x8*)&st.k[col][16 * (kb + 2) + 8 * half];
-        ql[(kb + 2) % 3] = *(const f16x8*)&sm.qlo[wave][col][16 * (kb + 2) + 8 * half];
-      }
+      if (kb + 2 < 8) ka[(kb + 2) % 3] = *(const f16x8*)&st.k[col][16 * (kb + 2) + 8 * half];
       s = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[kb % 3], qh[kb], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[kb % 3], ql[kb % 3], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[kb % 3], ql[kb], s, 0, 0, 0);
     }
     // register i holds key 8 (i/4) + 4 half + i%4 of the block, for row `col`; d[i] = S - m
     f32x16 d;
