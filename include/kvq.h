@@ -19,8 +19,10 @@
  *   - Pointers named as device pointers must point to device memory (hipMalloc / a torch
  *     CUDA tensor) owned by the caller; `cache` and scalars are host values.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only enqueued: the
- *     library never synchronizes, never allocates device memory and keeps no mutable
- *     global state, so calls are thread-safe; calls on one stream run in order.
+ *     library never synchronizes and never allocates device memory, and apart from two
+ *     documented exceptions (kvq_decode_step_noalloc's fixed scratch and the KVQ_DEBUG_CHECKS
+ *     verdict slot, one of each per device) it keeps no mutable global state, so calls are
+ *     thread-safe; calls on one stream run in order.
  *   - Host-side argument checks run before any HIP call and return a negative kvq_status;
  *     kvq_last_error() then names the argument.  Device-side data (token counts, sequence
  *     lengths, page ids) is trusted: out-of-range values are undefined behaviour -- except when
