@@ -221,11 +221,13 @@ __device__ __forceinline__ float raw_to_f32(uint32_t bits, int dt) {
   }
 }
 
+// Nontemporal: the outputs are not read again by the kernel that writes them (measured: the
+// llama decode step 25.60-25.63 -> 25.46-25.52 us in graph replays).
 __device__ __forceinline__ void store_elem(void* p, int64_t i, int dt, float x) {
   switch (dt) {
-    case DT_F16: ((uint16_t*)p)[i] = (uint16_t)f32_to_f16_bits(x); break;
-    case DT_BF16: ((uint16_t*)p)[i] = (uint16_t)f32_to_bf16_bits(x); break;
-    default: ((float*)p)[i] = x; break;
+    case DT_F16: __builtin_nontemporal_store((uint16_t)f32_to_f16_bits(x), (uint16_t*)p + i); break;
+    case DT_BF16: __builtin_nontemporal_store((uint16_t)f32_to_bf16_bits(x), (uint16_t*)p + i); break;
+    default: __builtin_nontemporal_store(x, (float*)p + i); break;
   }
 }
 
