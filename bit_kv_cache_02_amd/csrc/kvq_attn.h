@@ -314,12 +314,7 @@ __device__ __forceinline__ void rows_i4(const PageI4& u, int valid0, int valid1,
     const float mn0 = fmaxf(s.m0, pm0), mn1 = fmaxf(s.m1, pm1);
     const float f0 = __builtin_amdgcn_exp2f(s.m0 - mn0), f1 = __builtin_amdgcn_exp2f(s.m1 - mn1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      s.acc[i][0] *= f0;
-      s.acc[i][1] *= f0;
-      s.acc[i][2] *= f1;
-      s.acc[i][3] *= f1;
-    }
+    for (int i = 0; i < 8; ++i) s.acc[i] *= f32x4{f0, f0, f1, f1};
     s.l0 *= f0;
     s.l1 *= f1;
     s.pz0 *= f0;
@@ -621,12 +616,7 @@ __device__ __forceinline__ void softmax_pv_mx(const VTileMx& vt, f32x4 sc, int v
     const float mn0 = fmaxf(s.m0, pm0), mn1 = fmaxf(s.m1, pm1);
     const float f0 = __builtin_amdgcn_exp2f(s.m0 - mn0), f1 = __builtin_amdgcn_exp2f(s.m1 - mn1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      s.acc[i][0] *= f0;
-      s.acc[i][1] *= f0;
-      s.acc[i][2] *= f1;
-      s.acc[i][3] *= f1;
-    }
+    for (int i = 0; i < 8; ++i) s.acc[i] *= f32x4{f0, f0, f1, f1};
     s.l0 *= f0;
     s.l1 *= f1;
     s.m0 = mn0;
