@@ -248,7 +248,7 @@ __device__ __forceinline__ void merge_runs(const DecodeParams& a, int64_t s0, in
       }
       M = Mn;
     }
-    const float il = 1.0f / Ls;
+    const float il = __builtin_amdgcn_rcpf(Ls);  // Ls >= 1: 1 ulp
     store_head(a, O0 * il, O1 * il, b, kvh * G + g, lane);
   }
 }
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       Ls = fmaf(f, sm.wl[w][g], Ls);
     }
     if (pieces == 1) {
-      const float il = 1.0f / Ls;
+      const float il = __builtin_amdgcn_rcpf(Ls);  // Ls >= 1: 1 ulp
       store_head(a, O0 * il, O1 * il, b, kvh * G + g, lane);
     } else {
       float* po = a.part_o + (slot * G + g) * kHeadDim;
@@ -686,13 +686,12 @@ DecodePlan plan_decode(int num_seqs, int hkv, int max_seq_len) {
   if (env_w) W = env_w;
   if (env_p) P = env_p;
   if (eb) balanced = atoi(eb) != 0;
-  if (W != 4 && W != 8 && W != 16) W = 8;
+  if (W != 4 && W != 8) W = 8;
   // the cut runs one thread per sequence and counts pages in 32 bits
   if (balanced && (max_pg <= 0 || num_seqs > 64 * W || num_seqs > 256 || (int64_t)num_seqs * max_pg >= (1 << 30)))
     balanced = false;
   int D = env_d ? env_d : (balanced ? 2 : 3);
   if (D != 2 && D != 3 && D != 4) D = 3;
-  if (W == 16) D = 2;  // register budget of 1024-thread workgroups
   if (P > 64 * W) P = 64 * W;
   if (P < 1) P = 1;
   plan.waves = W;
@@ -763,13 +762,10 @@ hipError_t launch_decode(const DecodeParams& p, int variant, hipStream_t stream)
   } else
   KVQ_DECODE_CASE(0, 4, 2, 1) KVQ_DECODE_CASE(0, 4, 3, 1) KVQ_DECODE_CASE(0, 4, 4, 1)
   KVQ_DECODE_CASE(0, 8, 2, 1) KVQ_DECODE_CASE(0, 8, 3, 1) KVQ_DECODE_CASE(0, 8, 4, 1)
-  KVQ_DECODE_CASE(0, 16, 2, 1)
   KVQ_DECODE_CASE(0, 4, 2, 2) KVQ_DECODE_CASE(0, 4, 3, 2) KVQ_DECODE_CASE(0, 4, 4, 2)
   KVQ_DECODE_CASE(0, 8, 2, 2) KVQ_DECODE_CASE(0, 8, 3, 2) KVQ_DECODE_CASE(0, 8, 4, 2)
-  KVQ_DECODE_CASE(0, 16, 2, 2)
   KVQ_DECODE_CASE(1, 4, 2, 2) KVQ_DECODE_CASE(1, 4, 3, 2) KVQ_DECODE_CASE(1, 4, 4, 2)
   KVQ_DECODE_CASE(1, 8, 2, 2) KVQ_DECODE_CASE(1, 8, 3, 2) KVQ_DECODE_CASE(1, 8, 4, 2)
-  KVQ_DECODE_CASE(1, 16, 2, 2)
   KVQ_DECODE_CASE(2, 4, 3, 2) KVQ_DECODE_CASE(2, 8, 3, 2) { return hipErrorInvalidValue; }
 #undef KVQ_DECODE_CASE
   return hipGetLastError();

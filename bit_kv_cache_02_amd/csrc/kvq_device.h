@@ -79,8 +79,11 @@ __device__ __forceinline__ float xor_lane(float v, int lane) {
   else if constexpr (M == 2) return __int_as_float(dpp_i<0x4E, 0xF>(0, x));   // quad_perm [2,3,0,1]
   else if constexpr (M == 4) return __int_as_float(dpp_i<0x114, 0xA>(dpp_i<0x104, 0x5>(0, x), x));  // row_shl/shr:4
   else if constexpr (M == 8) return __int_as_float(dpp_i<0x128, 0xF>(0, x));  // row_ror:8
-  else if constexpr (M == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x401F));  // xor 16 in 32
-  else {
+  else if constexpr (M == 16) {
+    // swap: the odd 16-lane rows of the first copy take the even rows of the second, and back
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return __int_as_float((lane & 16) ? (int)r[0] : (int)r[1]);
+  } else {
     static_assert(M == 32, "lane exchange distance");
     // swap: lanes 32..63 of the first copy take lanes 0..31 of the second, and back
     const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
