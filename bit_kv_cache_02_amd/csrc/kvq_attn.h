@@ -167,9 +167,13 @@ __device__ __forceinline__ PageData<FMT> load_page(const uint8_t* base, bool liv
   return d;
 }
 
-// 2^(E-127) for the UE8M0 byte E at bit `shift` of w (E = 0 gives 0: an all-zero or sub-2^-125 group)
-__device__ __forceinline__ float ue8m0_scale(uint32_t w, int shift) {
-  return __uint_as_float(((w >> shift) & 0xFFu) << 23);
+// 2^(E-127) for the UE8M0 byte E at bit `shift` of w (E = 0 gives 0: an all-zero or sub-2^-125 group):
+// E moved into the fp32 exponent field.  e8sh is that field's position, 23, passed in as a kernel
+// argument: with the amount unknown at compile time the byte extraction stays a byte-select
+// operand of the one shift instruction, instead of being rewritten into a shift and a mask (two
+// instructions for three of the four bytes).
+__device__ __forceinline__ float ue8m0_scale(uint32_t w, int shift, int e8sh) {
+  return __uint_as_float(((w >> shift) & 0xFFu) << e8sh);
 }
 
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
@@ -457,14 +461,14 @@ struct KTileMx {
   f16x8 kb[4];
 };
 
-__device__ __forceinline__ KTileMx unpack_k_mx(const PageData<1>& pg) {
+__device__ __forceinline__ KTileMx unpack_k_mx(const PageData<1>& pg, int e8sh) {
   KTileMx t;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const uint32_t w = pg.k[kk];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const f16x2 h2 = cvt_fp4(w, ue8m0_scale(pg.kp, 8 * q), q);
+      const f16x2 h2 = cvt_fp4(w, ue8m0_scale(pg.kp, 8 * q, e8sh), q);
       t.kb[kk][2 * q] = h2[0];
       t.kb[kk][2 * q + 1] = h2[1];
     }
@@ -487,7 +491,7 @@ struct VTileMx {
   f16x4 blo[4], bhi[4];
 };
 
-__device__ __forceinline__ VTileMx unpack_v_mx(const PageData<1>& pg, int vlimit, int jg) {
+__device__ __forceinline__ VTileMx unpack_v_mx(const PageData<1>& pg, int vlimit, int jg, int e8sh) {
   VTileMx t;
   uint32_t vw[4];  // the scale words of tokens 4jg .. 4jg+3, zero past the sequence's end
 #pragma unroll
@@ -497,7 +501,7 @@ __device__ __forceinline__ VTileMx unpack_v_mx(const PageData<1>& pg, int vlimit
     const uint32_t Y = pg.v[q];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const f16x2 h2 = cvt_fp4(Y, ue8m0_scale(vw[r], 8 * q), r);
+      const f16x2 h2 = cvt_fp4(Y, ue8m0_scale(vw[r], 8 * q, e8sh), r);
       t.blo[q][r] = h2[0];
       t.bhi[q][r] = h2[1];
     }
@@ -654,17 +658,9 @@ __device__ __forceinline__ void softmax_pv_mx(const VTileMx& vt, f32x4 sc, int v
 
 __device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid0, int valid1, int vlimit,
                                                 WaveState& s, const f16x8 (&qh)[4], float c2, bool has0, bool has1,
-                                                int n, int jg, bool a_row_used, _Float16 (*ptile)[kPage]) {
-  softmax_pv_mx(unpack_v_mx(pg, vlimit, jg), scores_mx(unpack_k_mx(pg), qh), valid0, valid1, s, c2, has0, has1, n,
-                jg, a_row_used, ptile);
-}
-
-__device__ __forceinline__ void process_page_mx_scaled(const PageData<1>& pg, int valid0, int valid1, int vlimit,
-                                                       WaveState& s, const i32x8 (&qa8)[2], const int (&qsa)[2],
-                                                       float c2, bool has0, bool has1, int n, int jg,
-                                                       bool a_row_used, _Float16 (*ptile)[kPage]) {
-  softmax_pv_mx(unpack_v_mx(pg, vlimit, jg), scores_mx_scaled(pg, qa8, qsa, jg), valid0, valid1, s, c2, has0, has1,
-                n, jg, a_row_used, ptile);
+                                                int n, int jg, bool a_row_used, _Float16 (*ptile)[kPage], int e8sh) {
+  softmax_pv_mx(unpack_v_mx(pg, vlimit, jg, e8sh), scores_mx(unpack_k_mx(pg, e8sh), qh), valid0, valid1, s, c2, has0,
+                has1, n, jg, a_row_used, ptile);
 }
 
 // p.V of an MXFP4 cache on the scaled matrix cores as well (UltraQuant article, section on how

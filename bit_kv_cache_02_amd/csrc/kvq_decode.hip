@@ -559,7 +559,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
                        has0, has1, n, jg, a_row_used, sm.ptile[wave]);
         else if constexpr (FMT == 1)
           process_page_mx(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, valid0 - i * W * kPage, s, qh, c2,
-                          has0, has1, n, jg, a_row_used, sm.ptile[wave]);
+                          has0, has1, n, jg, a_row_used, sm.ptile[wave], a.e8_shift);
         else
           scaled_stage_page(st[d], valid0 - i * W * kPage, qa8, qsa, c2, n, jg, d, sm.wb[wave].st, xs0[d], xs1[d]);
       } else if constexpr (FMT == 2) {

@@ -326,6 +326,7 @@ static int decode_common(const kvq_cache* cache, const void* knew, const void* v
   p.out_rotated = (flags & KVQ_OUT_ROTATED) ? 1 : 0;
   p.q_scale = q_scale;
   p.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  p.e8_shift = 23;
   p.knew = (const uint8_t*)knew;
   p.vnew = (const uint8_t*)vnew;
   p.kv_dtype = append ? kv_dtype : KVQ_BF16;
@@ -440,6 +441,7 @@ int kvq_prefill_attn(const kvq_cache* cache, const void* q, int32_t q_dtype, flo
   p.tiles = (int32_t)tiles;
   p.q_scale = q_scale;
   p.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  p.e8_shift = 23;
   if (debug_checks()) {
     kvq::CheckParams c;
     memset(&c, 0, sizeof(c));

@@ -59,6 +59,7 @@ struct DecodeParams {
   int32_t out_rotated;
   float q_scale;
   float sm_scale_log2;  // sm_scale * log2(e)
+  int32_t e8_shift;     // 23: see ue8m0_scale
   // fused step (append != 0): token seq_lens[b]-1 of every sequence is appended from
   // knew/vnew [num_seqs][hkv][128] (kv_dtype F16 or BF16) before it is attended
   const uint8_t* knew;
@@ -90,6 +91,7 @@ struct PrefillParams {
   int32_t tiles;             // query tiles per (sequence, kv head)
   float q_scale;
   float sm_scale_log2;
+  int32_t e8_shift;          // 23: see ue8m0_scale
 };
 
 struct DequantParams {

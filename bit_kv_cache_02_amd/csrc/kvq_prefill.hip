@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       } else {
         // byte q holds channel group q: its two e2m1 codes times 2^(E_q - 127)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = __builtin_bit_cast(uint32_t, cvt_fp4(x, ue8m0_scale(r.kp, 8 * q), q));
+        for (int q = 0; q < 4; ++q) o[q] = __builtin_bit_cast(uint32_t, cvt_fp4(x, ue8m0_scale(r.kp, 8 * q, a.e8_shift), q));
       }
       *(u32x4*)&st.k[key][8 * s_kw] = u32x4{o[0], o[1], o[2], o[3]};
       if constexpr (FMT == 0) {
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const bool valid = blk * kBlk + key0 + rr < L;  // slots past the sequence: V taken as 0
-          const float sc = valid ? ue8m0_scale(r.vp[rr], 8 * (j & 3)) : 0.0f;
+          const float sc = valid ? ue8m0_scale(r.vp[rr], 8 * (j & 3), a.e8_shift) : 0.0f;
           const f16x2 hv = cvt_fp4(x, sc, rr);
           vlo[rr] = hv[0];
           vhi[rr] = hv[1];
