@@ -336,6 +336,9 @@ def time_mxfp4_decode(dev, repeats=40):
     nbytes = int(lens.sum()) * w.num_kv_heads * 136 + w.batch * w.num_q_heads * 128 * 3 + \
         int(sum(-(-int(n) // 16) for n in lens)) * 4 + w.batch * 4
     f16_us, sc_us = float(np.mean(times[False])), float(np.mean(times[True]))
+    # its page stream without the arithmetic, in its plan (4 waves, depth 3, 256-page splits)
+    pat_us = time_decode_pattern([c.pool for c in caches], w.num_kv_heads, bt, int(lens[0]) // 16, 4, 3, 256,
+                                 launches=8, repeats=repeats)
     del caches
     return {
         "workload": "MXFP4 decode: 64 seqs x context 16384, 64 q / 8 kv heads, fp8 e4m3 queries, e2m1 + "
@@ -347,6 +350,8 @@ def time_mxfp4_decode(dev, repeats=40):
         "frac_of_hbm_peak": round(nbytes / f16_us / 1e3 / HBM_PEAK_GBPS, 4),
         "GBps_scaled_mfma": round(nbytes / sc_us / 1e3, 1),
         "algorithmic_bytes": nbytes,
+        "us_access_pattern_probe": round(pat_us, 2),
+        "frac_of_access_pattern_probe": round(pat_us / f16_us, 4),
     }
 
 
@@ -545,6 +550,39 @@ def hbm_read_probe(dev, window=1 << 30, buf_bytes=1 << 30, repeats=20):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (replays * len(views))
     return window / us / 1e3
+
+
+def time_decode_pattern(pools, hkv, bt, pages_per_seq, waves, depth, pages_per_split, launches=8, repeats=40):
+    """The decode's page stream without its arithmetic (kvq_hbm_decode_pattern) on the same pools
+    and block table, in the decode's plan: us per launch, launches cycling over the pools in a
+    HIP graph of `launches` (as the decode legs are timed)."""
+    sink = kvq.hbm_decode_pattern(pools[0], hkv, bt, pages_per_seq, waves, depth, pages_per_split)
+    torch.cuda.synchronize()
+
+    def run():
+        for i in range(launches):
+            kvq.hbm_decode_pattern(pools[i % len(pools)], hkv, bt, pages_per_seq, waves, depth, pages_per_split, sink)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    settle(g.replay)
+    replays = max(1, -(-repeats // launches))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / (replays * launches)
 
 
 def cpu_baseline(w, budget_s=12.0, n_seqs=4):
@@ -786,6 +824,13 @@ def main():
     # the same probe at one step's byte count per launch (its launch and drain included)
     res["hbm_read_GBps_at_step_bytes"] = round(hbm_read_probe(dev, window=step_bytes, repeats=56), 1)
     res["step_frac_of_read_bw_at_step_bytes"] = round(achieved / res["hbm_read_GBps_at_step_bytes"], 4)
+    # the step's page stream without its arithmetic, in the step's plan (8 waves, depth 3, one split)
+    log("[bench] decode access-pattern probe")
+    pat_us = time_decode_pattern([c.pool for c in caches], w.num_kv_heads, step["bt"], int(lens[0]) // 16, 8, 3, 512,
+                                 launches=len(caches), repeats=56)
+    page_bytes = int(lens.sum()) * w.num_kv_heads * 136
+    res["decode_pattern_probe"] = {"us": round(pat_us, 3), "GBps": round(page_bytes / pat_us / 1e3, 1),
+                                   "step_frac_of_probe": round(pat_us / step_us, 4)}
     log("[bench] HBM 4:1 read:write probe")
     res["hbm_fold4_GBps"] = round(hbm_fold4_probe(dev), 1)
     log("[bench] page dequantization")

@@ -345,6 +345,70 @@ __global__ __launch_bounds__(1024) void append_pattern_page_kernel(const uint8_t
   __builtin_amdgcn_raw_buffer_store_b32(x[0], pr, poff, 0, 2);
 }
 
+// The decode's page stream without its arithmetic: the grid (a workgroup per (sequence, kv head,
+// split) in split-major order), W waves with the pages dealt round-robin (wave w takes pages
+// p_begin + w + W i), each lane's page loads (K row bytes 64 n + 16 g, V words 1024 + 16 l, the K
+// and V parameter words of token n; n = l % 16, g = l / 16), the buffer descriptors, nontemporal
+// policy and prefetch depth D of decode_kernel, for sequences of pages_per_seq full pages.  Each
+// lane adds up the 32-bit words it loaded (mod 2^32); wave w of workgroup j stores the sum over
+// its lanes at sink[W j + w].
+template <int W, int D>
+__global__ __launch_bounds__(W * 64) void decode_pattern_kernel(const uint8_t* __restrict__ pool,
+                                                                const int32_t* __restrict__ block_table, int hkv,
+                                                                int num_seqs, int pages_per_seq, int max_pages,
+                                                                int pages_per_split, uint32_t* __restrict__ sink) {
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(thread_id() >> 6);
+  const int units = num_seqs * hkv;
+  const int split = block_id_x() / units, unit = block_id_x() % units;
+  const int kvh = unit % hkv, b = unit / hkv;
+  const int p_begin = split * pages_per_split;
+  const int p_end = min(p_begin + pages_per_split, pages_per_seq);
+  const int pw0 = p_begin + wave;
+  const int npw = max(0, (p_end - pw0 + W - 1) / W);  // <= 64: pages_per_split <= 64 W
+  const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(block_table + (int64_t)b * max_pages, max_pages * 4);
+  const int pid_vec =
+      (int)__builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, lane < npw ? 4 * (pw0 + W * lane) : attn::kOutOfRange, 0, 0);
+  const uint8_t* pool_h = pool + (int64_t)kvh * kPageHeadBytes;
+  const int64_t page_stride = (int64_t)hkv * kPageHeadBytes;
+  const int n = lane & 15, g = lane >> 4;
+  const int koff = 64 * n + 16 * g, voff = kVCodesOff + 16 * lane, poff = 4 * n;
+  struct Words {
+    u32x4 k, v;
+    uint32_t kp, vp;
+  };
+  // page i of the wave (past its last: out-of-range offsets, the loads return zeros)
+  auto load = [&](int i) {
+    const uint64_t addr = (uint64_t)(pool_h + (int64_t)__builtin_amdgcn_readlane(pid_vec, min(i, 63)) * page_stride);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((const uint8_t*)(((uint64_t)hi << 32) | lo), kPageHeadBytes);
+    const bool live = i < npw;
+    Words d;
+    d.k = __builtin_amdgcn_raw_buffer_load_b128(r, live ? koff : attn::kOutOfRange, 0, 2);
+    d.v = __builtin_amdgcn_raw_buffer_load_b128(r, live ? voff : attn::kOutOfRange, 0, 2);
+    d.kp = __builtin_amdgcn_raw_buffer_load_b32(r, live ? poff : attn::kOutOfRange, kKParamsOff, 2);
+    d.vp = __builtin_amdgcn_raw_buffer_load_b32(r, live ? poff : attn::kOutOfRange, kVParamsOff, 2);
+    return d;
+  };
+  constexpr int NB = D + 1;
+  Words st[NB];
+#pragma unroll
+  for (int d = 0; d < D; ++d) st[d] = load(d);
+  uint32_t acc = 0u;
+  for (int i0 = 0; i0 < npw; i0 += NB) {
+#pragma unroll
+    for (int d = 0; d < NB; ++d) {
+      st[(d + D) % NB] = load(i0 + d + D);
+      const Words& w = st[d];
+      acc += w.k[0] + w.k[1] + w.k[2] + w.k[3] + w.v[0] + w.v[1] + w.v[2] + w.v[3] + w.kp + w.vp;
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += (uint32_t)__shfl_xor((int)acc, m, 64);
+  if (lane == 0) sink[(int64_t)W * block_id_x() + wave] = acc;
+}
+
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)p.n * p.hkv);
   if (p.unrotate && p.fmt == 0 && p.had_block == 128)
@@ -405,6 +469,22 @@ hipError_t launch_append_pattern(const void* k, const void* v, const int32_t* bl
                   (unsigned)((2 * hkv + 3) / 4));
   hipLaunchKernelGGL(append_pattern_kernel, grid, dim3(256), 0, stream, (const uint8_t*)k, (const uint8_t*)v,
                      block_table, (uint8_t*)pool, hkv, new_tokens, max_pages);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_pattern(const void* pool, const int32_t* block_table, int hkv, int num_seqs,
+                                 int pages_per_seq, int max_pages, int waves, int depth, int pages_per_split,
+                                 uint32_t* sink, hipStream_t stream) {
+  const int nsplit = (pages_per_seq + pages_per_split - 1) / pages_per_split;
+  const dim3 grid((unsigned)((int64_t)num_seqs * hkv * nsplit));
+#define KVQ_PATTERN_CASE(WV, DV)                                                                        \
+  if (waves == WV && depth == DV) {                                                                     \
+    hipLaunchKernelGGL((decode_pattern_kernel<WV, DV>), grid, dim3(WV * 64), 0, stream, (const uint8_t*)pool, \
+                       block_table, hkv, num_seqs, pages_per_seq, max_pages, pages_per_split, sink);     \
+  } else
+  KVQ_PATTERN_CASE(4, 2) KVQ_PATTERN_CASE(4, 3) KVQ_PATTERN_CASE(4, 4)
+  KVQ_PATTERN_CASE(8, 2) KVQ_PATTERN_CASE(8, 3) KVQ_PATTERN_CASE(8, 4) { return hipErrorInvalidValue; }
+#undef KVQ_PATTERN_CASE
   return hipGetLastError();
 }
 

@@ -554,4 +554,28 @@ int kvq_hbm_append_pattern(const void* k, const void* v, int32_t num_kv_heads, i
                     "kvq_hbm_append_pattern launch");
 }
 
+int kvq_hbm_decode_pattern(const void* pool, int32_t num_kv_heads, int32_t num_seqs, int32_t pages_per_seq,
+                           const int32_t* block_table, int32_t max_pages, int32_t waves, int32_t depth,
+                           int32_t pages_per_split, uint32_t* sink, void* stream) {
+  g_last_error[0] = 0;
+  if (!pool || !block_table || !sink) return fail(KVQ_ERR_INVALID_ARG, "pool, block_table and sink must not be NULL");
+  if ((uintptr_t)pool & 15) return fail(KVQ_ERR_INVALID_ARG, "pool must be 16-byte aligned");
+  if ((((uintptr_t)block_table) | ((uintptr_t)sink)) & 3)
+    return fail(KVQ_ERR_INVALID_ARG, "block_table and sink must be 4-byte aligned");
+  if (num_kv_heads < 1 || num_kv_heads > 1024) return fail(KVQ_ERR_INVALID_ARG, "num_kv_heads must be in [1, 1024]");
+  if (num_seqs < 0) return fail(KVQ_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (pages_per_seq < 1 || pages_per_seq > max_pages)
+    return fail(KVQ_ERR_INVALID_ARG, "pages_per_seq must be in [1, max_pages]");
+  if (waves != 4 && waves != 8) return fail(KVQ_ERR_INVALID_ARG, "waves must be 4 or 8");
+  if (depth < 2 || depth > 4) return fail(KVQ_ERR_INVALID_ARG, "depth must be 2, 3 or 4");
+  if (pages_per_split < 1 || pages_per_split > 64 * waves)
+    return fail(KVQ_ERR_INVALID_ARG, "pages_per_split must be in [1, 64 * waves]");
+  const int64_t grid = (int64_t)num_seqs * num_kv_heads * ((pages_per_seq + pages_per_split - 1) / pages_per_split);
+  if (grid > 0x7FFFFFFF) return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
+  if (num_seqs == 0) return KVQ_OK;
+  return hip_status(kvq::launch_decode_pattern(pool, block_table, num_kv_heads, num_seqs, pages_per_seq, max_pages,
+                                               waves, depth, pages_per_split, sink, (hipStream_t)stream),
+                    "kvq_hbm_decode_pattern launch");
+}
+
 }  // extern "C"

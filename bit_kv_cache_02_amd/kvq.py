@@ -75,6 +75,8 @@ SIGNATURES = [
     ("kvq_hbm_fold4", ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
     ("kvq_hbm_append_pattern", ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
                                               ctypes.c_int32, _P, ctypes.c_uint32, _P]),
+    ("kvq_hbm_decode_pattern", ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]),
 ]
 
 
@@ -372,3 +374,24 @@ def hbm_append_pattern(k: torch.Tensor, v: torch.Tensor, block_table: torch.Tens
         raise ValueError("k must hold num_seqs * new_tokens rows")
     _check(lib().kvq_hbm_append_pattern(_ptr(k), _ptr(v), k.shape[1], num_seqs, int(new_tokens), _ptr(block_table),
                                         max_pages, _ptr(pool), int(order), _stream()), "kvq_hbm_append_pattern")
+
+
+def hbm_decode_pattern(pool: torch.Tensor, num_kv_heads: int, block_table: torch.Tensor, pages_per_seq: int,
+                       waves: int, depth: int, pages_per_split: int, sink: torch.Tensor = None) -> torch.Tensor:
+    """The decode's page stream without its arithmetic (kvq_hbm_decode_pattern): pool uint8,
+    block_table int32 [num_seqs][max_pages], every sequence pages_per_seq full pages; returns the
+    uint32 sink, one word per wave (the sum of the words its lanes loaded)."""
+    _require(pool, "pool")
+    _require(block_table, "block_table", torch.int32)
+    num_seqs, max_pages = block_table.shape
+    nsplit = -(-int(pages_per_seq) // int(pages_per_split))
+    words = num_seqs * num_kv_heads * nsplit * waves
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=pool.device)
+    _require(sink, "sink", torch.int32)
+    if sink.numel() < words:
+        raise ValueError(f"sink must hold {words} words")
+    _check(lib().kvq_hbm_decode_pattern(_ptr(pool), int(num_kv_heads), num_seqs, int(pages_per_seq),
+                                        _ptr(block_table), max_pages, int(waves), int(depth), int(pages_per_split),
+                                        _ptr(sink), _stream()), "kvq_hbm_decode_pattern")
+    return sink

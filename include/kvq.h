@@ -351,6 +351,28 @@ int kvq_hbm_append_pattern(const void* k, const void* v, int32_t num_kv_heads, i
                            int32_t new_tokens, const int32_t* block_table, int32_t max_pages, void* pool,
                            uint32_t order, void* stream);
 
+/*
+ * kvq_hbm_decode_pattern -- the memory traffic of the decode's page stream without its arithmetic.
+ * Not part of the method: it measures what the decode's access pattern allows (page-head blocks
+ * gathered through the block table, each kv head's 17 KiB apart), with the workgroups, waves,
+ * lane map, prefetch depth and cache policy of kvq_decode_attn's fixed-split plan.
+ * pool: device [pages][num_kv_heads][2176] (only read; any format), 16-byte aligned;
+ * block_table: device int32 [num_seqs][max_pages] (page ids trusted, as for kvq_decode_attn);
+ * every sequence holds pages_per_seq full pages (1 <= pages_per_seq <= max_pages);
+ * waves 4 or 8, depth 2, 3 or 4, 1 <= pages_per_split <= 64 * waves; 1 <= num_kv_heads <= 1024.
+ * The grid has num_seqs * num_kv_heads * ceil(pages_per_seq / pages_per_split) workgroups in
+ * split-major order (workgroup j: split j / (num_seqs * num_kv_heads), sequence and kv head from
+ * j mod that, the kv head fastest); wave w of a workgroup streams pages p0 + w, p0 + w + waves, ..
+ * of its split (p0 = split * pages_per_split).  Lane l (n = l % 16, g = l / 16) loads, from each
+ * of those page-head blocks, the 16 bytes at 64 n + 16 g, the 16 bytes at 1024 + 16 l and the
+ * 32-bit words at 2048 + 4 n and 2112 + 4 n.  sink: device uint32, one word per wave (index
+ * waves * j + w): the sum mod 2^32 of every 32-bit word its lanes loaded.  Nothing else is
+ * written.
+ */
+int kvq_hbm_decode_pattern(const void* pool, int32_t num_kv_heads, int32_t num_seqs, int32_t pages_per_seq,
+                           const int32_t* block_table, int32_t max_pages, int32_t waves, int32_t depth,
+                           int32_t pages_per_split, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

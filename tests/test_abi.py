@@ -257,6 +257,19 @@ def test_dequant_and_copy_reject_bad_args():
     assert ap(FAKE, FAKE, 8, 1, 0, FAKE, 1, FAKE, 0, None) == kvq.KVQ_OK
     assert ap(FAKE, FAKE, 8, 1, 16, FAKE, 1, FAKE, 2, None) == kvq.KVQ_ERR_INVALID_ARG
     assert ap(FAKE, FAKE, 9, 1, 16, FAKE, 1, FAKE, 1, None) == kvq.KVQ_ERR_UNSUPPORTED
+    # the decode-pattern probe: argument checks (no launch)
+    dp = lib.kvq_hbm_decode_pattern
+    assert dp(None, 8, 1, 4, FAKE, 4, 4, 3, 16, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert dp(FAKE, 8, 1, 4, FAKE, 4, 4, 3, 16, None, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert dp(ctypes.c_void_p(4096 + 8), 8, 1, 4, FAKE, 4, 4, 3, 16, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert dp(FAKE, 0, 1, 4, FAKE, 4, 4, 3, 16, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert dp(FAKE, 8, 1, 5, FAKE, 4, 4, 3, 16, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG  # beyond max_pages
+    assert dp(FAKE, 8, 1, 0, FAKE, 4, 4, 3, 16, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert dp(FAKE, 8, 1, 4, FAKE, 4, 16, 2, 16, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG  # waves
+    assert dp(FAKE, 8, 1, 4, FAKE, 4, 4, 5, 16, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG  # depth
+    assert dp(FAKE, 8, 1, 4, FAKE, 4, 4, 3, 257, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG  # split > 64 waves
+    assert dp(FAKE, 8, 1, 4, FAKE, 4, 4, 3, 0, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert dp(FAKE, 8, 0, 4, FAKE, 4, 4, 3, 16, FAKE, None) == kvq.KVQ_OK
 
 
 def test_python_layer_raises_typed_errors():

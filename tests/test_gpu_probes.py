@@ -114,3 +114,45 @@ def test_launch_plan_log(capfd, monkeypatch):
     err = capfd.readouterr().err
     assert "kvq: kvq_decode_attn launch: 2 seqs, 8 q / 2 kv heads, max_seq_len 1000, variant 0" in err
     assert "kvq: kvq_dequant_page: 2 pages, 2 kv heads, format 0, had_block 128, rotated back on the matrix cores" in err
+
+
+def _decode_pattern_want(pool, hkv, table, pages_per_seq, waves, pages_per_split):
+    """Per wave, the sum mod 2^32 of the words its lanes load (the probe's definition)."""
+    num_seqs = table.shape[0]
+    blocks = pool.reshape(pool.shape[0], hkv, 2176)
+    nsplit = -(-pages_per_seq // pages_per_split)
+    units = num_seqs * hkv
+    want = np.zeros(units * nsplit * waves, np.uint64)
+    for j in range(units * nsplit):
+        split, unit = divmod(j, units)
+        b, h = divmod(unit, hkv)
+        p0, p1 = split * pages_per_split, min((split + 1) * pages_per_split, pages_per_seq)
+        for w in range(waves):
+            tot = 0
+            for p in range(p0 + w, p1, waves):
+                blk = blocks[table[b, p], h].view(np.uint32)
+                # K rows and V words once each (64 lanes x 16 bytes), the 16 K / V parameter words
+                # of each 64-byte run loaded by four lanes each
+                tot += int(blk[:512].sum(dtype=np.uint64)) + 4 * int(blk[512:544].sum(dtype=np.uint64))
+            want[waves * j + w] = tot
+    return (want & 0xFFFFFFFF).astype(np.uint32)
+
+
+@pytest.mark.parametrize("hkv,num_seqs,pages,waves,depth,pps", [
+    (2, 3, 37, 4, 3, 16), (1, 1, 5, 8, 2, 512), (8, 2, 256, 8, 3, 512), (3, 2, 70, 4, 4, 9), (8, 4, 129, 4, 2, 64)])
+def test_decode_pattern_probe(hkv, num_seqs, pages, waves, depth, pps):
+    # the decode's page stream without its arithmetic: each wave's sink word is the sum of the
+    # words its lanes loaded from the page-head blocks of its pages (permuted pool, ragged splits)
+    print(f"[probes] decode pattern hkv {hkv} B {num_seqs} pages {pages} W {waves} D {depth} split {pps}", flush=True)
+    rng = np.random.default_rng(1000 * hkv + pages)
+    n_pool = num_seqs * pages + 3
+    pool_h = rng.integers(0, 256, (n_pool, hkv, 2176), dtype=np.uint8)
+    max_pages = pages + 2
+    table = np.zeros((num_seqs, max_pages), np.int32)
+    table[:, :pages] = rng.permutation(n_pool)[:num_seqs * pages].reshape(num_seqs, pages)
+    pool = torch.from_numpy(pool_h).cuda()
+    bt = torch.from_numpy(table).cuda()
+    sink = kvq.hbm_decode_pattern(pool, hkv, bt, pages, waves, depth, pps)
+    torch.cuda.synchronize()
+    want = _decode_pattern_want(pool_h, hkv, table, pages, waves, pps)
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
