@@ -663,6 +663,69 @@ __device__ __forceinline__ void process_page_mx(const PageData<1>& pg, int valid
                 has1, n, jg, a_row_used, ptile);
 }
 
+// Two MXFP4 pages at once (pages a and b of the wave, ptile2 two p tiles): both pages' scores,
+// one update of the running maxima for the pair, then both pages' p.V products.  The two pages'
+// chains are independent, and the row reductions, the vote and the LDS round trip of p are
+// paid once per pair.
+__device__ __forceinline__ void process_pages_mx2(const PageData<1>& pa, const PageData<1>& pb, int valid_a,
+                                                  int valid_b, WaveState& s, const f16x8 (&qh)[4], float c2, bool has0,
+                                                  bool has1, int n, int jg, bool a_row_used,
+                                                  _Float16 (*ptile2)[2 * kMaxG][kPage], int e8sh) {
+  const VTileMx va = unpack_v_mx(pa, valid_a, jg, e8sh), vb = unpack_v_mx(pb, valid_b, jg, e8sh);
+  const f32x4 sa = scores_mx(unpack_k_mx(pa, e8sh), qh), sb = scores_mx(unpack_k_mx(pb, e8sh), qh);
+  const bool ta = n < valid_a, tb = n < valid_b;
+  const float xa0 = ta ? (sa[0] + sa[1]) * c2 : -INFINITY, xa1 = ta ? (sa[2] + sa[3]) * c2 : -INFINITY;
+  const float xb0 = tb ? (sb[0] + sb[1]) * c2 : -INFINITY, xb1 = tb ? (sb[2] + sb[3]) * c2 : -INFINITY;
+  const float pm0 = row_max16(fmaxf(xa0, xb0)), pm1 = row_max16(fmaxf(xa1, xb1));
+  // p <= 2^8 stays far inside fp16 (no value scale is folded into p here)
+  if (__any(pm0 > s.m0 + 8.0f || pm1 > s.m1 + 8.0f)) {
+    const float mn0 = fmaxf(s.m0, pm0), mn1 = fmaxf(s.m1, pm1);
+    const float f0 = __builtin_amdgcn_exp2f(s.m0 - mn0), f1 = __builtin_amdgcn_exp2f(s.m1 - mn1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s.acc[i] *= f32x4{f0, f0, f1, f1};
+    s.l0 *= f0;
+    s.l1 *= f1;
+    s.m0 = mn0;
+    s.m1 = mn1;
+  }
+  const float pa0 = __builtin_amdgcn_exp2f(xa0 - s.m0), pa1 = __builtin_amdgcn_exp2f(xa1 - s.m1);
+  const float pb0 = __builtin_amdgcn_exp2f(xb0 - s.m0), pb1 = __builtin_amdgcn_exp2f(xb1 - s.m1);
+  s.l0 += pa0 + pb0;
+  s.l1 += pa1 + pb1;
+  // p as fp16 high + low parts at A-tile rows 2g+limb of each page's tile (a masked score is
+  // -inf: its p is exactly 0)
+  const float pv[2][2] = {{pa0, pa1}, {pb0, pb1}};
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const _Float16 h0 = (_Float16)pv[t][0], h1 = (_Float16)pv[t][1];
+    const _Float16 r0 = (_Float16)(pv[t][0] - (float)h0), r1 = (_Float16)(pv[t][1] - (float)h1);
+    if (has0) {
+      ptile2[t][4 * jg + 0][n] = h0;
+      ptile2[t][4 * jg + 1][n] = r0;
+    }
+    if (has1) {
+      ptile2[t][4 * jg + 2][n] = h1;
+      ptile2[t][4 * jg + 3][n] = r1;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const f16x4 a0 = a_row_used ? *(const f16x4*)&ptile2[0][n][4 * jg] : f16x4{0, 0, 0, 0};
+  const f16x4 a1 = a_row_used ? *(const f16x4*)&ptile2[1][n][4 * jg] : f16x4{0, 0, 0, 0};
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, va.blo[q], s.acc[2 * q], 0, 0, 0);
+    s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, va.bhi[q], s.acc[2 * q + 1], 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    s.acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, vb.blo[q], s.acc[2 * q], 0, 0, 0);
+    s.acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, vb.bhi[q], s.acc[2 * q + 1], 0, 0, 0);
+  }
+}
+
 // p.V of an MXFP4 cache on the scaled matrix cores as well (UltraQuant article, section on how
 // the method works: FP8-quantized attention weights against the FP4 V tensors with their UE8M0
 // group scales): v_mfma_scale_f32_32x32x64_f8f6f4, 64 tokens (4 pages) per MFMA, one MFMA per V

@@ -55,7 +55,8 @@ struct DecodeSmem {
   uint8_t q8s[2][16][4];
   float qdelta[kMaxG];  // INT4: weight of the mid limb, 256 delta
   float qsum[kMaxG];
-  _Float16 ptile[W][2 * kMaxG][kPage];  // p~ split into fp16 high/low parts, A-tile rows 2g+limb
+  // p~ split into fp16 high/low parts, A-tile rows 2g+limb (MXFP4: one tile for each page of a pair)
+  _Float16 ptile[W][FMT == 1 ? 2 : 1][2 * kMaxG][kPage];
   // each wave's partial output (after its pages); on the scaled MXFP4 path the same bytes hold
   // the wave's staging while it streams
   union WaveBuf {
@@ -548,6 +549,27 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       else if (progress < 3 * npw) __builtin_amdgcn_s_setprio(1);
       else __builtin_amdgcn_s_setprio(0);
     }
+    if constexpr (FMT == 1 && NB % 2 == 0) {
+      // MXFP4 pages in pairs (process_pages_mx2): the pair's first load goes out before it, into
+      // the buffer freed by the previous pair's second page, and its second load after it, into
+      // the buffer of the pair's first page; the loads and their order are those of the
+      // one-page loop below
+#pragma unroll
+      for (int d = 0; d < NB; d += 2) {
+        const int i = i0 + d;
+        st[(d + D) % NB] = load_page<PF>(page_base(i + D), i + D < npw, koff, voff, poff, qoff);
+        if (i < npw) {
+          const bool has_b = i + 1 < npw;  // a page past the wave's last holds zeros: masked whole
+          if (app_wg && pw0 + W * i == last_pg) patch_appended<PF>(st[d], sm.arow, sm.aparam, app_slot, n, jg);
+          if (app_wg && has_b && pw0 + W * (i + 1) == last_pg)
+            patch_appended<PF>(st[d + 1], sm.arow, sm.aparam, app_slot, n, jg);
+          process_pages_mx2(st[d], st[d + 1], valid0 - i * W * kPage, has_b ? valid0 - (i + 1) * W * kPage : 0, s,
+                            qh, c2, has0, has1, n, jg, a_row_used, sm.ptile[wave], a.e8_shift);
+        }
+        st[(d + 1 + D) % NB] = load_page<PF>(page_base(i + 1 + D), i + 1 + D < npw, koff, voff, poff, qoff);
+      }
+      continue;
+    }
 #pragma unroll
     for (int d = 0; d < NB; ++d) {
       const int i = i0 + d;
@@ -557,10 +579,10 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
         if (app_wg && pw0 + W * i == last_pg) patch_appended<PF>(st[d], sm.arow, sm.aparam, app_slot, n, jg);
         if constexpr (FMT == 0)
           process_page<HPL>(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, s, qa, alpha0, beta0, alpha1, beta1,
-                       has0, has1, n, jg, a_row_used, sm.ptile[wave]);
+                       has0, has1, n, jg, a_row_used, sm.ptile[wave][0]);
         else if constexpr (FMT == 1)
           process_page_mx(st[d], valid0 - i * W * kPage, valid0 - i * W * kPage, valid0 - i * W * kPage, s, qh, c2,
-                          has0, has1, n, jg, a_row_used, sm.ptile[wave], a.e8_shift);
+                          has0, has1, n, jg, a_row_used, sm.ptile[wave][0], a.e8_shift);
         else
           scaled_stage_page(st[d], valid0 - i * W * kPage, qa8, qsa, c2, n, jg, d, sm.wb[wave].st, xs0[d], xs1[d]);
       } else if constexpr (FMT == 2) {
