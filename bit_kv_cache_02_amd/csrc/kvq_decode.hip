@@ -16,7 +16,8 @@
 //            p_t*sv_t enters split into an fp16 high part and an fp16 low part (rows 2g and
 //            2g+1), which keeps ~22 bits of it.
 // MXFP4 pages convert to fp16 tiles with the group scale applied (v_cvt_scalef32_pk_f16_fp4) and
-// run both contractions on the f16 matrix cores; with KVQ_MX_SCALED_MFMA both run on the scaled
+// run both contractions on the f16 matrix cores, two pages at a time (one softmax update per
+// pair); with KVQ_MX_SCALED_MFMA both run on the scaled
 // FP8 x FP4 matrix cores straight on the stored codes instead (layouts in kvq_attn.h).
 // kvq_decode_step runs the same kernel with the append folded in: the workgroup that streams a
 // sequence's last page also rotates and quantizes that step's new K/V token (a wave butterfly),
