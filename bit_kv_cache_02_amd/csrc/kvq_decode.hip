@@ -331,25 +331,26 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
   const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(bt, a.max_pages * 4);
   const int pid_vec = (int)__builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, lane * W < span ? 4 * bt_idx : kOutOfRange, 0, 0);
 
-  // Fused step: the workgroup that holds the sequence's last page appends the new token there,
-  // wave W-1 the K vector and wave W-2 the V vector (their words load here; every wave issues
-  // the loads, out of range where it does not append).
+  // Fused step: the workgroup that holds the sequence's last page appends the new token there;
+  // the wave that streams that page (pages are dealt round-robin) takes both the K and the V
+  // vector (their words load here; every wave issues the loads, out of range where it does not
+  // append).
   const int n_pages = (L + kPage - 1) / kPage;
   const int last_pg = n_pages - 1;
   const int app_slot = (L - 1) & (kPage - 1);
   const bool app_wg = a.append && last_pg >= p_begin && last_pg < p_begin + span;
-  const int app_which = wave == W - 1 ? 0 : 1;  // 0: K, 1: V
-  const bool app_wave = app_wg && wave >= W - 2;
-  uint32_t nword[2];
+  const bool app_wave = app_wg && (last_pg - p_begin) % W == wave;
+  uint32_t nword[2][2];  // [K|V][element lane | lane + 64]
   int nshift[2];
-  {
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
     // an empty range when this wave does not append: nothing can be read whatever the offset
     const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(app_which ? a.vnew : a.knew, app_wave ? a.num_seqs * a.hkv * kHeadDim * 2 : 0);
+        make_rsrc(which ? a.vnew : a.knew, app_wave ? a.num_seqs * a.hkv * kHeadDim * 2 : 0);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int byte = ((b * a.hkv + kvh) * kHeadDim + lane + 64 * e) * 2;
-      nword[e] = __builtin_amdgcn_raw_buffer_load_b32(r, app_wave ? (byte & ~3) : kOutOfRange, 0, 0);
+      nword[which][e] = __builtin_amdgcn_raw_buffer_load_b32(r, app_wave ? (byte & ~3) : kOutOfRange, 0, 0);
       nshift[e] = 8 * (byte & 3);
     }
   }
@@ -421,65 +422,75 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(DecodeParams a) {
       }
     }
   }
-  // ---- 2b. fused step: rotate and quantize the new K / V vector (one per appending wave),
-  //          exactly as the append path defines it, stage its row in LDS for the wave that
-  //          streams the last page, and store it into the page ----
-  uint32_t app_word = 0, app_byte = 0, app_param = 0;
+  if (lane == 0) sm.prog[wave] = 0;
+  __syncthreads();
+
+  // ---- 2b. fused step, after the barrier so that no other wave waits for it (its own first pages
+  //          are in flight meanwhile): the appending wave rotates and quantizes the new K and V
+  //          vectors exactly as the append path defines them, stages their rows in LDS for the
+  //          substitution into its last page, and stores them into the page ----
+  uint32_t app_word = 0, app_byte = 0, app_param[2] = {0u, 0u};
   if (app_wave) {
-    float x0 = raw_to_f32(nword[0] >> nshift[0], a.kv_dtype), x1 = raw_to_f32(nword[1] >> nshift[1], a.kv_dtype);
-    rotate_wave(x0, x1, a.had_block, a.quat, a.quat_full, lane);
-    uint32_t c0, c1;
-    if constexpr (FMT == 0) {
-      const float lo = -wave_max(-fminf(x0, x1)), hi = wave_max(fmaxf(x0, x1));
-      const uint32_t s_bits = f32_to_f16_bits((hi - lo) * (1.0f / 15.0f));
-      const uint32_t z_bits = f32_to_f16_bits(lo);
-      const float sf = f16_bits_to_f32(s_bits), zf = f16_bits_to_f32(z_bits);
-      const float r15 = sf > 0.0f ? __builtin_amdgcn_rcpf(15.0f * sf) : 0.0f;
-      c0 = __float_as_uint(fmaf(__builtin_amdgcn_fmed3f((x0 - zf) * r15, 0.0f, 1.0f), 15.0f, 12582912.0f)) & 15u;
-      c1 = __float_as_uint(fmaf(__builtin_amdgcn_fmed3f((x1 - zf) * r15, 0.0f, 1.0f), 15.0f, 12582912.0f)) & 15u;
-      app_param = s_bits | (z_bits << 16);
-    } else {
-      // UE8M0 exponent per 32 channels: lanes 0-31 / 32-63 hold groups 0 / 1 (x0) and 2 / 3 (x1)
-      float m0 = row_max16(fabsf(x0)), m1 = row_max16(fabsf(x1));
-      m0 = fmaxf(m0, xor_lane<16>(m0, lane_id()));
-      m1 = fmaxf(m1, xor_lane<16>(m1, lane_id()));
-      const int e0 = min(max((int)((__float_as_uint(m0) >> 23) & 255u) - 2, 0), 254);
-      const int e1 = min(max((int)((__float_as_uint(m1) >> 23) & 255u) - 2, 0), 254);
-      c0 = e2m1_code(ldexpf(x0, 127 - e0));
-      c1 = e2m1_code(ldexpf(x1, 127 - e1));
-      app_param = (uint32_t)__builtin_amdgcn_readlane(e0, 0) | ((uint32_t)__builtin_amdgcn_readlane(e0, 32) << 8) |
-                  ((uint32_t)__builtin_amdgcn_readlane(e1, 0) << 16) | ((uint32_t)__builtin_amdgcn_readlane(e1, 32) << 24);
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      float x0 = raw_to_f32(nword[which][0] >> nshift[0], a.kv_dtype);
+      float x1 = raw_to_f32(nword[which][1] >> nshift[1], a.kv_dtype);
+      rotate_wave(x0, x1, a.had_block, a.quat, a.quat_full, lane);
+      uint32_t c0, c1, prm;
+      if constexpr (FMT == 0) {
+        const float lo = -wave_max(-fminf(x0, x1)), hi = wave_max(fmaxf(x0, x1));
+        const uint32_t s_bits = f32_to_f16_bits((hi - lo) * (1.0f / 15.0f));
+        const uint32_t z_bits = f32_to_f16_bits(lo);
+        const float sf = f16_bits_to_f32(s_bits), zf = f16_bits_to_f32(z_bits);
+        const float r15 = sf > 0.0f ? __builtin_amdgcn_rcpf(15.0f * sf) : 0.0f;
+        c0 = __float_as_uint(fmaf(__builtin_amdgcn_fmed3f((x0 - zf) * r15, 0.0f, 1.0f), 15.0f, 12582912.0f)) & 15u;
+        c1 = __float_as_uint(fmaf(__builtin_amdgcn_fmed3f((x1 - zf) * r15, 0.0f, 1.0f), 15.0f, 12582912.0f)) & 15u;
+        prm = s_bits | (z_bits << 16);
+      } else {
+        // UE8M0 exponent per 32 channels: lanes 0-31 / 32-63 hold groups 0 / 1 (x0) and 2 / 3 (x1)
+        float m0 = row_max16(fabsf(x0)), m1 = row_max16(fabsf(x1));
+        m0 = fmaxf(m0, xor_lane<16>(m0, lane_id()));
+        m1 = fmaxf(m1, xor_lane<16>(m1, lane_id()));
+        const int e0 = min(max((int)((__float_as_uint(m0) >> 23) & 255u) - 2, 0), 254);
+        const int e1 = min(max((int)((__float_as_uint(m1) >> 23) & 255u) - 2, 0), 254);
+        c0 = e2m1_code(ldexpf(x0, 127 - e0));
+        c1 = e2m1_code(ldexpf(x1, 127 - e1));
+        prm = (uint32_t)__builtin_amdgcn_readlane(e0, 0) | ((uint32_t)__builtin_amdgcn_readlane(e0, 32) << 8) |
+              ((uint32_t)__builtin_amdgcn_readlane(e1, 0) << 16) | ((uint32_t)__builtin_amdgcn_readlane(e1, 32) << 24);
+      }
+      app_param[which] = prm;
+      sm.acode[which][lane] = (uint8_t)c0;
+      sm.acode[which][lane + 64] = (uint8_t)c1;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // row byte 4a+q holds channels a+32q (low nibble) and a+32q+16 (high nibble)
+      const int ra = lane >> 2, rq = lane & 3;
+      const uint32_t byte = (uint32_t)sm.acode[which][ra + 32 * rq] | ((uint32_t)sm.acode[which][ra + 32 * rq + 16] << 4);
+      ((uint8_t*)sm.arow[which])[lane] = (uint8_t)byte;
+      if (lane == 0) sm.aparam[which] = prm;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (which == 0) app_word = sm.arow[0][lane & 15];
+      else app_byte = byte;
     }
-    sm.acode[app_which][lane] = (uint8_t)c0;
-    sm.acode[app_which][lane + 64] = (uint8_t)c1;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // row byte 4a+q holds channels a+32q (low nibble) and a+32q+16 (high nibble)
-    const int ra = lane >> 2, rq = lane & 3;
-    app_byte = (uint32_t)sm.acode[app_which][ra + 32 * rq] | ((uint32_t)sm.acode[app_which][ra + 32 * rq + 16] << 4);
-    ((uint8_t*)sm.arow[app_which])[lane] = (uint8_t)app_byte;
-    if (lane == 0) sm.aparam[app_which] = app_param;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    app_word = sm.arow[app_which][lane & 15];
   }
   {
-    // every wave issues the three stores; out of range unless it appends
+    // every wave issues the four stores; out of range unless it appends
     const int app_pid = __builtin_amdgcn_readfirstlane(app_pid_w);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(a.pool + (int64_t)kvh * kPageHeadBytes + (int64_t)app_pid * page_stride,
                                                kPageHeadBytes);
-    const int kw = (app_wave && app_which == 0 && lane < 16) ? 64 * app_slot + 4 * lane : kOutOfRange;
-    const int vb = (app_wave && app_which == 1) ? kVCodesOff + 256 * (app_slot >> 2) + 4 * lane + (app_slot & 3)
-                                                : kOutOfRange;
-    const int pw = (app_wave && lane == 0) ? (app_which ? kVParamsOff : kKParamsOff) + 4 * app_slot : kOutOfRange;
+    const int kw = (app_wave && lane < 16) ? 64 * app_slot + 4 * lane : kOutOfRange;
+    const int vb = app_wave ? kVCodesOff + 256 * (app_slot >> 2) + 4 * lane + (app_slot & 3) : kOutOfRange;
+    const int pk = (app_wave && lane == 0) ? kKParamsOff + 4 * app_slot : kOutOfRange;
+    const int pv = (app_wave && lane == 0) ? kVParamsOff + 4 * app_slot : kOutOfRange;
     __builtin_amdgcn_raw_buffer_store_b32(app_word, r, kw, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)app_byte, r, vb, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(app_param, r, pw, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(app_param[0], r, pk, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(app_param[1], r, pv, 0, 0);
   }
-  if (lane == 0) sm.prog[wave] = 0;
-  __syncthreads();
+
 
   const int ga = n >> 1;   // A-tile row 2g+limb -> head of this lane's A row (HPL 2)
   const int limb = n & 1;  // 0: high limb / high fp16 part, 1: low
