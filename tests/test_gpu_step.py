@@ -133,6 +133,19 @@ def test_step_int4_wide_batch():
     run_step("int4/wide", lens, hkv=4, group=4, hb=128, seed=5)
 
 
+@pytest.mark.parametrize("fmt,hkv,fill", [("int4", 4, SENT), ("int4", 4, "random"), ("int4", 2, SENT),
+                                           ("mxfp4", 4, SENT), ("mxfp4", 2, "random")])
+def test_step_every_appending_wave(fmt, hkv, fill):
+    # 64 sequences x 4 kv heads = 256 units take the 8-wave plan, x 2 kv heads the 4-wave plan;
+    # either way one split per unit, page p streamed by wave p % W.  The wave that streams a
+    # sequence's last page also appends its token, so put the last page on every wave, with the
+    # new token in slot 0 (a fresh page), 1, 7 and 15 (the page's last slot)
+    lens = [16 * (i % 16) + (0, 1, 7, 15)[i // 16] + 1 for i in range(64)]
+    group, q_dtype = (4, "bf16") if fmt == "int4" else (8, "e4m3")
+    run_step(f"{fmt}/every-wave/hkv{hkv}/{fill}", lens, hkv=hkv, group=group, hb=128, fmt=fmt,
+             q_dtype=q_dtype, seed=6, fill=fill)
+
+
 @pytest.mark.parametrize("scaled", [False, True])
 @pytest.mark.parametrize("group,q_dtype", [(8, "e4m3"), (1, "bf16")])
 def test_step_mxfp4(group, q_dtype, scaled):
