@@ -399,8 +399,16 @@ def time_prefill_append(dev, repeats=10):
     new_tokens = int(lens[0])
     bt_inorder = torch.arange(w.batch * table.shape[1], dtype=torch.int32, device=dev).reshape(table.shape)
     bt_inorder = torch.minimum(bt_inorder, torch.tensor(num_pages - 1, dtype=torch.int32, device=dev))
+    # and the workload's own scattered pages written in increasing id (order 2: the list of
+    # (sequence, page) items sorted by the page each goes to; the rows are then read out of order).
+    # The workload's pages are 0 .. num_pages - 1, so page i of that order is the item's own page.
+    npg = new_tokens // 16
+    touched = table[:, :npg].reshape(-1)
+    assert np.array_equal(np.sort(touched), np.arange(num_pages)), "the prefill pages must be 0 .. num_pages - 1"
+    by_page = torch.from_numpy(np.argsort(touched, kind="stable").astype(np.int32).reshape(w.batch, npg)).to(dev)
     pattern_us = {}
-    for name, order, tbl in (("own", 0, bt), ("page", 1, bt), ("page_in_order", 1, bt_inorder)):
+    for name, order, tbl in (("own", 0, bt), ("page", 1, bt), ("page_in_order", 1, bt_inorder),
+                             ("page_by_id", 2, by_page)):
         settle(lambda: kvq.hbm_append_pattern(k, v, tbl, pools[0], new_tokens, order), 0.1)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(repeats)]
         for i in range(repeats):
@@ -428,6 +436,7 @@ def time_prefill_append(dev, repeats=10):
         "frac_of_access_pattern_probe": round(pattern_us["own"] / res[128], 4),
         "us_access_pattern_probe_page_major": round(pattern_us["page"], 2),
         "us_access_pattern_probe_page_major_pages_in_order": round(pattern_us["page_in_order"], 2),
+        "us_access_pattern_probe_page_major_written_by_page_id": round(pattern_us["page_by_id"], 2),
     }
 
 

@@ -317,18 +317,28 @@ __global__ __launch_bounds__(256) void append_pattern_kernel(const uint8_t* __re
 
 // The same traffic in another order: one workgroup per (page, sequence) with one wave per (K|V,
 // kv head), so the workgroup reads the page's tokens of all kv heads (one contiguous run of
-// 16 token rows for K and one for V) and writes all of the page's head blocks.
+// 16 token rows for K and one for V) and writes all of the page's head blocks.  With a list
+// (the destination order), workgroup i = b P + pg (P pages per sequence) takes list item
+// e = list[i] instead: it reads sequence e / P's page e % P and writes page i, so the pages are
+// written in launch order whatever order the rows are read in.
 __global__ __launch_bounds__(1024) void append_pattern_page_kernel(const uint8_t* __restrict__ k,
                                                                   const uint8_t* __restrict__ v,
                                                                   const int32_t* __restrict__ block_table,
                                                                   uint8_t* __restrict__ pool, int hkv,
-                                                                  int new_tokens, int max_pages) {
+                                                                  int new_tokens, int max_pages, bool list) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(thread_id() >> 6);
   if (wave >= 2 * hkv) return;
   const int is_v = wave >= hkv;
   const int h = is_v ? wave - hkv : wave;
-  const int b = block_id_y(), pg = block_id_x();
+  int b = block_id_y(), pg = block_id_x();
+  const int npg = new_tokens / kPage;
+  const int dest = b * npg + pg;  // list form: the page written
+  if (list) {
+    const int e = __builtin_amdgcn_readfirstlane(block_table[dest]);
+    b = e / npg;
+    pg = e - b * npg;
+  }
   const int n = lane & 15, g = lane >> 4;
   const int row_stride = hkv * kHeadDim * 2;
   const uint8_t* src = (is_v ? v : k) + (((int64_t)b * new_tokens + pg * kPage) * hkv + h) * (kHeadDim * 2);
@@ -337,7 +347,7 @@ __global__ __launch_bounds__(1024) void append_pattern_page_kernel(const uint8_t
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     x ^= __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, n * row_stride + 16 * g + 64 * j, 0, 0));
-  const int page_id = block_table[(int64_t)b * max_pages + pg];
+  const int page_id = list ? dest : block_table[(int64_t)b * max_pages + pg];
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(pool + ((int64_t)page_id * hkv + h) * (int64_t)kPageHeadBytes, kPageHeadBytes);
   const int off = is_v ? kVCodesOff + 256 * (n >> 2) + 64 * g + 16 * (n & 3) : 64 * n + 16 * g;
   __builtin_amdgcn_raw_buffer_store_b128(x, pr, off, 0, 2);
@@ -458,11 +468,11 @@ hipError_t launch_fold4(const void* src, void* dst, size_t dst_bytes, hipStream_
 }
 
 hipError_t launch_append_pattern(const void* k, const void* v, const int32_t* block_table, void* pool, int hkv,
-                                 int num_seqs, int new_tokens, int max_pages, int page_major, hipStream_t stream) {
+                                 int num_seqs, int new_tokens, int max_pages, int order, hipStream_t stream) {
   const int pages = new_tokens / kPage;
-  if (page_major) {
+  if (order != 0) {
     hipLaunchKernelGGL(append_pattern_page_kernel, dim3((unsigned)pages, (unsigned)num_seqs), dim3(1024), 0, stream,
-                       (const uint8_t*)k, (const uint8_t*)v, block_table, (uint8_t*)pool, hkv, new_tokens, max_pages);
+                       (const uint8_t*)k, (const uint8_t*)v, block_table, (uint8_t*)pool, hkv, new_tokens, max_pages, order == 2);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((pages + kAppendPagesPerWave - 1) / kAppendPagesPerWave), (unsigned)num_seqs,

@@ -546,8 +546,10 @@ int kvq_hbm_append_pattern(const void* k, const void* v, int32_t num_kv_heads, i
   if (new_tokens < 0 || new_tokens % 16) return fail(KVQ_ERR_INVALID_ARG, "new_tokens must be a non-negative multiple of 16");
   if (max_pages < 0 || (int64_t)new_tokens > 16 * (int64_t)max_pages)
     return fail(KVQ_ERR_INVALID_ARG, "new_tokens must be at most 16 * max_pages");
-  if (order > 1) return fail(KVQ_ERR_INVALID_ARG, "order must be 0 or 1");
-  if (order == 1 && num_kv_heads > 8) return fail(KVQ_ERR_UNSUPPORTED, "order 1 takes at most 8 kv heads");
+  if (order > 2) return fail(KVQ_ERR_INVALID_ARG, "order must be 0, 1 or 2");
+  if (order != 0 && num_kv_heads > 8) return fail(KVQ_ERR_UNSUPPORTED, "orders 1 and 2 take at most 8 kv heads");
+  if (order == 2 && (int64_t)max_pages * 16 != new_tokens)
+    return fail(KVQ_ERR_INVALID_ARG, "order 2 takes a list of exactly num_seqs * new_tokens / 16 items");
   if (num_seqs == 0 || new_tokens == 0) return KVQ_OK;
   return hip_status(kvq::launch_append_pattern(k, v, block_table, pool, num_kv_heads, num_seqs, new_tokens, max_pages,
                                                (int)order, (hipStream_t)stream),

@@ -147,7 +147,7 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t str
 hipError_t launch_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_fold4(const void* src, void* dst, size_t dst_bytes, hipStream_t stream);
 hipError_t launch_append_pattern(const void* k, const void* v, const int32_t* block_table, void* pool, int hkv,
-                                 int num_seqs, int new_tokens, int max_pages, int page_major, hipStream_t stream);
+                                 int num_seqs, int new_tokens, int max_pages, int order, hipStream_t stream);
 hipError_t launch_decode_pattern(const void* pool, const int32_t* block_table, int hkv, int num_seqs,
                                  int pages_per_seq, int max_pages, int waves, int depth, int pages_per_split,
                                  uint32_t* sink, hipStream_t stream);

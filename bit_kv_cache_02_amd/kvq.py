@@ -363,7 +363,9 @@ def hbm_append_pattern(k: torch.Tensor, v: torch.Tensor, block_table: torch.Tens
                        new_tokens: int, order: int = 0):
     """The append's memory traffic without its arithmetic (kvq_hbm_append_pattern): k, v
     [num_seqs * new_tokens][Hkv][128] 2-byte elements, block_table int32 [num_seqs][max_pages],
-    pool uint8 [pages][Hkv][2176]; order 0 the append's own, 1 one workgroup per page."""
+    pool uint8 [pages][Hkv][2176]; order 0 the append's own, 1 one workgroup per page, 2 as 1 with
+    the pages written in increasing id: block_table is then the [num_seqs][new_tokens / 16] list
+    whose item i names the (sequence, page) b * (new_tokens / 16) + j written to page i."""
     for t, n in ((k, "k"), (v, "v"), (pool, "pool")):
         _require(t, n)
     _require(block_table, "block_table", torch.int32)

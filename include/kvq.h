@@ -346,6 +346,12 @@ int kvq_hbm_fold4(const void* src, void* dst, size_t dst_bytes, void* stream);
  * such waves per workgroup); order 1: one workgroup per (sequence, page) holding a wave per
  * (K|V, kv head), which reads the page's token rows of all kv heads together and writes all of
  * its head blocks (at most 8 kv heads, else KVQ_ERR_UNSUPPORTED).  Both write the same bytes.
+ * order 2: as order 1, with the pages written in the order of their ids: block_table is then a
+ * list of exactly num_seqs * P items (P = new_tokens / 16, so max_pages must equal P, else
+ * KVQ_ERR_INVALID_ARG), and workgroup i (launched as order 1 launches the i-th (sequence, page)
+ * in row-major order) takes item e = block_table[i] (0 <= e < num_seqs * P, trusted): it reads
+ * the rows of sequence e / P's page e % P and writes them to page i, as order 1 would with that
+ * page's table entry equal to i.  The pool must hold num_seqs * P pages.
  */
 int kvq_hbm_append_pattern(const void* k, const void* v, int32_t num_kv_heads, int32_t num_seqs,
                            int32_t new_tokens, const int32_t* block_table, int32_t max_pages, void* pool,

@@ -255,8 +255,11 @@ def test_dequant_and_copy_reject_bad_args():
     assert ap(ctypes.c_void_p(4096 + 8), FAKE, 8, 1, 16, FAKE, 1, FAKE, 0, None) == kvq.KVQ_ERR_INVALID_ARG
     assert ap(FAKE, FAKE, 8, 0, 16, FAKE, 1, FAKE, 0, None) == kvq.KVQ_OK
     assert ap(FAKE, FAKE, 8, 1, 0, FAKE, 1, FAKE, 0, None) == kvq.KVQ_OK
-    assert ap(FAKE, FAKE, 8, 1, 16, FAKE, 1, FAKE, 2, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert ap(FAKE, FAKE, 8, 1, 16, FAKE, 1, FAKE, 3, None) == kvq.KVQ_ERR_INVALID_ARG
     assert ap(FAKE, FAKE, 9, 1, 16, FAKE, 1, FAKE, 1, None) == kvq.KVQ_ERR_UNSUPPORTED
+    assert ap(FAKE, FAKE, 9, 1, 16, FAKE, 1, FAKE, 2, None) == kvq.KVQ_ERR_UNSUPPORTED
+    # order 2 reads block_table as a list of exactly num_seqs * new_tokens / 16 items
+    assert ap(FAKE, FAKE, 8, 1, 16, FAKE, 2, FAKE, 2, None) == kvq.KVQ_ERR_INVALID_ARG
     # the decode-pattern probe: argument checks (no launch)
     dp = lib.kvq_hbm_decode_pattern
     assert dp(None, 8, 1, 4, FAKE, 4, 4, 3, 16, FAKE, None) == kvq.KVQ_ERR_INVALID_ARG

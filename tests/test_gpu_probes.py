@@ -73,10 +73,29 @@ def test_append_pattern_probe(hkv, num_seqs, new_tokens):
         kvq.hbm_append_pattern(torch.from_numpy(kh.view(np.int16)).cuda(), torch.from_numpy(vh.view(np.int16)).cuda(),
                                torch.from_numpy(table).cuda(), pool, new_tokens, order)
         pools.append(pool)
+    # order 2 (pages written in increasing id): the list item written to page i is the
+    # (sequence, page) whose table entry is i; a table of pages 0 .. num_seqs * pages - 1 in a
+    # random order, so that order 1 over that table writes the same bytes
+    items = rng.permutation(num_seqs * pages).astype(np.int32)
+    table_i = np.zeros((num_seqs, pages + 1), np.int32)
+    for i, e in enumerate(items):
+        table_i[e // pages, e % pages] = i
+    pools_i = []
+    for order, tbl in ((1, table_i), (2, items.reshape(num_seqs, pages))):
+        pool = torch.full((total, hkv, 2176), 0xA5, dtype=torch.uint8, device="cuda")
+        kvq.hbm_append_pattern(torch.from_numpy(kh.view(np.int16)).cuda(), torch.from_numpy(vh.view(np.int16)).cuda(),
+                               torch.from_numpy(np.ascontiguousarray(tbl)).cuda(), pool, new_tokens, order)
+        pools_i.append(pool)
     torch.cuda.synchronize()
+    assert np.array_equal(pools_i[0].cpu().numpy(), pools_i[1].cpu().numpy())
     got = pools[0].cpu().numpy()
     assert np.array_equal(pools[1].cpu().numpy(), got)
-    want = np.full_like(got, 0xA5)
+    assert np.array_equal(pools_i[0].cpu().numpy(), _append_pattern_want(kh, vh, table_i, num_seqs, pages, hkv, total))
+    assert np.array_equal(got, _append_pattern_want(kh, vh, table, num_seqs, pages, hkv, total))
+
+
+def _append_pattern_want(kh, vh, table, num_seqs, pages, hkv, total):
+    want = np.full((total, hkv, 2176), 0xA5, np.uint8)
     for which, src in ((0, kh), (1, vh)):
         rows = src.view(np.uint8).reshape(num_seqs, pages, 16, hkv, 256)  # [b][page][slot][h][byte]
         words = rows.reshape(num_seqs, pages, 16, hkv, 4, 4, 16)  # [..][i (64-byte piece)][g][16 bytes]
@@ -90,7 +109,7 @@ def test_append_pattern_probe(hkv, num_seqs, new_tokens):
                         blk[:, off:off + 16] = x[b, j, n, :, g]
                     poff = (2048 if which == 0 else 2112) + 4 * n
                     blk[:, poff:poff + 4] = x[b, j, n, :, 0, :4]
-    assert np.array_equal(got, want)
+    return want
 
 
 
