@@ -19,9 +19,10 @@
 // run both contractions on the f16 matrix cores, two pages at a time (one softmax update per
 // pair); with KVQ_MX_SCALED_MFMA both run on the scaled
 // FP8 x FP4 matrix cores straight on the stored codes instead (layouts in kvq_attn.h).
-// kvq_decode_step runs the same kernel with the append folded in: the workgroup that streams a
-// sequence's last page also rotates and quantizes that step's new K/V token (a wave butterfly),
-// writes it into the page, and substitutes its bytes into the page registers it streams.
+// kvq_decode_step runs the same kernel with the append folded in: in the workgroup that streams a
+// sequence's last page, the wave that streams that page also rotates and quantizes that step's
+// new K/V token (a wave butterfly) after the workgroup barrier, while its first pages are in
+// flight, writes it into the page, and substitutes its bytes into the page registers it streams.
 // The page layout puts V codes of four consecutive tokens in one 32-bit word per row byte, which
 // is the B-operand shape of the p.V MFMA, so one 16-byte load per lane feeds it directly.
 // Each wave streams its pages through a register prefetch pipeline (the query loads and the
